@@ -1,0 +1,347 @@
+"""Plain CPU oracle for the EPLB hot path.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  The product path (the HIP library
+and its Python binding) never does, and this module imports nothing from it.
+
+What it computes, and where the pages define it.  "The pages" are the web pages
+on DeepSeek's Expert Parallelism Load Balancer; the authority is the Russian
+translation page «DualPipe и EPLB: конвейер в обе стороны и балансировщик
+экспертов» (ai.flicky.cc), Part 2 "EPLB", cited below as [EPLB-ru] plus the
+section name:
+
+* ``load_hist`` / ``window_load`` -- the load of a logical expert is the number
+  of tokens the router sent to it during the observation period ([EPLB-ru],
+  translator's glossary box "термины"); the predicted load is built from
+  historical statistics over a window of steps ([EPLB-ru], opening section,
+  "moving average" remark).  Here: integer counts, summed over the last W steps.
+* ``balanced_packing``, ``replicate``, ``rebalance`` -- the three-step
+  hierarchical policy and the global policy ([EPLB-ru] sections "Алгоритм",
+  "Иерархическая балансировка", "Глобальная балансировка", the flowchart, and
+  the appendix's three functions and entry point as described there), taken in
+  the pages' order: groups -> nodes, replicas within a node, replicas -> GPUs.
+* ``redirect`` -- each routed (token, k) goes to one physical replica of its
+  logical expert; replica ``t mod logcnt`` of token row t.
+
+Arithmetic: every value is an exact Python integer or ``fractions.Fraction``.
+The pages compute replica loads and pack sums in float32; this oracle uses
+exact rationals instead (readings R1 and R5 in the design notes), so the result
+is the one the greedy procedure defines, with no rounding at all.
+
+Readings of points the pages leave open (each is a design decision, stated once
+more where it is used):
+  * sorts are stable: equal weights keep ascending item index;
+  * a tie between packs of equal sum goes to the lowest pack index;
+  * a tie in "highest load per replica" goes to the lowest node-local index;
+  * one item per pack is the identity assignment, not a greedy pass;
+  * the global policy is the hierarchical one with one group and one node;
+  * loads must lie in [0, 2**40]; outside that, the problem's status is
+    STATUS_BAD_LOAD and all its outputs are -1;
+  * if lcm(replica counts of a node) * (sum of that node's loads) >= 2**127 the
+    problem's status is STATUS_OVERFLOW and all its outputs are -1 (the exact
+    common-denominator pack sums would not fit 127 bits).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from math import lcm
+
+import numpy as np
+
+LOAD_MAX = 1 << 40          # largest accepted load (tokens) of one logical expert
+SUM_LIMIT = 1 << 127        # bound on lcm(counts) * node load sum
+
+# Per-problem device status values (documented in the C header as well).
+STATUS_OK = 0
+STATUS_BAD_LOAD = 1
+STATUS_OVERFLOW = 2
+
+
+# --------------------------------------------------------------------------
+# Policy selection and argument rules
+# --------------------------------------------------------------------------
+
+def policy(num_groups: int, num_nodes: int) -> tuple[int, int, bool]:
+    """Return (groups, nodes, hierarchical) for the policy the pages select.
+
+    [EPLB-ru] "Алгоритм": the hierarchical policy is used when the number of
+    nodes divides the number of expert groups; otherwise the global policy,
+    which the flowchart and appendix entry point describe as the same routine
+    run with a single group on a single node.
+    """
+    if num_groups % num_nodes == 0:
+        return num_groups, num_nodes, True
+    return 1, 1, False
+
+
+def argument_error(E: int, P: int, G: int, N: int, RK: int, X: int) -> str | None:
+    """Name the first argument rule a rebalance call breaks, or None.
+
+    Rules: every size positive; the divisibility requirements stated in the
+    appendix functions' docstrings and checks (groups divide the experts on the
+    hierarchical path, nodes divide the GPUs, GPUs divide the physical experts);
+    no fewer physical than logical experts (the replication step adds a
+    non-negative number of replicas); and a log2phy capacity X that can hold
+    the largest count the policy can produce, 1 + (P - E) / nodes.
+    """
+    if min(E, P, G, N, RK, X) < 1:
+        return "arg"
+    Gp, Np, hier = policy(G, N)
+    if hier and E % G != 0:
+        return "div"
+    if RK % Np != 0 or P % RK != 0:
+        return "div"
+    if P < E:
+        return "redundancy"
+    if X < 1 + (P - E) // Np:
+        return "capacity"
+    return None
+
+
+# --------------------------------------------------------------------------
+# The two greedy building blocks
+# --------------------------------------------------------------------------
+
+def balanced_packing(weights, num_packs: int) -> tuple[list[int], list[int]]:
+    """Greedy balanced packing of n weighted items into num_packs packs.
+
+    [EPLB-ru] appendix, first function as described in the translator's
+    summary above it: every pack ends with exactly n / num_packs items; items
+    are visited heaviest first and each goes into the lightest pack that still
+    has room.  When each pack holds one item the assignment is the identity.
+
+    ``weights`` are exact numbers (int or Fraction).  Returns, per item, the
+    pack it went to and its position (arrival order) inside that pack.
+
+    Readings: the heaviest-first order is a stable sort (equal weights keep
+    ascending item index); among packs with room and equal sums the lowest
+    pack index wins.
+    """
+    n = len(weights)
+    assert num_packs >= 1 and n % num_packs == 0
+    per_pack = n // num_packs
+    if per_pack == 1:
+        return list(range(n)), [0] * n
+
+    order = sorted(range(n), key=lambda i: weights[i], reverse=True)
+    # ``sorted(reverse=True)`` keeps equal keys in their original order, which
+    # is the stable descending order used here.
+    pack_sum = [0] * num_packs
+    pack_len = [0] * num_packs
+    pack_of = [-1] * n
+    slot_of = [-1] * n
+    for item in order:
+        open_packs = [p for p in range(num_packs) if pack_len[p] < per_pack]
+        target = min(open_packs, key=lambda p: (pack_sum[p], p))
+        pack_of[item] = target
+        slot_of[item] = pack_len[target]
+        pack_sum[target] += weights[item]
+        pack_len[target] += 1
+    return pack_of, slot_of
+
+
+def replicate(loads: list[int], num_phy: int) -> tuple[list[int], list[int], list[int]]:
+    """Grow ``len(loads)`` logical experts to ``num_phy`` physical ones.
+
+    [EPLB-ru] appendix, second function as summarised by the translator: each
+    added replica goes to the expert whose load per replica (load / count) is
+    currently highest.  Physical slot j < num_log is the original of expert j;
+    slot num_log + r is the r-th replica created.  A replica's rank is the
+    expert's count just before it was added (the original has rank 0).
+
+    Reading: a tie in load per replica goes to the lowest index.
+    Returns (phy2log, rank, count) for this subproblem.
+    """
+    num_log = len(loads)
+    assert num_phy >= num_log
+    count = [1] * num_log
+    phy2log = list(range(num_log))
+    rank = [0] * num_log
+    for _ in range(num_phy - num_log):
+        best = 0
+        best_val = Fraction(loads[0], count[0])
+        for i in range(1, num_log):
+            val = Fraction(loads[i], count[i])
+            if val > best_val:
+                best, best_val = i, val
+        phy2log.append(best)
+        rank.append(count[best])
+        count[best] += 1
+    return phy2log, rank, count
+
+
+# --------------------------------------------------------------------------
+# One rebalance problem (one MoE layer or one load snapshot)
+# --------------------------------------------------------------------------
+
+def rebalance_problem(w: list[int], P: int, G: int, N: int, RK: int) -> dict:
+    """Run the policy on one problem's logical loads ``w``.
+
+    Returns a dict with ``status``, and for STATUS_OK also ``phy2log`` (P ints),
+    ``phyrank`` (P ints) and ``logcnt`` (E ints).
+
+    Steps, in the order [EPLB-ru] "Иерархическая балансировка" gives them:
+      1. sum each group's loads and pack the groups onto the nodes, balanced;
+         the experts are renumbered node by node ("mlog" order): expert
+         g*S + j of a group placed on node n at slot s gets node-local index
+         s*S + j;
+      2. within each node, replicate experts greedily;
+      3. the node's physical experts, each carrying its expert's load divided
+         by the expert's final count, are packed onto the node's GPUs,
+         balanced; physical id = node*Pn + gpu*ppr + position on the GPU.
+    """
+    E = len(w)
+    if any((x < 0 or x > LOAD_MAX) for x in w):
+        return {"status": STATUS_BAD_LOAD}
+    Gp, Np, _ = policy(G, N)
+    S = E // Gp                 # experts per group
+    En = E // Np                # logical experts per node
+    Pn = P // Np                # physical experts per node
+    RKn = RK // Np              # GPUs per node
+    ppr = P // RK               # physical experts per GPU
+    groups_per_node = Gp // Np
+
+    # Step 1: groups -> nodes.
+    group_load = [sum(w[g * S:(g + 1) * S]) for g in range(Gp)]
+    node_of_group, slot_of_group = balanced_packing(group_load, Np)
+    mlog2log = [-1] * E
+    for g in range(Gp):
+        base = (node_of_group[g] * groups_per_node + slot_of_group[g]) * S
+        for j in range(S):
+            mlog2log[base + j] = g * S + j
+
+    phy2log = [-1] * P
+    phyrank = [-1] * P
+    logcnt = [-1] * E
+    for n in range(Np):
+        # Step 2: replicas within node n.
+        u = [w[mlog2log[n * En + i]] for i in range(En)]
+        local_phy, local_rank, count = replicate(u, Pn)
+
+        if lcm(*count) * sum(u) >= SUM_LIMIT:
+            return {"status": STATUS_OVERFLOW}
+
+        # Step 3: physical experts of node n -> its GPUs.
+        per_replica = [Fraction(u[local_phy[j]], count[local_phy[j]]) for j in range(Pn)]
+        gpu_of, pos_of = balanced_packing(per_replica, RKn)
+        for j in range(Pn):
+            pid = n * Pn + gpu_of[j] * ppr + pos_of[j]
+            phy2log[pid] = mlog2log[n * En + local_phy[j]]
+            phyrank[pid] = local_rank[j]
+        for i in range(En):
+            logcnt[mlog2log[n * En + i]] = count[i]
+    return {"status": STATUS_OK, "phy2log": phy2log, "phyrank": phyrank, "logcnt": logcnt}
+
+
+def rebalance(load, P: int, G: int, N: int, RK: int, X: int):
+    """Batched rebalance: every row of ``load`` ([B, E] integers) is a problem.
+
+    Returns numpy int32 arrays ``phy2log`` [B, P], ``log2phy`` [B, E, X],
+    ``logcnt`` [B, E] and ``status`` [B], plus ``maxlogcnt`` (the largest
+    count over all problems, the width the pages give log2phy).
+
+    log2phy[b, e, r] is the physical id of the rank-r replica of expert e, and
+    -1 for r >= logcnt[b, e] ([EPLB-ru] appendix entry point, and the
+    translator's exercise on layer 0 of the example).  A problem whose status
+    is not STATUS_OK has every output entry set to -1.
+    """
+    arr = np.asarray(load)
+    B, E = arr.shape
+    load = [[int(x) for x in row] for row in arr.tolist()]
+    phy2log = np.full((B, P), -1, dtype=np.int32)
+    log2phy = np.full((B, E, X), -1, dtype=np.int32)
+    logcnt = np.full((B, E), -1, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    maxlogcnt = 0
+    for b in range(B):
+        res = rebalance_problem(load[b], P, G, N, RK)
+        status[b] = res["status"]
+        if res["status"] != STATUS_OK:
+            continue
+        phy2log[b] = res["phy2log"]
+        logcnt[b] = res["logcnt"]
+        maxlogcnt = max(maxlogcnt, max(res["logcnt"]))
+        for pid in range(P):
+            log2phy[b, res["phy2log"][pid], res["phyrank"][pid]] = pid
+    return {"phy2log": phy2log, "log2phy": log2phy, "logcnt": logcnt,
+            "status": status, "maxlogcnt": maxlogcnt}
+
+
+# --------------------------------------------------------------------------
+# Load statistics and redirect
+# --------------------------------------------------------------------------
+
+def load_hist(idx: np.ndarray, E: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-layer token counts from top-k routing ids.
+
+    ``idx`` is [L, T, K] (any integer dtype).  cnt[l, e] is the number of
+    (t, k) with idx[l, t, k] == e, for 0 <= e < E ([EPLB-ru] glossary: the load
+    is the tokens routed to the expert).  Ids outside [0, E) are not counted;
+    invalid[l] says how many there were in layer l.
+    """
+    idx = np.asarray(idx)
+    L = idx.shape[0]
+    cnt = np.zeros((L, E), dtype=np.int64)
+    invalid = np.zeros(L, dtype=np.int64)
+    for l in range(L):
+        flat = idx[l].reshape(-1).astype(np.int64)
+        ok = (flat >= 0) & (flat < E)
+        cnt[l] = np.bincount(flat[ok], minlength=E)
+        invalid[l] = flat.size - int(ok.sum())
+    return cnt, invalid
+
+
+def window_load(step_hists: list[np.ndarray], W: int) -> np.ndarray:
+    """Sum of the last W per-step histograms (fewer while fewer exist).
+
+    The pages predict load from a moving average over history ([EPLB-ru]
+    opening section); the placement only compares loads, and every comparison
+    is unchanged by a common positive factor, so the windowed sum is used.
+    """
+    assert W >= 1 and len(step_hists) >= 1
+    recent = step_hists[-W:]
+    total = np.zeros_like(np.asarray(recent[0], dtype=np.int64))
+    for h in recent:
+        total += np.asarray(h, dtype=np.int64)
+    return total
+
+
+def redirect(idx: np.ndarray, log2phy: np.ndarray, logcnt: np.ndarray) -> np.ndarray:
+    """Logical -> physical expert ids for every routed (token, k).
+
+    out[l, t, k] = log2phy[l, e, t mod logcnt[l, e]] with e = idx[l, t, k], so
+    the tokens of an expert with c replicas are spread over the c replicas by
+    token row ([EPLB-ru] glossary: with two copies each gets about half).
+    An id outside [0, E), or a count outside [1, X], gives -1.
+    """
+    idx = np.asarray(idx)
+    L, T, K = idx.shape
+    E, X = log2phy.shape[1], log2phy.shape[2]
+    out = np.full((L, T, K), -1, dtype=np.int32)
+    t = np.arange(T, dtype=np.int64)[:, None]
+    for l in range(L):
+        e = idx[l].astype(np.int64)
+        ok_e = (e >= 0) & (e < E)
+        e_safe = np.where(ok_e, e, 0)
+        c = logcnt[l].astype(np.int64)[e_safe]
+        ok = ok_e & (c >= 1) & (c <= X)
+        r = np.where(ok, t % np.where(ok, c, 1), 0)
+        vals = log2phy[l][e_safe, r]
+        out[l] = np.where(ok, vals, -1)
+    return out
+
+
+def redirect_loop(idx, log2phy, logcnt) -> list:
+    """Same as :func:`redirect`, as plain Python loops (for small inputs)."""
+    L, T, K = len(idx), len(idx[0]), len(idx[0][0])
+    E, X = len(log2phy[0]), len(log2phy[0][0])
+    out = [[[-1] * K for _ in range(T)] for _ in range(L)]
+    for l in range(L):
+        for t in range(T):
+            for k in range(K):
+                e = int(idx[l][t][k])
+                if 0 <= e < E:
+                    c = int(logcnt[l][e])
+                    if 1 <= c <= X:
+                        out[l][t][k] = int(log2phy[l][e][t % c])
+    return out

@@ -1,0 +1,374 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError (or any exception) when the
+oracle module ``o`` disagrees with what the pages print, with a closed form,
+with brute force, or with an invariant.  ``test_oracle_pins.py`` runs them on
+the real oracle; ``test_oracle_mutations.py`` plants plausible mistakes in the
+oracle and shows that at least one pin fails for each.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import invariants as inv
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+
+
+def _example(o, groups=None, X=2):
+    g = GOLDEN["inputs"]
+    w = np.array(g["weight"], dtype=np.int64)
+    return w, o.rebalance(w, g["num_replicas"], groups or g["num_groups"], g["num_nodes"], g["num_gpus"], X)
+
+
+# ---------------------------------------------------------------- worked example
+
+def pin_golden_phy2log(o):
+    """The printed phy2log of both layers (hierarchical policy)."""
+    _, r = _example(o)
+    assert (r["status"] == 0).all()
+    assert r["phy2log"].tolist() == GOLDEN["phy2log"]["value"]
+
+
+def pin_golden_layer0(o):
+    """Layer 0 walk-through: node contents, replicated experts, logcnt, log2phy."""
+    w, r = _example(o)
+    logcnt = r["logcnt"][0].tolist()
+    assert logcnt == GOLDEN["layer0_logcnt"]["value"]
+    assert r["maxlogcnt"] == 2
+    phy = r["phy2log"][0]
+    node0 = set(phy[:8].tolist())
+    node1 = set(phy[8:].tolist())
+    S = 3
+    assert node0 == {e for g in GOLDEN["layer0_node_groups"]["node0_groups"] for e in range(g * S, g * S + S)}
+    assert node1 == {e for g in GOLDEN["layer0_node_groups"]["node1_groups"] for e in range(g * S, g * S + S)}
+    assert sorted(w[0][sorted(node0)].tolist()) and int(w[0][sorted(node0)].sum()) == 446
+    assert int(w[0][sorted(node1)].sum()) == 587
+    rep = GOLDEN["layer0_replicated"]
+    assert {e for e in node0 if logcnt[e] == 2} == set(rep["node0"])
+    assert {e for e in node1 if logcnt[e] == 2} == set(rep["node1"])
+    l2p = GOLDEN["layer0_log2phy"]
+    assert r["log2phy"][0, 0].tolist() == l2p["expert0"]
+    assert r["log2phy"][0, 1].tolist() == l2p["expert1"]
+
+
+def pin_golden_gpu_loads(o):
+    """Per-GPU loads of layer 0: hierarchical 86.5..156 (mean ~129); global
+    (num_groups = 3) 95.5..138.5."""
+    w, r = _example(o)
+    loads = inv.gpu_loads(w[0], r["phy2log"][0], r["logcnt"][0], 8)
+    g = GOLDEN["layer0_gpu_load_hierarchical"]
+    assert min(loads) == Fraction(g["min"]) and max(loads) == Fraction(g["max"])
+    assert round(sum(loads) / len(loads)) == g["mean_rounded"]
+    gg = GOLDEN["layer0_gpu_load_global_groups3"]
+    w, r = _example(o, groups=gg["num_groups"], X=5)
+    loads = inv.gpu_loads(w[0], r["phy2log"][0], r["logcnt"][0], 8)
+    assert min(loads) == Fraction(gg["min"]) and max(loads) == Fraction(gg["max"])
+    # without replication the hottest expert alone exceeds the balanced maximum
+    hot = GOLDEN["layer0_no_replica_hot_gpu"]
+    assert int(w[0][hot["expert"]]) == hot["load"] > max(loads)
+
+
+def pin_dsv3_shape(o):
+    """DeepSeek-V3 scale: 256 + 32 = 288 physical experts, 9 per GPU on 32 GPUs
+    (hierarchical prefill); 144 GPUs on 18 nodes takes the global policy."""
+    d = GOLDEN["dsv3_shape"]
+    E, G, P = d["E"], d["G"], d["P"]
+    assert E + d["redundant"] == P
+    pre, dec = d["prefill"], d["decode"]
+    assert P // pre["RK"] == pre["per_gpu"]
+    assert o.policy(G, pre["N"])[2] == pre["hierarchical"]
+    assert o.policy(G, dec["N"])[2] == dec["hierarchical"]
+    rng = np.random.default_rng(7)
+    w = rng.zipf(1.5, size=(2, E)).astype(np.int64) * 3
+    for N, RK in ((pre["N"], pre["RK"]), (dec["N"], dec["RK"])):
+        X = 1 + (P - E) // (N if G % N == 0 else 1)
+        r = o.rebalance(w, P, G, N, RK, X)
+        for b in range(2):
+            inv.check_placement(w[b], r["phy2log"][b], r["log2phy"][b], r["logcnt"][b], E, P, G, N, RK)
+            phy = r["phy2log"][b]
+            assert all(len(phy[k * (P // RK):(k + 1) * (P // RK)]) == P // RK for k in range(RK))
+
+
+# ---------------------------------------------------------------- replication
+
+def pin_replication_bruteforce(o):
+    """Greedy replication reaches the smallest possible max load per replica:
+    brute force over every count vector for up to 5 experts and 6 replicas."""
+    rng = np.random.default_rng(11)
+    for trial in range(150):
+        En = int(rng.integers(1, 6))
+        Rn = int(rng.integers(0, 7))
+        u = [int(x) for x in rng.integers(0, 40, size=En)]
+        if trial % 5 == 0:
+            u = [int(x) for x in rng.integers(0, 3, size=En)]     # many ties
+        _, _, count = o.replicate(u, En + Rn)
+        got = max(Fraction(u[i], count[i]) for i in range(En))
+        best = None
+        for extra in itertools.product(range(Rn + 1), repeat=En):
+            if sum(extra) != Rn:
+                continue
+            m = max(Fraction(u[i], 1 + extra[i]) for i in range(En))
+            best = m if best is None else min(best, m)
+        assert got == best, (u, Rn, count)
+        assert sum(count) == En + Rn and min(count) >= 1
+
+
+def pin_replication_dhondt(o):
+    """Closed form: the replicas are the Rn largest of the merged sequences
+    {u_i / k : k >= 1} (D'Hondt apportionment), created in that order, with
+    ties by lower expert index then lower k; replica rank is k."""
+    rng = np.random.default_rng(12)
+    for trial in range(200):
+        En = int(rng.integers(1, 12))
+        Rn = int(rng.integers(0, 20))
+        hi = [3, 50, 10**6, 1 << 40][trial % 4]
+        u = [int(x) for x in rng.integers(0, hi, size=En)]
+        phy, rank, count = o.replicate(u, En + Rn)
+        cands = [(Fraction(u[i], k), i, k) for i in range(En) for k in range(1, Rn + 1)]
+        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        top = cands[:Rn]
+        assert phy[En:] == [c[1] for c in top]
+        assert rank[En:] == [c[2] for c in top]
+        assert phy[:En] == list(range(En)) and rank[:En] == [0] * En
+        assert count == [1 + sum(1 for c in top if c[1] == i) for i in range(En)]
+
+
+# ---------------------------------------------------------------- packing
+
+def pin_packing_closed_forms(o):
+    """Special cases with closed forms.
+
+    * one item per pack: identity;
+    * one pack: everything in pack 0, positions in heaviest-first order;
+    * m packs of q equal positive weights: item t -> pack t % m, position
+      t // m; all-zero weights: item t -> pack t // q, position t % q;
+    * 2m distinct positive weights into m packs of 2: the pack that takes the
+      r-th heaviest item also takes the (2m-1-r)-th ("snake" pairing), and the
+      r-th heaviest goes to pack r.
+    """
+    rng = np.random.default_rng(13)
+    for n in (1, 3, 8):
+        assert o.balanced_packing([int(x) for x in rng.integers(0, 9, n)], n) == (list(range(n)), [0] * n)
+    ws = [5, 9, 9, 1, 7]
+    pack, pos = o.balanced_packing(ws, 1)
+    assert pack == [0] * 5 and pos == [3, 0, 1, 4, 2]
+    for m, q in ((2, 2), (3, 4), (4, 3), (5, 5)):
+        for val in (1, Fraction(7, 3)):
+            pack, pos = o.balanced_packing([val] * (m * q), m)
+            assert pack == [t % m for t in range(m * q)] and pos == [t // m for t in range(m * q)]
+        # all-zero weights never separate the packs: each fills before the next
+        pack, pos = o.balanced_packing([0] * (m * q), m)
+        assert pack == [t // q for t in range(m * q)] and pos == [t % q for t in range(m * q)]
+    for m in (2, 3, 5, 8):
+        for _ in range(20):
+            ws = [int(x) for x in rng.choice(10**6, size=2 * m, replace=False) + 1]
+            pack, pos = o.balanced_packing(ws, m)
+            order = sorted(range(2 * m), key=lambda i: -ws[i])
+            for r in range(m):
+                assert pack[order[r]] == r and pos[order[r]] == 0
+                assert pack[order[2 * m - 1 - r]] == r and pos[order[2 * m - 1 - r]] == 1
+
+
+def pin_identity_cases(o):
+    """One item per pack is the identity, not a greedy pass.
+
+    * G == N: group g goes to node g whatever its load;
+    * P == RK (one physical expert per GPU): GPU k of a node holds the node's
+      k-th physical expert: first the node's experts group by group in slot
+      order, then the replicas in creation order (per-replica value
+      non-increasing)."""
+    rng = np.random.default_rng(14)
+    w = rng.integers(0, 100, size=(3, 16))
+    w[:, 12:] += 1000                                # group 3 heaviest: greedy would move it
+    r = o.rebalance(w, 24, 4, 4, 8, 3)
+    for b in range(3):
+        for g in range(4):
+            assert set(r["phy2log"][b][g * 6:(g + 1) * 6].tolist()) == set(range(g * 4, g * 4 + 4))
+    r = o.rebalance(w, 24, 4, 2, 24, 5)
+    for b in range(3):
+        phy, cnt = r["phy2log"][b], r["logcnt"][b]
+        inv.check_placement(w[b], phy, r["log2phy"][b], cnt, 16, 24, 4, 2, 24)
+        for n in range(2):
+            node = phy[n * 12:(n + 1) * 12].tolist()
+            for s in range(2):
+                blk = node[s * 4:(s + 1) * 4]
+                assert blk[0] % 4 == 0 and blk == list(range(blk[0], blk[0] + 4))
+            reps = node[8:]
+            seen = {}
+            vals = []
+            for e in reps:
+                seen[e] = seen.get(e, 0) + 1
+                vals.append(Fraction(int(w[b][e]), seen[e]))
+            assert vals == sorted(vals, reverse=True)
+            assert all(cnt[e] == 1 + reps.count(e) for e in set(node))
+
+
+def pin_degenerate_loads(o):
+    """All-zero loads: every comparison ties, so groups fill node 0 first
+    (groups 0, 1 on node 0; 2, 3 on node 1) and all redundant slots of a node
+    go to its lowest node-local expert (experts 0 and 8).  All-equal positive loads: the first
+    replica halves an expert's share, so the extras go one each to the lowest
+    node-local experts; with 4 equal groups on 2 nodes, groups 0 and 2 land on
+    node 0 and groups 1 and 3 on node 1 (ties to the lower node), so experts
+    0-3 and 4-7 are the ones copied."""
+    w = np.zeros((1, 16), dtype=np.int64)
+    r = o.rebalance(w, 24, 4, 2, 8, 5)
+    inv.check_placement(w[0], r["phy2log"][0], r["log2phy"][0], r["logcnt"][0], 16, 24, 4, 2, 8)
+    assert r["logcnt"][0].tolist() == [5] + [1] * 7 + [5] + [1] * 7
+    w = np.full((1, 16), 5, dtype=np.int64)
+    r = o.rebalance(w, 24, 4, 2, 8, 5)
+    inv.check_placement(w[0], r["phy2log"][0], r["log2phy"][0], r["logcnt"][0], 16, 24, 4, 2, 8)
+    assert r["logcnt"][0].tolist() == [2] * 8 + [1] * 8
+    w = np.zeros((1, 8), dtype=np.int64)
+    r = o.rebalance(w, 12, 3, 2, 4, 5)                # global: expert 0 gets all 4 extras
+    assert r["logcnt"][0].tolist() == [5, 1, 1, 1, 1, 1, 1, 1]
+
+
+def pin_exact_arithmetic(o):
+    """Loads near 2^30-2^40 that float32 cannot tell apart must still be
+    ordered exactly.
+
+    * 4 experts, one node, 2 GPUs of 2, no replicas: the snake pairing puts the
+      heaviest and the lightest on GPU 0, the 2nd and 3rd on GPU 1, so
+      phy2log = [1st, 4th, 2nd, 3rd] by exact weight;
+    * 2 experts, 3 physical: the only replica goes to the exactly heavier one.
+    """
+    for hi in (1 << 30, (1 << 40) - 4096):
+        w = np.array([[hi - 64, hi - 32, 5, 3], [hi - 32, hi - 64, 3, 5]], dtype=np.int64)
+        r = o.rebalance(w, 4, 1, 1, 2, 1)
+        assert r["phy2log"][0].tolist() == [1, 3, 0, 2]
+        assert r["phy2log"][1].tolist() == [0, 2, 1, 3]
+        w = np.array([[hi - 64, hi - 32], [hi - 32, hi - 64]], dtype=np.int64)
+        r = o.rebalance(w, 3, 1, 1, 1, 2)
+        assert r["logcnt"].tolist() == [[1, 2], [2, 1]]
+    # replica loads w/3 vs w': (3*2^30 + 4)/3 > 2^30 + 1 exactly; in float32
+    # both round to 2^30 and the lower index would win.
+    w = np.array([[(1 << 30) + 1, 3 * (1 << 30) + 4, 1, 1]], dtype=np.int64)
+    _, _, count = o.replicate([int(x) for x in w[0]], 6)
+    assert count == [1, 3, 1, 1]
+    r = o.rebalance(w, 6, 1, 1, 3, 3)
+    # replica loads: e1 x3 at (3*2^30+4)/3 each, e0 at 2^30+1, e2 and e3 at 1;
+    # heaviest-first: e1, e1, e1, e0, e2, e3.  The copies of e1 open GPUs 0,
+    # 1, 2; e0 joins GPU 0 (three equal sums, lowest index); e2 and e3 fill
+    # GPUs 1 and 2.
+    assert r["phy2log"][0].tolist() == [1, 0, 1, 2, 1, 3]
+
+
+def pin_invariants_random(o):
+    """Structural invariants on random problems of many shapes, both policies."""
+    rng = np.random.default_rng(15)
+    shapes = [(16, 4, 2, 8, 24), (12, 4, 2, 8, 16), (12, 3, 2, 8, 16), (32, 8, 4, 8, 48),
+              (24, 6, 4, 8, 32), (64, 4, 1, 8, 80), (20, 5, 5, 10, 30), (18, 9, 3, 3, 27)]
+    for (E, G, N, RK, P) in shapes:
+        Np = N if G % N == 0 else 1
+        X = 1 + (P - E) // Np
+        w = rng.integers(0, 1000, size=(4, E)) * rng.integers(0, 2, size=(4, E))
+        r = o.rebalance(w, P, G, N, RK, X)
+        assert (r["status"] == 0).all()
+        for b in range(4):
+            inv.check_placement(w[b], r["phy2log"][b], r["log2phy"][b], r["logcnt"][b], E, P, G, N, RK)
+
+
+def pin_status_rules(o):
+    """Loads outside [0, 2^40] mark the problem; so does a node whose exact
+    common-denominator pack sums need 127 bits or more.  Marked problems are
+    all -1.  The argument rules follow the pages' divisibility requirements."""
+    w = np.array([[1, 2, 3, 4], [1, -1, 3, 4], [1, 2, 3, (1 << 40) + 1], [1, 2, 3, 1 << 40]], dtype=np.int64)
+    r = o.rebalance(w, 6, 2, 1, 2, 3)
+    assert r["status"].tolist() == [0, 1, 1, 0]
+    assert (r["phy2log"][1] == -1).all() and (r["log2phy"][2] == -1).all() and (r["logcnt"][1] == -1).all()
+    # Loads u_i = (i + 1) * V give final counts exactly i + 1 (every pick has
+    # a value above V, every unpicked candidate equals V), so the node's
+    # denominator is lcm(1..60) and its load sum is 1830 V.
+    for V, want in (((1 << 40) // 60, 2), (1 << 30, 0)):
+        from math import lcm
+        E = 60
+        P = E + sum(range(E))
+        assert (lcm(*range(1, E + 1)) * V * P >= (1 << 127)) == (want == 2)
+        w = np.array([[(i + 1) * V for i in range(E)]], dtype=np.int64)
+        r = o.rebalance(w, P, 1, 1, 10, E)
+        assert r["status"].tolist() == [want]
+        if want == 0:
+            assert r["logcnt"][0].tolist() == list(range(1, E + 1))
+    assert o.argument_error(16, 24, 4, 2, 8, 5) is None
+    assert o.argument_error(15, 24, 4, 2, 8, 5) == "div"        # groups do not divide experts
+    assert o.argument_error(16, 24, 4, 2, 7, 5) == "div"        # GPUs not a multiple of nodes
+    assert o.argument_error(16, 25, 4, 2, 8, 5) == "div"        # physical not a multiple of GPUs
+    assert o.argument_error(16, 8, 4, 2, 8, 5) == "redundancy"
+    assert o.argument_error(16, 24, 4, 2, 8, 4) == "capacity"   # 1 + (24 - 16) / 2 = 5 needed
+    assert o.argument_error(15, 24, 3, 2, 8, 10) is None        # global path: E % G not required
+    assert o.argument_error(15, 24, 3, 2, 8, 9) == "capacity"
+    assert o.argument_error(0, 24, 4, 2, 8, 3) == "arg"
+
+
+# ---------------------------------------------------------------- hist / window / redirect
+
+def pin_hist_bruteforce(o):
+    """Counts equal a plain loop's on small inputs, including out-of-range ids;
+    per layer, counts plus invalid ids equal T*K."""
+    rng = np.random.default_rng(16)
+    for (L, T, K, E) in ((1, 1, 1, 1), (2, 7, 3, 5), (3, 50, 4, 16), (2, 0, 2, 4)):
+        idx = rng.integers(-2, E + 2, size=(L, T, K)).astype(np.int32)
+        cnt, bad = o.load_hist(idx, E)
+        ref = [[0] * E for _ in range(L)]
+        refbad = [0] * L
+        for l in range(L):
+            for t in range(T):
+                for k in range(K):
+                    e = int(idx[l, t, k])
+                    if 0 <= e < E:
+                        ref[l][e] += 1
+                    else:
+                        refbad[l] += 1
+        assert cnt.tolist() == ref and bad.tolist() == refbad
+        assert (cnt.sum(axis=1) + bad == T * K).all()
+
+
+def pin_window(o):
+    """The window is the sum of the last W per-step histograms (all of them
+    while fewer than W exist)."""
+    rng = np.random.default_rng(17)
+    hs = [rng.integers(0, 9, size=(2, 5)) for _ in range(7)]
+    for W in (1, 3, 7, 10):
+        for s in range(1, 8):
+            got = o.window_load(hs[:s], W)
+            want = np.zeros((2, 5), dtype=np.int64)
+            for h in hs[max(0, s - W):s]:
+                want = want + h
+            assert (got == want).all()
+
+
+def pin_redirect(o):
+    """Redirect: every output names a replica of the routed expert; replica r
+    of expert e receives exactly the token rows t with t mod logcnt = r; the
+    loop form and the vectorised form agree; invalid ids give -1."""
+    w = np.array(GOLDEN["inputs"]["weight"], dtype=np.int64)
+    r = o.rebalance(w, 16, 4, 2, 8, 3)
+    rng = np.random.default_rng(18)
+    idx = rng.integers(-1, 13, size=(2, 40, 3)).astype(np.int32)
+    out = o.redirect(idx, r["log2phy"], r["logcnt"])
+    assert out.tolist() == o.redirect_loop(idx.tolist(), r["log2phy"].tolist(), r["logcnt"].tolist())
+    for l in range(2):
+        for t in range(40):
+            for k in range(3):
+                e = int(idx[l, t, k])
+                if not 0 <= e < 12:
+                    assert out[l, t, k] == -1
+                    continue
+                p = int(out[l, t, k])
+                assert r["phy2log"][l, p] == e
+                c = int(r["logcnt"][l, e])
+                assert list(r["log2phy"][l, e, :c]).index(p) == t % c
+
+
+ALL_PINS = [pin_golden_phy2log, pin_golden_layer0, pin_golden_gpu_loads, pin_dsv3_shape,
+            pin_replication_bruteforce, pin_replication_dhondt, pin_packing_closed_forms,
+            pin_identity_cases, pin_degenerate_loads, pin_exact_arithmetic, pin_invariants_random,
+            pin_status_rules,
+            pin_hist_bruteforce, pin_window, pin_redirect]
