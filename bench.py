@@ -1,0 +1,236 @@
+"""Benchmark of the EPLB hot path on one MI355X.
+
+One step = one pass of the whole path over one step of routing ids:
+    eplb_load_hist  (count the step into the window ring, sum the window)
+    eplb_rebalance  (58 DeepSeek-V3-shaped problems: 256 experts in 8 groups,
+                     288 physical on 4 nodes x 8 ranks, hierarchical policy)
+    eplb_redirect   (every (token, k) of the step -> a physical replica)
+on the streaming workload: 58 MoE layers x 2^20 tokens x top-8 int32 ids per
+step (1.95 GB), Zipf(1.1) expert popularity, a 10-step window.  Ten distinct
+steps are generated on the device up front and cycled; inputs are resident
+in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is the histogram + redirect throughput of the
+whole step in GB/s of algorithmic bytes (4 B read per id for the histogram,
+4 B read + 4 B written per id for the redirect) over the step's wall time,
+rebalance included.  The 58-layer rebalance latency is reported next to it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-layers", type=int, default=16,
+                    help="layers of one step the oracle baseline histograms and redirects")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the path on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; EP ranks and nodes are placement "
+              f"parameters, not devices)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_expert_load_eplb_amd as eplb
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    work = wl.STREAM_1M
+    pl = work.placement
+    L, T, K, E, W = work.layers, work.tokens, work.topk, pl.E, work.window
+    X = pl.max_count
+    ids = L * T * K
+    hist_bytes = 4 * ids
+    redir_bytes = 8 * ids
+
+    log(f"generating {W} steps of {L}x{T}x{K} ids on {torch.cuda.get_device_name(dev)}")
+    steps = [wl.routing_step_device(work, s, dev) for s in range(W)]
+    ring = torch.zeros((W, L, E), dtype=torch.int32, device=dev)
+    load = torch.empty((L, E), dtype=torch.int64, device=dev)
+    n_invalid = torch.empty((L,), dtype=torch.int64, device=dev)
+    phy2log = torch.empty((L, pl.P), dtype=torch.int32, device=dev)
+    log2phy = torch.empty((L, E, X), dtype=torch.int32, device=dev)
+    logcnt = torch.empty((L, E), dtype=torch.int32, device=dev)
+    status = torch.empty((L,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(steps[0])
+    placement = (phy2log, log2phy, logcnt, status)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, ev=None):
+        idx = steps[s % W]
+        if ev is not None:
+            ev[0].record(stream)
+        eplb.load_hist(idx, E, ring, s, load, n_invalid)
+        if ev is not None:
+            ev[1].record(stream)
+        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
+        if ev is not None:
+            ev[2].record(stream)
+        eplb.redirect(idx, log2phy, logcnt, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    # warm-up: fills the window once and more
+    nwarm = max(args.warmup, W)
+    for s in range(nwarm):
+        step(s)
+    torch.cuda.synchronize()
+    assert int(status.sum()) == 0, "rebalance reported a failed problem"
+
+    # timed region: K steps, per-call HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(nwarm + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hist_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    reb_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    red_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+
+    # 58-layer rebalance, API call to completion (host clock), median of 50
+    lat = []
+    for _ in range(50):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - a) * 1e6)
+    reb_dev = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
+        e1.record(stream)
+        e1.synchronize()
+        reb_dev.append(e0.elapsed_time(e1) * 1e3)
+
+    avg = lambda xs: sum(xs) / len(xs)
+    redir_gbs = redir_bytes / (avg(red_ms) * 1e-3) / 1e9
+    hist_gbs = hist_bytes / (avg(hist_ms) * 1e-3) / 1e9
+    value = (hist_bytes + redir_bytes) / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "58-layer rebalance latency (us); histogram+redirect GB/s vs HBM peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": nwarm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": work.name,
+            "layers": L, "tokens_per_step": T, "topk": K, "window_steps": W,
+            "experts": E, "groups": pl.G, "nodes": pl.N, "ranks": pl.RK, "physical": pl.P,
+            "policy": "hierarchical", "routing": "Zipf(1.1) over a per-layer permutation, i.i.d. ids",
+            "bytes_per_step": hist_bytes + redir_bytes,
+        },
+        "stages": {
+            "hist_ms": round(avg(hist_ms), 4), "hist_GBps": round(hist_gbs, 1),
+            "hist_frac_of_peak": round(hist_gbs / HBM_PEAK_GBS, 4),
+            "rebalance_ms": round(avg(reb_ms), 4),
+            "redirect_ms": round(avg(red_ms), 4), "redirect_GBps": round(redir_gbs, 1),
+            "redirect_frac_of_peak": round(redir_gbs / HBM_PEAK_GBS, 4),
+            "step_ms_events": round(avg(step_ms), 4),
+        },
+        "rebalance_58_layers": {
+            "shape": "E=256 G=8 N=4 RK=32 P=288 (hierarchical), 58 problems",
+            "device_us_median": round(statistics.median(reb_dev), 2),
+            "api_to_completion_us_median": round(statistics.median(lat), 2),
+            "target_us": 100,
+        },
+        "roofline": {
+            "kernel": "redirect_kernel",
+            "bound": "hbm",
+            "achieved": round(redir_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(redir_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, work, steps[(nwarm + args.steps - 1) % W], load,
+                                              placement, hist_bytes + redir_bytes)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(args, work, idx_dev, load_dev, placement, step_bytes):
+    """The oracle, untuned, on this host: histogram + redirect of a sample of
+    layers of one step, and the full 58-layer rebalance; scaled to one whole
+    step and reported in the same unit as `value`."""
+    import numpy as np
+
+    from oracle import eplb_oracle as ora
+
+    pl = work.placement
+    nl = max(1, min(args.cpu_layers, work.layers))
+    idx_h = idx_dev[:nl].cpu().numpy()
+    load_h = load_dev.cpu().numpy()
+    X = placement[1].shape[2]
+    log(f"cpu baseline: oracle hist + redirect on {nl} layers, rebalance on {work.layers}")
+    t0 = time.perf_counter()
+    cnt, _ = ora.load_hist(idx_h, pl.E)
+    t1 = time.perf_counter()
+    ref = ora.rebalance(load_h, pl.P, pl.G, pl.N, pl.RK, X)
+    t2 = time.perf_counter()
+    ora.redirect(idx_h, ref["log2phy"][:nl], ref["logcnt"][:nl])
+    t3 = time.perf_counter()
+    per_layer = ((t1 - t0) + (t3 - t2)) / nl
+    step_s = per_layer * work.layers + (t2 - t1)
+    return {
+        "value": round(step_bytes / step_s / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one step: histogram and redirect of {nl} of {work.layers} layers "
+                   f"({nl}x2^20x8 ids, numpy, scaled to 58 layers) plus the full 58-layer "
+                   f"exact-rational rebalance; {step_s:.2f} s per step"),
+        "rebalance_58_layers_s": round(t2 - t1, 3),
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,152 @@
+/*
+ * eplb.h -- C ABI of the EPLB hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Three calls make up the path: a per-layer expert-load histogram of top-k
+ * routing ids summed over a window of steps, the batched rebalance that turns
+ * loads into a replica placement (phy2log / log2phy / logcnt), and the
+ * redirect of routed logical ids to physical replicas.
+ *
+ * What each call computes is defined by the EPLB README and its annotated
+ * source on the translation page «DualPipe и EPLB: конвейер в обе стороны и
+ * балансировщик экспертов» (ai.flicky.cc), Part 2 "EPLB"; every declaration
+ * below names the section it follows.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers to contiguous, row-major memory
+ *     that the caller allocates, owns and keeps alive until the work enqueued
+ *     on `stream` has finished.  The library allocates, frees and synchronises
+ *     nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; the return code reports host-side validation and launch
+ *     only.  Calls on different streams may run concurrently provided their
+ *     output buffers do not overlap.
+ *   - A non-zero return code means nothing was enqueued (EPLB_E_HIP: a launch
+ *     failed and earlier kernels of the same call may have run).
+ *   - Conditions only the device can see are reported through output
+ *     arguments (`n_invalid`, `status`), never by faulting.
+ */
+#ifndef EPLB_H_
+#define EPLB_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes (host side) ------------------------------------------ */
+#define EPLB_OK            0  /* enqueued                                          */
+#define EPLB_E_ARG         1  /* NULL pointer or a size out of its range           */
+#define EPLB_E_DIV         2  /* a divisibility rule of the placement is broken    */
+#define EPLB_E_REDUNDANCY  3  /* fewer physical than logical experts (P < E)       */
+#define EPLB_E_CAPACITY    4  /* log2phy width X below 1 + (P - E) / nodes         */
+#define EPLB_E_LIMIT       5  /* problem larger than the kernels' on-chip budget   */
+#define EPLB_E_RANGE       6  /* T * K >= 2^31 (ids per layer must fit int32)      */
+#define EPLB_E_HIP         7  /* a HIP launch failed                               */
+
+/* ---- per-problem status written by eplb_rebalance ------------------------ */
+#define EPLB_S_OK          0  /* placement written                                 */
+#define EPLB_S_BAD_LOAD   16  /* some load < 0 or > 2^40; outputs set to -1        */
+#define EPLB_S_OVERFLOW   17  /* lcm(replica counts of a node) * (node load sum)
+                                 >= 2^127; outputs set to -1                       */
+
+/*
+ * eplb_load_hist -- expert load of one step, and the load over a window.
+ *
+ * Follows: the translator's glossary of Part 2 (the load of an expert is the
+ * number of tokens the router sent to it in the observation period) and the
+ * opening section of Part 2 (load is predicted from historical statistics,
+ * e.g. a moving average).  The window here is a SUM of the last W per-step
+ * histograms; the rebalance only compares loads, so a sum and an average
+ * place experts identically.
+ *
+ *   idx        [L][T][K] int32   logical expert id of each (layer, token, k)
+ *   L, T, K                      layers, tokens, top-k (L, T >= 0, K >= 1,
+ *                                T * K < 2^31)
+ *   E                            logical experts per layer (1 .. 4096)
+ *   ring       [W][L][E] int32   caller-owned history of per-step counts.
+ *                                Zero it once before the first step; this
+ *                                call overwrites slot (step % W) with the
+ *                                counts of `idx` and leaves the other slots.
+ *   W, step                      window length (>= 1) and step number (>= 0)
+ *   load       [L][E] int64      out: sum over all W slots of `ring`
+ *   n_invalid  [L] int64         out: ids of layer l outside [0, E); they are
+ *                                not counted
+ */
+int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                       int32_t* ring, int32_t W, int64_t step,
+                       int64_t* load, int64_t* n_invalid, void* stream);
+
+/*
+ * eplb_rebalance -- replica placement for B independent problems.
+ *
+ * Follows: Part 2 sections "Алгоритм" (hierarchical policy when the number
+ * of nodes divides the number of groups, global policy otherwise), the
+ * flowchart (the global policy is the same routine with one group on one
+ * node), "Интерфейс и пример" (inputs and the meaning of phy2log), and the
+ * appendix's packing, replication and three-step hierarchical routines.
+ *
+ *   load       [B][E] int64      token count per logical expert, 0 .. 2^40
+ *   B                            problems (layers or load snapshots), >= 0
+ *   E, P                         logical and physical experts per problem
+ *   G, N, RK                     expert groups, nodes, ranks (GPUs)
+ *   X                            width of log2phy, >= 1 + (P - E) / N'
+ *                                where N' = N if G % N == 0 else 1
+ *   phy2log    [B][P] int32      out: logical expert held by physical slot
+ *                                p = node*(P/N') + gpu_in_node*(P/RK) + pos
+ *   log2phy    [B][E][X] int32   out: physical slot of replica r of expert e
+ *                                (r = 0 is the original), -1 for r >= logcnt
+ *   logcnt     [B][E] int32      out: replicas of each logical expert (>= 1)
+ *   status     [B] int32         out: EPLB_S_* per problem
+ *
+ * Exact, integer-only semantics (the pages use float32): loads per replica
+ * are compared as exact rationals; sorts are stable (equal values keep
+ * ascending index); ties between packs go to the lowest pack index; a tie in
+ * load per replica goes to the lowest node-local expert index; one item per
+ * pack is the identity assignment.
+ *
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, or a NULL array), EPLB_E_DIV
+ * (E % G on the hierarchical path, RK % N', P % RK), EPLB_E_REDUNDANCY
+ * (P < E), EPLB_E_CAPACITY (X too small), EPLB_E_LIMIT (E > 4096,
+ * P > 8192, X > 65535, a possible replica count above 16128, or a working
+ * set above 64 KiB of LDS), EPLB_E_HIP.
+ */
+int32_t eplb_rebalance(const int64_t* load, int64_t B, int32_t E, int32_t P,
+                       int32_t G, int32_t N, int32_t RK, int32_t X,
+                       int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
+                       int32_t* status, void* stream);
+
+/*
+ * eplb_redirect -- route every (token, k) to a physical replica.
+ *
+ * Follows: the glossary of Part 2 (an expert with two copies gives each about
+ * half of its tokens).  Replica r = t mod logcnt[l][e] of expert
+ * e = idx[l][t][k] serves token row t:
+ *     out[l][t][k] = log2phy[l][e][t mod logcnt[l][e]]
+ * An id outside [0, E), or a count outside [1, X], gives -1.
+ *
+ *   idx        [L][T][K] int32   logical ids (as for eplb_load_hist)
+ *   log2phy    [L][E][X] int32   from eplb_rebalance
+ *   logcnt     [L][E] int32      from eplb_rebalance
+ *   out        [L][T][K] int32   out: physical ids; must not overlap idx
+ */
+int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                      const int32_t* log2phy, const int32_t* logcnt, int32_t X,
+                      int32_t* out, void* stream);
+
+/* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
+const char* eplb_status_string(int32_t code);
+
+/*
+ * eplb_rebalance_lds_bytes -- the LDS working set of one rebalance problem,
+ * in bytes, or a negative EPLB_E_* code if the arguments are invalid.  Host
+ * only; touches no device.  Lets a caller check EPLB_E_LIMIT ahead of time.
+ */
+int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N,
+                                 int32_t RK, int32_t X);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPLB_H_ */

@@ -1,0 +1,171 @@
+"""Python binding of libeplb (the EPLB hot path on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libeplb.so``; this module checks dtypes, devices and contiguity, passes raw
+device pointers and the current HIP stream through the C ABI declared in
+``include/eplb.h``, and raises :class:`EplbError` on a non-zero return code.
+PyTorch supplies device memory and streams.
+
+Importing this package loads the library; if it has not been built
+(``python -m moe_expert_load_eplb_amd.build``) the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeplb.so")
+
+EPLB_OK = 0
+EPLB_E_ARG = 1
+EPLB_E_DIV = 2
+EPLB_E_REDUNDANCY = 3
+EPLB_E_CAPACITY = 4
+EPLB_E_LIMIT = 5
+EPLB_E_RANGE = 6
+EPLB_E_HIP = 7
+EPLB_S_OK = 0
+EPLB_S_BAD_LOAD = 16
+EPLB_S_OVERFLOW = 17
+
+EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
+           "eplb_rebalance_lds_bytes")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m moe_expert_load_eplb_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.eplb_load_hist.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p]
+    lib.eplb_load_hist.restype = i32
+    lib.eplb_rebalance.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, p, p, p]
+    lib.eplb_rebalance.restype = i32
+    lib.eplb_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, p, p]
+    lib.eplb_redirect.restype = i32
+    lib.eplb_status_string.argtypes = [i32]
+    lib.eplb_status_string.restype = ctypes.c_char_p
+    lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.eplb_rebalance_lds_bytes.restype = i64
+    return lib
+
+
+lib = _load()
+
+
+class EplbError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {lib.eplb_status_string(code).decode()} (code {code})")
+
+
+def status_string(code: int) -> str:
+    return lib.eplb_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != EPLB_OK:
+        raise EplbError(code, where)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def load_hist(idx: torch.Tensor, E: int, ring: torch.Tensor, step: int,
+              load: torch.Tensor | None = None, n_invalid: torch.Tensor | None = None):
+    """Count one step's routing ids into ring[step % W] and sum the window.
+
+    idx [L, T, K] int32; ring [W, L, E] int32 (zeroed once by the caller).
+    Returns (load [L, E] int64, n_invalid [L] int64).
+    """
+    if idx.dim() != 3:
+        raise ValueError("idx must be [L, T, K]")
+    L, T, K = idx.shape
+    if ring.dim() != 3 or ring.shape[1] != L or ring.shape[2] != E:
+        raise ValueError(f"ring must be [W, {L}, {E}], got {tuple(ring.shape)}")
+    W = ring.shape[0]
+    dev = idx.device
+    if load is None:
+        load = torch.empty((L, E), dtype=torch.int64, device=dev)
+    if n_invalid is None:
+        n_invalid = torch.empty((L,), dtype=torch.int64, device=dev)
+    if tuple(load.shape) != (L, E) or tuple(n_invalid.shape) != (L,):
+        raise ValueError("load must be [L, E] and n_invalid [L]")
+    rc = lib.eplb_load_hist(_dev(idx, torch.int32, "idx"), L, T, K, E,
+                            _dev(ring, torch.int32, "ring"), W, int(step),
+                            _dev(load, torch.int64, "load"), _dev(n_invalid, torch.int64, "n_invalid"),
+                            _stream(dev))
+    _check(rc, "eplb_load_hist")
+    return load, n_invalid
+
+
+def max_count(E: int, P: int, G: int, N: int) -> int:
+    """Largest replica count a placement can give one expert: 1 + (P - E) / N'."""
+    nodes = N if G % N == 0 else 1
+    return 1 + (P - E) // nodes
+
+
+def rebalance(load: torch.Tensor, P: int, G: int, N: int, RK: int, X: int | None = None,
+              out: tuple | None = None):
+    """Replica placement for every row of ``load`` ([B, E] int64).
+
+    Returns (phy2log [B, P], log2phy [B, E, X], logcnt [B, E], status [B]),
+    all int32.  X defaults to the largest possible count.
+    """
+    if load.dim() != 2:
+        raise ValueError("load must be [B, E]")
+    B, E = load.shape
+    if X is None:
+        X = max(1, max_count(E, P, G, N))
+    dev = load.device
+    if out is None:
+        out = (torch.empty((B, P), dtype=torch.int32, device=dev),
+               torch.empty((B, E, X), dtype=torch.int32, device=dev),
+               torch.empty((B, E), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    phy2log, log2phy, logcnt, status = out
+    if (tuple(phy2log.shape) != (B, P) or tuple(log2phy.shape) != (B, E, X)
+            or tuple(logcnt.shape) != (B, E) or tuple(status.shape) != (B,)):
+        raise ValueError("output shapes must be [B, P], [B, E, X], [B, E], [B]")
+    rc = lib.eplb_rebalance(_dev(load, torch.int64, "load"), B, E, P, G, N, RK, X,
+                            _dev(phy2log, torch.int32, "phy2log"), _dev(log2phy, torch.int32, "log2phy"),
+                            _dev(logcnt, torch.int32, "logcnt"), _dev(status, torch.int32, "status"),
+                            _stream(dev))
+    _check(rc, "eplb_rebalance")
+    return phy2log, log2phy, logcnt, status
+
+
+def redirect(idx: torch.Tensor, log2phy: torch.Tensor, logcnt: torch.Tensor,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Physical replica of every routed (token, k): [L, T, K] int32."""
+    if idx.dim() != 3 or log2phy.dim() != 3 or logcnt.dim() != 2:
+        raise ValueError("idx [L, T, K], log2phy [L, E, X], logcnt [L, E] expected")
+    L, T, K = idx.shape
+    _, E, X = log2phy.shape
+    if log2phy.shape[0] != L or tuple(logcnt.shape) != (L, E):
+        raise ValueError("log2phy / logcnt do not match idx's layers")
+    if out is None:
+        out = torch.empty_like(idx)
+    if out.shape != idx.shape:
+        raise ValueError("out must have idx's shape")
+    rc = lib.eplb_redirect(_dev(idx, torch.int32, "idx"), L, T, K, E,
+                           _dev(log2phy, torch.int32, "log2phy"), _dev(logcnt, torch.int32, "logcnt"), X,
+                           _dev(out, torch.int32, "out"), _stream(idx.device))
+    _check(rc, "eplb_redirect")
+    return out

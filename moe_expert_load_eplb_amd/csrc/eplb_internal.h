@@ -1,0 +1,94 @@
+// Internal declarations shared by the EPLB HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eplb {
+
+typedef unsigned long long u64;
+typedef unsigned __int128 u128;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));   // one 16-byte vector of ids
+
+constexpr int64_t kLoadMax = int64_t(1) << 40;   // largest accepted load
+constexpr int kMaxLdsBytes = 64 * 1024;          // per-workgroup LDS budget
+constexpr int kMaxE = 4096;                      // per-expert LDS tables
+constexpr int kMaxX = 65535;                     // log2phy width
+constexpr int kMaxCount = 16128;                 // replica count bound (< 131^2)
+
+// ---------------------------------------------------------------- helpers
+// Magic numbers for floor(n / d) with 0 <= n < 2^31 and 1 <= d < 2^31
+// (round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994, Thm 4.2 with N = 31):
+// l = ceil(log2 d), m = floor(2^(31+l) / d) + 1 < 2^32, and then
+// floor(n / d) = umulhi(n, m) >> (l - 1) for d >= 2; d = 1 is the identity.
+struct FastDiv {
+  uint32_t mul;
+  int32_t shift;           // l - 1, or -1 for d == 1
+};
+
+__host__ __device__ inline FastDiv fastdiv_make(uint32_t d) {
+  FastDiv f;
+  if (d <= 1) { f.mul = 0; f.shift = -1; return f; }
+  int l = 0;
+  while ((1u << l) < d) ++l;                        // l = ceil(log2 d), 1 <= l <= 31
+  u64 m = ((u64)1 << (31 + l)) / d + 1;
+  f.mul = (uint32_t)m;
+  f.shift = l - 1;
+  return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv_apply(uint32_t n, FastDiv f) {
+  if (f.shift < 0) return n;
+  return (uint32_t)(((u64)n * f.mul) >> 32) >> f.shift;     // v_mul_hi_u32 on the device
+}
+
+// ---------------------------------------------------------------- streaming
+// Work split of a [L][n] int32 stream: each workgroup takes one contiguous
+// chunk of one layer.  Chunk lengths are multiples of 4 ids, so every chunk
+// but the last of a layer covers whole 16-byte vectors when the layer starts
+// 16-byte aligned.
+struct StreamSplit {
+  int64_t per_layer;       // ids per layer (T * K)
+  int64_t chunk;           // ids per workgroup (multiple of 4)
+  int32_t chunks;          // workgroups per layer
+};
+
+StreamSplit plan_stream(int64_t L, int64_t per_layer, int target_blocks, int64_t min_chunk);
+
+// ---------------------------------------------------------------- rebalance
+// Everything the rebalance kernel needs about one problem shape, derived on
+// the host: the effective policy, the per-node sizes, and the byte offsets of
+// every LDS array.
+struct RbPlan {
+  int32_t E, P, Gp, Np, RK, X;
+  int32_t S, En, Pn, Rn, RKn, ppr, gpn;
+  int32_t G2;              // power of two >= Gp (group sort width)
+  int32_t Pn2, logPn2;     // power of two >= Pn (per-node item sort width)
+  int32_t threads;         // workgroup size
+  // LDS byte offsets
+  int32_t o_w, o_wl, o_m2l, o_l2m, o_cnt, o_gsum, o_gnode, o_gslot, o_gsort;
+  int32_t o_rep, o_kexp, o_ikey, o_sort, o_pid, o_emax, o_bigf, o_big, o_nbig;
+  int32_t o_nsum, o_dn, o_psum, o_pcnt, o_flags;
+  int32_t pack_slots;      // packs per wave in the packing scratch
+  int32_t bigw;            // 32-bit words of a node's big-prime presence bitset
+  int32_t bigcap;          // capacity of a node's list of primes above 127
+  int32_t lds_bytes;
+  FastDiv fd_S, fd_En, fd_X;
+};
+
+// Returns 0 and fills `plan`, or an EPLB_E_* code.
+int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X, RbPlan* plan);
+
+// Kernel launchers (return hipSuccess or the launch error).
+hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                       int32_t* ring, int32_t W, int64_t step, int64_t* load,
+                       int64_t* n_invalid, hipStream_t stream);
+hipError_t launch_rebalance(const int64_t* load, int64_t B, const RbPlan& plan,
+                            int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
+                            int32_t* status, hipStream_t stream);
+hipError_t launch_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                           const int32_t* log2phy, const int32_t* logcnt, int32_t X,
+                           int32_t* out, hipStream_t stream);
+
+}  // namespace eplb

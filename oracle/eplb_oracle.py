@@ -51,10 +51,10 @@ import numpy as np
 LOAD_MAX = 1 << 40          # largest accepted load (tokens) of one logical expert
 SUM_LIMIT = 1 << 127        # bound on lcm(counts) * node load sum
 
-# Per-problem device status values (documented in the C header as well).
+# Per-problem status values (the C header documents the same numbers).
 STATUS_OK = 0
-STATUS_BAD_LOAD = 1
-STATUS_OVERFLOW = 2
+STATUS_BAD_LOAD = 16
+STATUS_OVERFLOW = 17
 
 
 # --------------------------------------------------------------------------

@@ -281,16 +281,16 @@ def pin_status_rules(o):
     all -1.  The argument rules follow the pages' divisibility requirements."""
     w = np.array([[1, 2, 3, 4], [1, -1, 3, 4], [1, 2, 3, (1 << 40) + 1], [1, 2, 3, 1 << 40]], dtype=np.int64)
     r = o.rebalance(w, 6, 2, 1, 2, 3)
-    assert r["status"].tolist() == [0, 1, 1, 0]
+    assert r["status"].tolist() == [0, o.STATUS_BAD_LOAD, o.STATUS_BAD_LOAD, 0]
     assert (r["phy2log"][1] == -1).all() and (r["log2phy"][2] == -1).all() and (r["logcnt"][1] == -1).all()
     # Loads u_i = (i + 1) * V give final counts exactly i + 1 (every pick has
     # a value above V, every unpicked candidate equals V), so the node's
     # denominator is lcm(1..60) and its load sum is 1830 V.
-    for V, want in (((1 << 40) // 60, 2), (1 << 30, 0)):
+    for V, want in (((1 << 40) // 60, o.STATUS_OVERFLOW), (1 << 30, 0)):
         from math import lcm
         E = 60
         P = E + sum(range(E))
-        assert (lcm(*range(1, E + 1)) * V * P >= (1 << 127)) == (want == 2)
+        assert (lcm(*range(1, E + 1)) * V * P >= (1 << 127)) == (want != 0)
         w = np.array([[(i + 1) * V for i in range(E)]], dtype=np.int64)
         r = o.rebalance(w, P, 1, 1, 10, E)
         assert r["status"].tolist() == [want]

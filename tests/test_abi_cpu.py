@@ -1,0 +1,150 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/eplb.h declares, and rejects bad arguments on the host with
+the documented codes before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import eplb_oracle as ora
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eplb.h")
+LIB = os.path.join(ROOT, "moe_expert_load_eplb_amd", "libeplb.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libeplb.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(eplb_[a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def header_constants():
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(EPLB_[A-Z_]+)\s+(-?\d+)", open(HEADER).read())}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    lib = ctypes.CDLL(LIB)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.eplb_load_hist.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p]
+    lib.eplb_rebalance.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, p, p, p]
+    lib.eplb_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, p, p]
+    lib.eplb_status_string.restype = ctypes.c_char_p
+    lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
+    lib.eplb_rebalance_lds_bytes.restype = i64
+    return lib
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
+                          "eplb_rebalance_lds_bytes"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
+
+
+def test_codes_match_binding_and_oracle():
+    c = header_constants()
+    assert c["EPLB_OK"] == 0 and len({v for k, v in c.items() if k.startswith("EPLB_E_")}) == 7
+    assert c["EPLB_S_BAD_LOAD"] == ora.STATUS_BAD_LOAD and c["EPLB_S_OVERFLOW"] == ora.STATUS_OVERFLOW
+    src = open(os.path.join(ROOT, "moe_expert_load_eplb_amd", "__init__.py")).read()
+    for k, v in c.items():
+        if k.startswith("EPLB_"):
+            assert re.search(rf"^{k} = {v}$", src, flags=re.M), k
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.eplb_status_string(code)
+    assert b"unknown" in lib.eplb_status_string(99)
+    assert lib.eplb_status_string(16) != lib.eplb_status_string(99)
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("E,P,G,N,RK,X", [
+    (16, 24, 4, 2, 8, 5), (15, 24, 4, 2, 8, 5), (16, 24, 4, 2, 7, 5), (16, 25, 4, 2, 8, 5),
+    (16, 8, 4, 2, 8, 5), (16, 24, 4, 2, 8, 4), (15, 24, 3, 2, 8, 10), (15, 24, 3, 2, 8, 9),
+    (0, 24, 4, 2, 8, 3), (16, 24, 0, 2, 8, 5), (16, 24, 4, 2, 8, 0), (256, 288, 8, 4, 32, 9),
+    (256, 320, 8, 5, 40, 65), (12, 16, 4, 2, 8, 2), (12, 16, 4, 2, 8, 3),
+])
+def test_rebalance_validation_matches_oracle_rules(lib, E, P, G, N, RK, X):
+    """The library's argument rules are the pages' (as the oracle states them)."""
+    want = {None: 0, "arg": 1, "div": 2, "redundancy": 3, "capacity": 4}[ora.argument_error(E, P, G, N, RK, X)]
+    got = lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, X)
+    if want == 0:
+        assert got > 0
+    else:
+        assert got == -want
+        assert lib.eplb_rebalance(FAKE, 1, E, P, G, N, RK, X, FAKE, FAKE, FAKE, FAKE, None) == want
+
+
+def test_rebalance_limits_and_nulls(lib):
+    assert lib.eplb_rebalance(FAKE, -1, 16, 24, 4, 2, 8, 5, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.eplb_rebalance(None, 1, 16, 24, 4, 2, 8, 5, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.eplb_rebalance(FAKE, 1, 16, 24, 4, 2, 8, 5, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.eplb_rebalance(FAKE, 1, 8192, 8192, 1, 1, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == 5
+    assert lib.eplb_rebalance_lds_bytes(4096, 8192, 1, 1, 8, 4097) == -5        # LDS budget
+    # the documented workloads fit
+    for args in [(16, 24, 4, 2, 8, 5), (256, 288, 8, 4, 32, 9), (256, 320, 8, 5, 40, 65),
+                 (512, 640, 16, 8, 64, 17), (256, 288, 8, 18, 144, 33), (60, 1830, 1, 1, 10, 1771)]:
+        assert 0 < lib.eplb_rebalance_lds_bytes(*args) <= 64 * 1024, args
+
+
+def test_gpu_test_shapes_fit(lib):
+    """Every placement shape the GPU parity tests use passes host validation."""
+    import ast
+    src = open(os.path.join(ROOT, "tests", "test_gpu_parity.py")).read()
+    block = src[src.index("@pytest.mark.parametrize(\"shape\", [") + len("@pytest.mark.parametrize(\"shape\", "):]
+    block = block[:block.index("])") + 1]
+    for E, G, N, RK, P in ast.literal_eval(block):
+        X = 1 + (P - E) // (N if G % N == 0 else 1)
+        assert lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, X) > 0, (E, G, N, RK, P)
+
+
+def test_stream_validation(lib):
+    ok = dict(idx=FAKE, L=2, T=10, K=8, E=256)
+    # hist: bad sizes, null buffers, id count per layer >= 2^31
+    assert lib.eplb_load_hist(FAKE, -1, 10, 8, 256, FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 0, 256, FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 8, 0, FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 8, 256, FAKE, 0, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 8, 256, FAKE, 4, -1, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(None, 2, 10, 8, 256, FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 8, 256, None, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.eplb_load_hist(FAKE, 2, 10, 8, 4097, FAKE, 4, 0, FAKE, FAKE, None) == 5
+    assert lib.eplb_load_hist(FAKE, 2, 1 << 28, 8, 256, FAKE, 4, 0, FAKE, FAKE, None) == 6
+    # redirect
+    assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, FAKE, FAKE, 70000, FAKE, None) == 5
+    assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, None, FAKE, 9, FAKE, None) == 1
+    assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, FAKE, FAKE, 9, FAKE, None) == 1     # out == idx
+    assert lib.eplb_redirect(FAKE, 2, (1 << 31) // 8, 8, 256, FAKE, FAKE, 9, FAKE + 64, None) == 6
+    assert ok
+
+
+def test_fastdiv_magic_numbers():
+    """The exact-division magic used for t mod c and t / K: for every divisor
+    up to 2^16 and dividends near the 31-bit edge and near multiples of the
+    divisor, floor(n/d) == (n * m >> 32) >> (l - 1), m = floor(2^(31+l)/d) + 1,
+    l = ceil(log2 d) (Granlund & Montgomery 1994, Thm 4.2, N = 31)."""
+    rng = np.random.default_rng(3)
+    top = (1 << 31) - 1
+    for d in range(2, 1 << 16):
+        l = (d - 1).bit_length()
+        m = (1 << (31 + l)) // d + 1
+        assert m < (1 << 32)
+        k = top // d
+        ns = [0, 1, d - 1, d, d + 1, top, top - 1, k * d, k * d - 1, (k - 1) * d - 1]
+        ns += [int(x) for x in rng.integers(0, top, 4)]
+        for n in ns:
+            assert ((n * m) >> 32) >> (l - 1) == n // d, (d, n)
