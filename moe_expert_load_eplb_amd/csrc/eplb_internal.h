@@ -63,16 +63,12 @@ StreamSplit plan_stream(int64_t L, int64_t per_layer, int target_blocks, int64_t
 struct RbPlan {
   int32_t E, P, Gp, Np, RK, X;
   int32_t S, En, Pn, Rn, RKn, ppr, gpn;
-  int32_t G2;              // power of two >= Gp (group sort width)
-  int32_t Pn2, logPn2;     // power of two >= Pn (per-node item sort width)
+  int32_t KR, KP, KN;      // registers per lane for the sorted experts / GPU packs / node packs
   int32_t threads;         // workgroup size
   // LDS byte offsets
-  int32_t o_w, o_wl, o_m2l, o_l2m, o_cnt, o_gsum, o_gnode, o_gslot, o_gsort;
-  int32_t o_rep, o_kexp, o_ikey, o_sort, o_pid, o_emax, o_bigf, o_big, o_nbig;
-  int32_t o_nsum, o_dn, o_psum, o_pcnt, o_flags;
-  int32_t pack_slots;      // packs per wave in the packing scratch
-  int32_t bigw;            // 32-bit words of a node's big-prime presence bitset
-  int32_t bigcap;          // capacity of a node's list of primes above 127
+  int32_t o_kexp, o_w, o_wl, o_gsum, o_ordk, o_m2l, o_l2m, o_cnt, o_srt;
+  int32_t o_gnode, o_gslot, o_gord, o_gres, o_rep, o_posaux, o_ordr, o_ores, o_rcls;
+  int32_t o_nflag, o_flags;
   int32_t lds_bytes;
   FastDiv fd_S, fd_En, fd_X;
 };

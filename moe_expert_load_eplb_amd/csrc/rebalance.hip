@@ -1,5 +1,6 @@
 // Batched EPLB rebalance: one workgroup per problem (an MoE layer or a load
-// snapshot), the whole problem resident in LDS.
+// snapshot), one wavefront per node, the whole problem resident in LDS and
+// registers.
 //
 // The policy is the one of the EPLB README and its annotated source on the
 // translation page «DualPipe и EPLB: конвейер в обе стороны и балансировщик
@@ -14,21 +15,30 @@
 //   step 3  pack the node's physical experts (load = expert load / count)
 //           onto the node's GPUs the same way as step 1.
 //
-// All arithmetic is integer and exact.  Step 2 compares u_a / c_a with
-// u_b / c_b by cross-multiplication (u <= 2^40, c < 2^13, products < 2^53).
-// Step 3 scales every per-replica load by D = lcm(replica counts of the
-// node), so item keys u * (D / c) and pack sums are exact 128-bit integers;
-// D is built from the prime factorisation of the counts, and a node with
-// D * (node load sum) >= 2^127 marks the problem EPLB_S_OVERFLOW.
+// Exact integer arithmetic.  Step 2 compares u_a / c_a with u_b / c_b by
+// cross-multiplication (u <= 2^40, c <= 16128, products < 2^54).  Step 3
+// scales every per-replica load by D = lcm(replica counts of the node): item
+// keys u * (D / c) and pack sums are exact integers, 64-bit when
+// D * (node load sum) < 2^64, else 128-bit; a node with D * sum >= 2^127
+// marks the problem EPLB_S_OVERFLOW.  D and D / c come from a table of prime
+// powers: D is the product of p over the prime powers p^k that divide some
+// count, and D / c the product over those that do not divide c.
 //
-// Layout in LDS (offsets from RbPlan): loads w[E] and their node-major copy
-// wl[E] ("mlog" order: node n holds wl[n*En .. n*En+En)), the mlog<->logical
-// permutations, per-mlog counts, the replicas created per node, 128-bit keys
-// per expert and per item, per-node sort rows, and the packing scratch.
-//
-// The sequential parts of the method (the greedy packs and the replication
-// rounds) run one wavefront per node with wave-wide reductions; sorts and
-// all elementwise phases use the whole workgroup.
+// The two greedy procedures are sequential chains.  Each runs in one
+// wavefront with its state in registers, kept SORTED across the lanes (the
+// element at position pos lives in register pos / 64 of lane pos % 64):
+//   packing      positions hold packs ordered by (sum, pack index), full
+//                packs last.  An item goes to the pack at position 0; the
+//                updated pack is re-inserted at the position one ballot
+//                counts, and the positions before it move down one lane
+//                (DPP wave_shl).  No reduction tree, no LDS on the chain.
+//   replication  positions hold experts ordered by (load per replica desc,
+//                index asc).  The expert at position 0 gets the replica and
+//                is re-inserted the same way.
+// After replication the experts are already in the order step 3 visits them
+// (per-replica load desc); the stable order of the node's physical experts
+// (equal loads in ascending physical index) follows from prefix sums over
+// that order, so no sort is needed.
 #include "eplb.h"
 #include "eplb_internal.h"
 
@@ -36,12 +46,98 @@ namespace eplb {
 
 namespace {
 
-#define SMALL_PRIMES 2, 3, 5, 7, 11, 13, 17, 19, 23, 29, 31, 37, 41, 43, 47, 53, 59, 61, 67, \
-                     71, 73, 79, 83, 89, 97, 101, 103, 107, 109, 113, 127
-constexpr int kNumSmallPrimes = 31;
-__device__ __constant__ int kSmallPrimes[kNumSmallPrimes] = {SMALL_PRIMES};
+// ---------------------------------------------------------------- prime powers
+// Every prime power q = p^k (k >= 1) up to kMaxCount, ascending, with its
+// prime p and the magic numbers of a division by q.
+struct PrimePowers {
+  uint16_t q[2048];
+  uint16_t p[2048];
+  uint32_t mul[2048];
+  int8_t shift[2048];
+  int count;
+};
 
-// ---------------------------------------------------------------- 128-bit helpers
+constexpr PrimePowers make_prime_powers() {
+  PrimePowers t{};
+  int spf[kMaxCount + 1] = {};               // smallest prime factor
+  for (int i = 2; i <= kMaxCount; ++i) {
+    if (spf[i] == 0) {
+      for (int j = i; j <= kMaxCount; j += i)
+        if (spf[j] == 0) spf[j] = i;
+    }
+  }
+  int n = 0;
+  for (int q = 2; q <= kMaxCount; ++q) {
+    const int p = spf[q];
+    int r = q;
+    while (r % p == 0) r /= p;
+    if (r == 1) {                            // q is a power of p
+      int l = 0;
+      while ((1 << l) < q) ++l;
+      t.q[n] = (uint16_t)q;
+      t.p[n] = (uint16_t)p;
+      t.mul[n] = (uint32_t)((((unsigned long long)1) << (31 + l)) / (unsigned long long)q + 1);
+      t.shift[n] = (int8_t)(l - 1);
+      ++n;
+    }
+  }
+  t.count = n;
+  return t;
+}
+
+__device__ __constant__ PrimePowers kPrimePowers = make_prime_powers();
+
+// ---------------------------------------------------------------- lane helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int shl1(int x) {           // lane i <- lane i + 1
+  return __builtin_amdgcn_update_dpp(0, x, 0x130, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int rdl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ u64 rdl64(u64 x, int l) {
+  const int lo = rdl((int)(uint32_t)x, l);
+  const int hi = rdl((int)(uint32_t)(x >> 32), l);
+  return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ u64 shl1_64(u64 x) {
+  const int lo = shl1((int)(uint32_t)x);
+  const int hi = shl1((int)(uint32_t)(x >> 32));
+  return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ u64 ballot(bool b) { return __ballot(b); }
+// Orders this wavefront's LDS accesses before and after it (no workgroup sync).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// y[pos] = x[pos + 1] over the K registers (pos = r * 64 + lane); the last
+// position gets 0.
+template <int K>
+__device__ __forceinline__ void shift_down(const int (&x)[K], int (&y)[K]) {
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    int v = shl1(x[r]);
+    if (r + 1 < K) {
+      const int carry = rdl(x[r + 1], 0);
+      if (lane_id() == 63) v = carry;
+    }
+    y[r] = v;
+  }
+}
+template <int K>
+__device__ __forceinline__ void shift_down64(const u64 (&x)[K], u64 (&y)[K]) {
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    u64 v = shl1_64(x[r]);
+    if (r + 1 < K) {
+      const u64 carry = rdl64(x[r + 1], 0);
+      if (lane_id() == 63) v = carry;
+    }
+    y[r] = v;
+  }
+}
 
 __device__ __forceinline__ u128 mul_u128_u64(u128 a, u64 b, bool& ovf) {
   const u64 lo = (u64)a;
@@ -54,200 +150,199 @@ __device__ __forceinline__ u128 mul_u128_u64(u128 a, u64 b, bool& ovf) {
   return r;
 }
 
-__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
-  return (u64)__shfl_xor((unsigned long long)v, m);
+__device__ __forceinline__ u64 wave_sum64(u64 v) {
+  for (int off = 32; off > 0; off >>= 1) v += (u64)__shfl_xor((unsigned long long)v, off);
+  return v;
 }
-__device__ __forceinline__ u64 shfl_u64(u64 v, int src) {
-  return (u64)__shfl((unsigned long long)v, src);
+__device__ __forceinline__ int wave_max(int v) {
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+  return v;
 }
-
-template <typename K> struct KeyOps;
-template <> struct KeyOps<u64> {
-  __device__ static u64 max() { return ~0ull; }
-  __device__ static u64 shfl_xor(u64 v, int m) { return shfl_xor_u64(v, m); }
-};
-template <> struct KeyOps<u128> {
-  __device__ static u128 max() { return ~(u128)0; }
-  __device__ static u128 shfl_xor(u128 v, int m) {
-    const u64 lo = shfl_xor_u64((u64)v, m);
-    const u64 hi = shfl_xor_u64((u64)(v >> 64), m);
-    return ((u128)hi << 64) | lo;
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = lane_id();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
   }
-};
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// ---------------------------------------------------------------- sorting
-
-// Bitonic sort of `nseg` independent rows of n2 (a power of two) item ids,
-// stored back to back in `arr`.  `before(seg, a, b)` must be a strict total
-// order on the ids of one row; the whole workgroup takes part.
-template <class Before>
-__device__ void seg_bitonic(int32_t* arr, int nseg, int n2, int log2n2, Before before) {
-  const int total = nseg * n2;
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < total; i += blockDim.x) {
-        const int li = i & (n2 - 1);
-        if ((li & j) == 0) {
-          const int seg = i >> log2n2;
-          const int a = arr[i];
-          const int b = arr[i + j];
-          const bool asc = (li & k) == 0;
-          const bool a_first = before(seg, a, b);
-          if (asc != a_first) {
-            arr[i] = b;
-            arr[i + j] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  return v;
+}
+__device__ __forceinline__ int wave_incl_max(int v) {
+  const int lane = lane_id();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v = max(v, o);
   }
+  return v;
 }
 
 // ---------------------------------------------------------------- greedy packing
-
-// Balanced packing of n items (visited in the order given by `order`) into m
-// packs of `cap` items each, by one wavefront: each item goes into the pack
-// with the smallest sum among packs with room, lowest pack index on ties.
-// Pack p lives in lane p % 64 (sums in psum[], counts in pcnt[], wave-private
-// LDS); each lane caches its best open pack and a wave-wide argmin picks the
-// winner.  result[item] = pack * cap + arrival position.
-template <typename K, class KeyOf>
-__device__ void wave_pack(const int32_t* order, int n, int m, int cap, KeyOf key_of,
-                          int32_t* result, K* psum, int32_t* pcnt) {
+// n items, visited in the order of keys[] (item t's key: KW 64-bit words at
+// keys[t * stride], least significant first), go into m packs of `cap` items:
+// each into the pack with the smallest sum among packs with room, lowest pack
+// index on ties.  res[t] = pack * cap + arrival position of item t.
+// The packs stay sorted across the K registers of the wave (m <= 64 * K).
+template <int K, int KW>
+__device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, int32_t* res) {
   const int lane = lane_id();
-  for (int p = lane; p < m; p += 64) {
-    psum[p] = 0;
-    pcnt[p] = 0;
+  u64 s[KW][K];
+  int ic[K];                                   // pack index << 16 | items in it
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) s[w][r] = pos < m ? 0ull : ~0ull;
+    ic[r] = pos < m ? (pos << 16) : (0x7fff << 16);
   }
-  int m2 = 1;
-  while (m2 < m && m2 < 64) m2 <<= 1;
-  // Lane-local best open pack (sum, index); index INT_MAX marks none.
-  K bs = KeyOps<K>::max();
-  int bp = 0x7fffffff;
-  int bc = 0;
-  for (int p = lane; p < m; p += 64) {
-    if (bp == 0x7fffffff) { bs = 0; bp = p; bc = 0; }   // all sums are 0: lowest own index
-  }
-  for (int t = 0; t < n; ++t) {
-    const int item = order[t];
-    K s = bs;
-    int p = bp;
-    int c = bc;
-    for (int off = 1; off < m2; off <<= 1) {
-      const K os = KeyOps<K>::shfl_xor(s, off);
-      const int op = __shfl_xor(p, off);
-      const int oc = __shfl_xor(c, off);
-      if (os < s || (os == s && op < p)) { s = os; p = op; c = oc; }
-    }
-    // Lanes 0 .. m2-1 now agree on the winner (p, c); it belongs to lane p % 64.
-    if (lane == 0) result[item] = p * cap + c;
-    if (lane == (p & 63) && p != 0x7fffffff) {
-      psum[p] += key_of(item);
-      pcnt[p] = c + 1;
-      bs = KeyOps<K>::max();
-      bp = 0x7fffffff;
-      bc = 0;
-      for (int q = lane; q < m; q += 64) {
-        const int qc = pcnt[q];
-        if (qc < cap) {
-          const K qs = psum[q];
-          if (qs < bs || (qs == bs && q < bp)) { bs = qs; bp = q; bc = qc; }
-        }
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int tn = n - t0 < 64 ? n - t0 : 64;
+    u64 kk[KW];
+#pragma unroll
+    for (int w = 0; w < KW; ++w) kk[w] = lane < tn ? keys[(int64_t)(t0 + lane) * stride + w] : 0ull;
+    int rec = 0;
+    for (int j = 0; j < tn; ++j) {
+      const int ic0 = rdl(ic[0], 0);
+      const int c0 = ic0 & 0xffff;
+      const int id0 = ic0 & ~0xffff;
+      if (lane == j) rec = (ic0 >> 16) * cap + c0;
+      u64 nk[KW];
+      u64 carry = 0;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        const u64 a = rdl64(s[w][0], 0);
+        const u64 t = a + rdl64(kk[w], j);
+        const u64 c1 = t < a ? 1ull : 0ull;
+        nk[w] = t + carry;
+        carry = c1 | (nk[w] < t ? 1ull : 0ull);
+      }
+      const int nc = c0 + 1;
+      if (nc == cap) {
+#pragma unroll
+        for (int w = 0; w < KW; ++w) nk[w] = ~0ull;
+      }
+      const int nic = id0 | nc;
+      int q = 0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        bool lt = (ic[r] & ~0xffff) < id0;        // decides equal sums
+#pragma unroll
+        for (int w = 0; w < KW; ++w) lt = (s[w][r] < nk[w]) || (s[w][r] == nk[w] && lt);
+        u64 mask = ballot(lt);
+        if (r == 0) mask &= ~1ull;
+        q += __popcll(mask);
+      }
+      u64 sd[KW][K];
+      int icd[K];
+#pragma unroll
+      for (int w = 0; w < KW; ++w) shift_down64<K>(s[w], sd[w]);
+      shift_down<K>(ic, icd);
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int pos = r * 64 + lane;
+        const bool below = pos < q;
+        const bool at = pos == q;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) s[w][r] = below ? sd[w][r] : (at ? nk[w] : s[w][r]);
+        ic[r] = below ? icd[r] : (at ? nic : ic[r]);
       }
     }
+    if (lane < tn) res[t0 + lane] = rec;
   }
 }
 
 // ---------------------------------------------------------------- replication
-
-// Grow the node's En experts to En + Rn physical ones, one replica at a time,
-// each to the expert with the highest load per replica u[i] / c[i] (lowest
-// index on ties).  c[] enters as all ones.  rep[r] = expert | (rank << 16) of
-// the r-th replica created (its rank is the expert's count before it).
-// Also returns the node's load sum.
-__device__ u64 wave_replicate(const u64* u, int32_t* c, int En, int Rn, int32_t* rep) {
+// The node's experts sorted by (load desc, index asc), all counts 1, are in
+// (u, ci) (ci = count << 16 | local index); positions >= En hold the
+// sentinel (0, 1 << 16 | 0xffff), which never moves ahead of an expert.
+// Rn times: the expert at position 0 (highest load per replica, lowest index
+// on ties) gets a replica and moves to its new place.
+// rep[r] = local index | rank << 16 of the r-th replica created.
+template <int K>
+__device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep) {
   const int lane = lane_id();
-  // (u, c, i) is better than (u', c', i') if u * c' > u' * c, or equal and i < i'.
-  u64 bu = 0;
-  int bc = 1;
-  int bi = 0x7fffffff;
-  u64 sum = 0;
-  for (int i = lane; i < En; i += 64) {
-    const u64 ui = u[i];
-    sum += ui;
-    if (bi == 0x7fffffff || ui * (u64)bc > bu) { bu = ui; bc = 1; bi = i; }
-  }
-  for (int off = 32; off > 0; off >>= 1) sum += shfl_xor_u64(sum, off);
-  for (int r = 0; r < Rn; ++r) {
-    u64 xu = bu;
-    int xc = bc;
-    int xi = bi;
-    for (int off = 1; off < 64; off <<= 1) {
-      const u64 ou = shfl_xor_u64(xu, off);
-      const int oc = __shfl_xor(xc, off);
-      const int oi = __shfl_xor(xi, off);
-      const u64 lhs = ou * (u64)xc;
-      const u64 rhs = xu * (u64)oc;
-      if (lhs > rhs || (lhs == rhs && oi < xi)) { xu = ou; xc = oc; xi = oi; }
-    }
-    if (lane == 0) rep[r] = xi | (xc << 16);
-    if (lane == (xi & 63)) {
-      c[xi] = xc + 1;
-      bu = 0;
-      bc = 1;
-      bi = 0x7fffffff;
-      for (int i = lane; i < En; i += 64) {
-        const u64 ui = u[i];
-        const int ci = c[i];
-        if (bi == 0x7fffffff || ui * (u64)bc > bu * (u64)ci) { bu = ui; bc = ci; bi = i; }
+  for (int r0 = 0; r0 < Rn; r0 += 64) {
+    const int tn = Rn - r0 < 64 ? Rn - r0 : 64;
+    int rec = 0;
+    for (int j = 0; j < tn; ++j) {
+      const u64 u0 = rdl64(u[0], 0);
+      const int ci0 = rdl(ci[0], 0);
+      const int c0 = ci0 >> 16;
+      const int i0 = ci0 & 0xffff;
+      if (lane == j) rec = i0 | (c0 << 16);
+      const int nc = c0 + 1;
+      const int nci = (nc << 16) | i0;
+      int q = 0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const u64 lhs = u[r] * (u64)(uint32_t)nc;             // u_p / c_p  vs  u0 / nc
+        const u64 rhs = u0 * (u64)(uint32_t)(ci[r] >> 16);
+        const bool before = lhs > rhs || (lhs == rhs && (ci[r] & 0xffff) < i0);
+        u64 mask = ballot(before);
+        if (r == 0) mask &= ~1ull;
+        q += __popcll(mask);
+      }
+      u64 ud[K];
+      int cid[K];
+      shift_down64<K>(u, ud);
+      shift_down<K>(ci, cid);
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int pos = r * 64 + lane;
+        const bool below = pos < q;
+        const bool at = pos == q;
+        u[r] = below ? ud[r] : (at ? u0 : u[r]);
+        ci[r] = below ? cid[r] : (at ? nci : ci[r]);
       }
     }
+    if (lane < tn) rep[r0 + lane] = rec;
   }
-  return sum;
 }
 
-// Exponent of each prime up to 127 in c; returns the cofactor.  Counts are at
-// most kMaxCount < 131^2, so once the primes below 131 are divided out the
-// cofactor is 1 or a single prime, which keeps the lcm built from these
-// factorisations exact.
-__device__ __forceinline__ int factor_small(int c, int* ex) {
-  const int primes[kNumSmallPrimes] = {SMALL_PRIMES};
-#pragma unroll
-  for (int k = 0; k < kNumSmallPrimes; ++k) {
-    const int q = primes[k];
-    int e = 0;
-    while (c % q == 0) { c /= q; ++e; }
-    ex[k] = e;
-  }
-  return c;
-}
-
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- LDS carving
 
 struct Smem {
-  u64* w; u64* wl; int32_t* m2l; int32_t* l2m; int32_t* cnt;
-  u64* gsum; int32_t* gnode; int32_t* gslot; int32_t* gsort;
-  int32_t* rep; u128* kexp; u128* ikey; int32_t* sort; int32_t* pid;
-  int32_t* emax; int32_t* bigf; int32_t* big; int32_t* nbig; u64* nsum; u128* dn;
-  unsigned char* psum; int32_t* pcnt; int32_t* flags;
+  u128* kexp;      // [E]   step-3 key per mlog expert
+  u64* w;          // [E]   loads, logical order
+  u64* wl;         // [E]   loads, mlog order (node n: [n*En, n*En+En))
+  u64* gsum;       // [Gp]
+  u64* ordk;       // [nscr][max(Pn, Gp)][2]  per-wave item keys in visiting order
+  int32_t* m2l;    // [E]
+  int32_t* l2m;    // [E]
+  int32_t* cnt;    // [E]   replica count per mlog expert
+  int32_t* srt;    // [E]   per node: local expert index at each sorted position
+  int32_t* gnode;  // [Gp]
+  int32_t* gslot;  // [Gp]
+  int32_t* gord;   // [Gp]  groups, heaviest first
+  int32_t* gres;   // [Gp]  packing result per visiting rank
+  int32_t* rep;    // [Np][Rn]
+  int32_t* posaux; // [nscr][3 * En]  per wave: class start, item offset, position of expert
+  int32_t* ordr;   // [nscr][Pn]  per wave: item (logical expert | rank << 16) in visiting order
+  int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
+  int32_t* rcls;   // [nscr][Rn]  per wave: class of each replica
+  int32_t* nflag;  // [Np]  1 when the node's sums fit 64 bits
+  int32_t* flags;  // [4]
 };
 
 __device__ Smem carve(unsigned char* base, const RbPlan& p) {
   Smem s;
-  s.w = (u64*)(base + p.o_w);          s.wl = (u64*)(base + p.o_wl);
-  s.m2l = (int32_t*)(base + p.o_m2l);  s.l2m = (int32_t*)(base + p.o_l2m);
-  s.cnt = (int32_t*)(base + p.o_cnt);  s.gsum = (u64*)(base + p.o_gsum);
-  s.gnode = (int32_t*)(base + p.o_gnode); s.gslot = (int32_t*)(base + p.o_gslot);
-  s.gsort = (int32_t*)(base + p.o_gsort); s.rep = (int32_t*)(base + p.o_rep);
-  s.kexp = (u128*)(base + p.o_kexp);   s.ikey = (u128*)(base + p.o_ikey);
-  s.sort = (int32_t*)(base + p.o_sort); s.pid = (int32_t*)(base + p.o_pid);
-  s.emax = (int32_t*)(base + p.o_emax); s.bigf = (int32_t*)(base + p.o_bigf);
-  s.big = (int32_t*)(base + p.o_big);  s.nbig = (int32_t*)(base + p.o_nbig);
-  s.nsum = (u64*)(base + p.o_nsum);    s.dn = (u128*)(base + p.o_dn);
-  s.psum = base + p.o_psum;            s.pcnt = (int32_t*)(base + p.o_pcnt);
+  s.kexp = (u128*)(base + p.o_kexp);
+  s.w = (u64*)(base + p.o_w);
+  s.wl = (u64*)(base + p.o_wl);
+  s.gsum = (u64*)(base + p.o_gsum);
+  s.ordk = (u64*)(base + p.o_ordk);
+  s.m2l = (int32_t*)(base + p.o_m2l);
+  s.l2m = (int32_t*)(base + p.o_l2m);
+  s.cnt = (int32_t*)(base + p.o_cnt);
+  s.srt = (int32_t*)(base + p.o_srt);
+  s.gnode = (int32_t*)(base + p.o_gnode);
+  s.gslot = (int32_t*)(base + p.o_gslot);
+  s.gord = (int32_t*)(base + p.o_gord);
+  s.gres = (int32_t*)(base + p.o_gres);
+  s.rep = (int32_t*)(base + p.o_rep);
+  s.posaux = (int32_t*)(base + p.o_posaux);
+  s.ordr = (int32_t*)(base + p.o_ordr);
+  s.ores = (int32_t*)(base + p.o_ores);
+  s.rcls = (int32_t*)(base + p.o_rcls);
+  s.nflag = (int32_t*)(base + p.o_nflag);
   s.flags = (int32_t*)(base + p.o_flags);
   return s;
 }
@@ -255,12 +350,220 @@ __device__ Smem carve(unsigned char* base, const RbPlan& p) {
 __device__ void write_failed(const RbPlan& p, int64_t b, int32_t code, int32_t* phy2log,
                              int32_t* log2phy, int32_t* logcnt, int32_t* status) {
   for (int i = threadIdx.x; i < p.P; i += blockDim.x) phy2log[b * p.P + i] = -1;
-  for (int i = threadIdx.x; i < p.E * p.X; i += blockDim.x) log2phy[b * p.E * p.X + i] = -1;
+  for (int i = threadIdx.x; i < p.E * p.X; i += blockDim.x) log2phy[b * p.E * (int64_t)p.X + i] = -1;
   for (int i = threadIdx.x; i < p.E; i += blockDim.x) logcnt[b * p.E + i] = -1;
   if (threadIdx.x == 0) status[b] = code;
 }
 
-__global__ __launch_bounds__(1024) void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
+// ---------------------------------------------------------------- per-node phases
+
+// Step 2 and the denominators of node n (one wave): the node's experts in
+// load order go through replication; counts, the final order and the exact
+// step-3 keys are stored.
+template <int K>
+__device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
+  const int lane = lane_id();
+  const int En = p.En;
+  u64 u[K];
+  int ci[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    if (pos < En) {
+      const int i = s.srt[n * En + pos];
+      u[r] = s.wl[n * En + i];
+      ci[r] = (1 << 16) | i;
+    } else {
+      u[r] = 0;
+      ci[r] = (1 << 16) | 0xffff;
+    }
+  }
+  replicate_sorted<K>(u, ci, p.Rn, s.rep + n * p.Rn);
+
+  u64 sum = 0;
+  int cmax = 1;
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    if (pos < En) {
+      const int i = ci[r] & 0xffff;
+      const int c = ci[r] >> 16;
+      s.cnt[n * En + i] = c;
+      s.srt[n * En + pos] = i;
+      sum += u[r];
+      cmax = max(cmax, c);
+    }
+  }
+  sum = wave_sum64(sum);
+  cmax = wave_max(cmax);
+
+  // D = product of p over the prime powers p^k <= cmax dividing some count;
+  // Q = D / c = product of p over those not dividing c.
+  u128 D = 1;
+  u128 Q[K];
+  bool ovf = false;
+#pragma unroll
+  for (int r = 0; r < K; ++r) Q[r] = 1;
+  for (int t = 0; t < kPrimePowers.count && (int)kPrimePowers.q[t] <= cmax; ++t) {
+    const uint32_t q = kPrimePowers.q[t];
+    const u64 pr = kPrimePowers.p[t];
+    const FastDiv fd{kPrimePowers.mul[t], kPrimePowers.shift[t]};
+    bool div[K];
+    u64 any = 0;
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      const uint32_t c = (uint32_t)(ci[r] >> 16);
+      div[r] = pos < En && fastdiv_apply(c, fd) * q == c;
+      any |= ballot(div[r]);
+    }
+    if (any != 0) {
+      D = mul_u128_u64(D, pr, ovf);
+#pragma unroll
+      for (int r = 0; r < K; ++r)
+        if (!div[r]) Q[r] = mul_u128_u64(Q[r], pr, ovf);
+    }
+  }
+  const u128 total = mul_u128_u64(D, sum, ovf);
+  if (lane == 0) {
+    if (ovf || (total >> 127) != 0) s.flags[0] = EPLB_S_OVERFLOW;
+    s.nflag[n] = (u64)(total >> 64) == 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    if (pos < En) {
+      bool o2 = false;                 // u * D / c <= D * sum < 2^127 once checked
+      s.kexp[n * En + (ci[r] & 0xffff)] = mul_u128_u64(Q[r], u[r], o2);
+    }
+  }
+}
+
+// Step 3 of node n (one wave, scratch slot ws): the visiting order of the
+// node's physical experts, packing onto its GPUs, and the outputs.
+template <int K, int KP>
+__device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
+                           int32_t* o_phy, int32_t* o_l2p, int32_t* o_cnt) {
+  const int lane = lane_id();
+  const int En = p.En, Pn = p.Pn, Rn = p.Rn;
+  const int32_t* rep = s.rep + n * Rn;
+  const int32_t* m2l = s.m2l + n * En;
+
+  if (p.ppr == 1) {
+    // One physical expert per GPU: item j sits on GPU j (identity).
+    for (int j = lane; j < Pn; j += 64) {
+      int li, rk;
+      if (j < En) { li = j; rk = 0; }
+      else { const int v = rep[j - En]; li = v & 0xffff; rk = v >> 16; }
+      const int e = m2l[li];
+      const int pid = n * Pn + j;
+      o_phy[pid] = e;
+      o_l2p[(int64_t)e * p.X + rk] = pid;
+    }
+  } else {
+    int32_t* ordr = s.ordr + ws * Pn;
+    int32_t* ores = s.ores + ws * Pn;
+    u64* ordk = s.ordk + (int64_t)ws * (Pn > p.Gp ? Pn : p.Gp) * 2;
+    int32_t* cstart = s.posaux + ws * 3 * En;   // class start of each position
+    int32_t* coff = cstart + En;                 // item offset of each position
+    int32_t* posof = coff + En;                  // position of each local expert
+    int32_t* rcls = s.rcls + ws * (Rn > 0 ? Rn : 1);
+    const bool wide = s.nflag[n] == 0;
+
+    // positions in the final order: (u, c, local index)
+    u64 u[K];
+    int c[K], li[K];
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      if (pos < En) {
+        li[r] = s.srt[n * En + pos];
+        u[r] = s.wl[n * En + li[r]];
+        c[r] = s.cnt[n * En + li[r]];
+      } else {
+        li[r] = 0; u[r] = 0; c[r] = 0;
+      }
+    }
+    // A class is a run of positions with equal load per replica.  Its items
+    // in visiting order: the originals (ascending local index, which is
+    // ascending position), then the replicas of its experts in creation order.
+    int carry_off = 0, carry_start = 0;
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      u64 pu = (u64)__shfl_up((unsigned long long)u[r], 1);
+      int pc = __shfl_up(c[r], 1);
+      if (r > 0) {
+        const u64 lu = rdl64(u[r - 1], 63);
+        const int lc = rdl(c[r - 1], 63);
+        if (lane == 0) { pu = lu; pc = lc; }
+      }
+      const bool tie = pos > 0 && pos < En && u[r] * (u64)(uint32_t)pc == pu * (u64)(uint32_t)c[r];
+      const int st = max(wave_incl_max((pos < En && !tie) ? pos : -1), carry_start);
+      const int incl = wave_incl_sum(pos < En ? c[r] : 0) + carry_off;
+      if (pos < En) {
+        cstart[pos] = st;
+        coff[pos] = incl - c[r];
+        posof[li[r]] = pos;
+      }
+      carry_off = rdl(incl, 63);
+      carry_start = rdl(st, 63);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < K; ++r) {              // originals
+      const int pos = r * 64 + lane;
+      if (pos < En) {
+        const int st = cstart[pos];
+        const int rank = coff[st] + (pos - st);
+        ordr[rank] = m2l[li[r]];
+        const u128 key = s.kexp[n * En + li[r]];
+        ordk[rank * 2] = (u64)key;
+        ordk[rank * 2 + 1] = (u64)(key >> 64);
+      }
+    }
+    for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]];
+    wave_lds_sync();
+    for (int rr = lane; rr < Rn; rr += 64) {   // replicas
+      const int v = rep[rr];
+      const int cls = rcls[rr];
+      int before = 0;
+      for (int r2 = 0; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
+      int size = 1;
+      while (cls + size < En && cstart[cls + size] == cls) ++size;
+      const int rank = coff[cls] + size + before;
+      const int li_r = v & 0xffff;
+      ordr[rank] = m2l[li_r] | (v & ~0xffff);
+      const u128 key = s.kexp[n * En + li_r];
+      ordk[rank * 2] = (u64)key;
+      ordk[rank * 2 + 1] = (u64)(key >> 64);
+    }
+    wave_lds_sync();
+    if (wide) pack_sorted<KP, 2>(ordk, 2, Pn, p.RKn, p.ppr, ores);
+    else pack_sorted<KP, 1>(ordk, 2, Pn, p.RKn, p.ppr, ores);
+    wave_lds_sync();
+    for (int t = lane; t < Pn; t += 64) {
+      const int v = ordr[t];
+      const int e = v & 0xffff;
+      const int rk = v >> 16;
+      const int pid = n * Pn + ores[t];
+      o_phy[pid] = e;
+      o_l2p[(int64_t)e * p.X + rk] = pid;
+    }
+  }
+  // counts, and -1 beyond them in log2phy, for the node's experts
+  for (int i = lane; i < En; i += 64) {
+    const int e = m2l[i];
+    const int c = s.cnt[n * En + i];
+    o_cnt[e] = c;
+    for (int k = c; k < p.X; ++k) o_l2p[(int64_t)e * p.X + k] = -1;
+  }
+}
+
+// ---------------------------------------------------------------- kernel
+
+template <int KR, int KP>
+__global__ __launch_bounds__(512) void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
                                                          int32_t* __restrict__ phy2log,
                                                          int32_t* __restrict__ log2phy,
                                                          int32_t* __restrict__ logcnt,
@@ -295,30 +598,34 @@ __global__ __launch_bounds__(1024) void rebalance_kernel(const int64_t* __restri
   } else {
     for (int g = wid; g < p.Gp; g += NW) {
       u64 sum = 0;
-      for (int j = lane; j < p.S; j += 64) sum += s.w[(int64_t)g * p.S + j];
-      for (int off = 32; off > 0; off >>= 1) sum += shfl_xor_u64(sum, off);
+      for (int j = lane; j < p.S; j += 64) sum += s.w[g * p.S + j];
+      sum = wave_sum64(sum);
       if (lane == 0) s.gsum[g] = sum;
     }
-    for (int i = tid; i < p.G2; i += NT) s.gsort[i] = i;
     __syncthreads();
-    const int Gp = p.Gp;
-    const u64* gsum = s.gsum;
-    int log2g = 0;
-    while ((1 << log2g) < p.G2) ++log2g;
-    seg_bitonic(s.gsort, 1, p.G2, log2g, [=](int, int a, int b2) {
-      if (a >= Gp || b2 >= Gp) return (a < Gp) || (b2 >= Gp && a < b2);
-      const u64 wa = gsum[a], wb = gsum[b2];
-      return wa > wb || (wa == wb && a < b2);
-    });
-    if (wid == 0) {
-      wave_pack<u64>(s.gsort, Gp, p.Np, p.gpn, [=](int item) { return gsum[item]; }, s.gnode,
-                     (u64*)s.psum, s.pcnt);
+    // heaviest first, equal loads in ascending group index (rank by counting)
+    for (int g = tid; g < p.Gp; g += NT) {
+      const u64 wg = s.gsum[g];
+      int rank = 0;
+      for (int h = 0; h < p.Gp; ++h) {
+        const u64 wh = s.gsum[h];
+        rank += (wh > wg || (wh == wg && h < g)) ? 1 : 0;
+      }
+      s.gord[rank] = g;
     }
     __syncthreads();
-    for (int g = tid; g < Gp; g += NT) {
-      const int r = s.gnode[g];
-      s.gnode[g] = r / p.gpn;
-      s.gslot[g] = r - (r / p.gpn) * p.gpn;
+    if (wid == 0) {
+      for (int t = lane; t < p.Gp; t += 64) s.ordk[t] = s.gsum[s.gord[t]];
+      wave_lds_sync();
+      if (p.KN == 1) pack_sorted<1, 1>(s.ordk, 1, p.Gp, p.Np, p.gpn, s.gres);
+      else pack_sorted<8, 1>(s.ordk, 1, p.Gp, p.Np, p.gpn, s.gres);
+      wave_lds_sync();
+      for (int t = lane; t < p.Gp; t += 64) {
+        const int g = s.gord[t];
+        const int v = s.gres[t];
+        s.gnode[g] = v / p.gpn;
+        s.gslot[g] = v - (v / p.gpn) * p.gpn;
+      }
     }
   }
   __syncthreads();
@@ -331,152 +638,62 @@ __global__ __launch_bounds__(1024) void rebalance_kernel(const int64_t* __restri
     s.m2l[m] = e;
     s.l2m[e] = m;
     s.wl[m] = s.w[e];
-    s.cnt[m] = 1;
-  }
-  // clear the per-node factorisation tables
-  for (int i = tid; i < p.Np * kNumSmallPrimes; i += NT) s.emax[i] = 0;
-  for (int i = tid; i < p.Np * p.bigw; i += NT) s.bigf[i] = 0;
-  for (int i = tid; i < p.Np; i += NT) s.nbig[i] = 0;
-  __syncthreads();
-
-  // ---- step 2: replicas within each node (one wave per node)
-  for (int n = wid; n < p.Np; n += NW) {
-    const u64 sum = wave_replicate(s.wl + n * p.En, s.cnt + n * p.En, p.En, p.Rn, s.rep + n * p.Rn);
-    if (lane == 0) s.nsum[n] = sum;
   }
   __syncthreads();
-
-  // ---- step 3a: D_n = lcm of the node's counts, from their factorisations
+  // experts of each node by (load desc, local index asc)
   for (int m = tid; m < p.E; m += NT) {
-    const int c = s.cnt[m];
-    if (c > 1) {
-      const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-      int ex[kNumSmallPrimes];
-      const int cof = factor_small(c, ex);
-#pragma unroll
-      for (int k = 0; k < kNumSmallPrimes; ++k)
-        if (ex[k]) atomicMax(&s.emax[n * kNumSmallPrimes + k], ex[k]);
-      if (cof > 1) {
-        // cof is a prime above 127; list it once per node (bit cof of the
-        // node's presence bitset), the list holds at most bigcap entries
-        // because only counts >= 131 have such a factor.
-        const unsigned bit = 1u << (cof & 31);
-        if ((atomicOr((unsigned*)&s.bigf[n * p.bigw + (cof >> 5)], bit) & bit) == 0) {
-          const int slot = atomicAdd(&s.nbig[n], 1);
-          s.big[n * p.bigcap + slot] = cof;
-        }
-      }
+    const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
+    const int i = m - n * p.En;
+    const u64* wn = s.wl + n * p.En;
+    const u64 wi = wn[i];
+    int rank = 0;
+    for (int h = 0; h < p.En; ++h) {
+      const u64 wh = wn[h];
+      rank += (wh > wi || (wh == wi && h < i)) ? 1 : 0;
     }
+    s.srt[n * p.En + rank] = i;
   }
   __syncthreads();
-  for (int n = tid; n < p.Np; n += NT) {
-    bool ovf = false;
-    u128 d = 1;
-    for (int k = 0; k < kNumSmallPrimes; ++k)
-      for (int e = s.emax[n * kNumSmallPrimes + k]; e > 0; --e) d = mul_u128_u64(d, (u64)kSmallPrimes[k], ovf);
-    for (int q = 0; q < s.nbig[n]; ++q) d = mul_u128_u64(d, (u64)s.big[n * p.bigcap + q], ovf);
-    const u128 tot = mul_u128_u64(d, s.nsum[n], ovf);
-    if (ovf || (tot >> 127) != 0) s.flags[0] = EPLB_S_OVERFLOW;
-    s.dn[n] = d;
-  }
+
+  // ---- step 2 and the denominators, one wave per node
+  for (int n = wid; n < p.Np; n += NW) node_replicate<KR>(p, s, n);
   __syncthreads();
   if (s.flags[0] != 0) {
     write_failed(p, b, s.flags[0], phy2log, log2phy, logcnt, status);
     return;
   }
 
-  // ---- step 3b: exact scaled loads: expert key u * (D_n / c), item keys
-  for (int m = tid; m < p.E; m += NT) {
-    const int c = s.cnt[m];
-    const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-    u128 q = s.dn[n];
-    if (c > 1) {
-      int ex[kNumSmallPrimes];
-      const int cof = factor_small(c, ex);
-      bool ovf = false;
-      q = 1;
-      for (int k = 0; k < kNumSmallPrimes; ++k)
-        for (int e = s.emax[n * kNumSmallPrimes + k] - ex[k]; e > 0; --e)
-          q = mul_u128_u64(q, (u64)kSmallPrimes[k], ovf);
-      for (int i = 0; i < s.nbig[n]; ++i) {
-        const int bq = s.big[n * p.bigcap + i];
-        if (bq != cof) q = mul_u128_u64(q, (u64)bq, ovf);
-      }
-    }
-    bool ovf = false;
-    s.kexp[m] = mul_u128_u64(q, s.wl[m], ovf);     // <= D_n * u < 2^127
-  }
-  __syncthreads();
-  for (int i = tid; i < p.Np * p.Pn2; i += NT) {
-    const int n = i >> p.logPn2;
-    const int j = i & (p.Pn2 - 1);
-    s.sort[i] = j;
-    if (j < p.Pn) {
-      const int li = j < p.En ? j : (s.rep[n * p.Rn + (j - p.En)] & 0xffff);
-      s.ikey[n * p.Pn + j] = s.kexp[n * p.En + li];
-    }
-  }
-  __syncthreads();
-
-  // ---- step 3c: heaviest first (stable), then pack onto the node's GPUs
-  if (p.ppr == 1) {
-    for (int i = tid; i < p.P; i += NT) s.pid[i] = i;
-  } else {
-    const int Pn = p.Pn;
-    const u128* ikey = s.ikey;
-    seg_bitonic(s.sort, p.Np, p.Pn2, p.logPn2, [=](int seg, int a, int b2) {
-      if (a >= Pn || b2 >= Pn) return (a < Pn) || (b2 >= Pn && a < b2);
-      const u128 ka = ikey[seg * Pn + a], kb = ikey[seg * Pn + b2];
-      return ka > kb || (ka == kb && a < b2);
-    });
-    const int slots = p.pack_slots;
-    for (int n = wid; n < p.Np; n += NW) {
-      const u128* nkey = ikey + n * Pn;
-      wave_pack<u128>(s.sort + n * p.Pn2, Pn, p.RKn, p.ppr, [=](int item) { return nkey[item]; },
-                      s.pid + n * Pn, (u128*)s.psum + wid * slots, s.pcnt + wid * slots);
-    }
-    __syncthreads();
-    for (int i = tid; i < p.P; i += NT) {
-      const int n = i / Pn;            // Pn >= 2 here; a division per item, once
-      s.pid[i] += n * Pn;
-    }
-  }
-  __syncthreads();
-
-  // ---- outputs
+  // ---- step 3 and outputs, one wave per node
   int32_t* o_phy = phy2log + b * p.P;
   int32_t* o_l2p = log2phy + b * (int64_t)p.E * p.X;
   int32_t* o_cnt = logcnt + b * p.E;
-  for (int i = tid; i < p.P; i += NT) {
-    const int n = i / p.Pn;
-    const int j = i - n * p.Pn;
-    int li, rank;
-    if (j < p.En) { li = j; rank = 0; }
-    else { const int r = s.rep[n * p.Rn + (j - p.En)]; li = r & 0xffff; rank = r >> 16; }
-    const int e = s.m2l[n * p.En + li];
-    const int pid = s.pid[i];
-    o_phy[pid] = e;
-    o_l2p[(int64_t)e * p.X + rank] = pid;
-  }
-  for (int i = tid; i < p.E * p.X; i += NT) {
-    const int e = (int)fastdiv_apply((uint32_t)i, p.fd_X);
-    const int r = i - e * p.X;
-    if (r >= s.cnt[s.l2m[e]]) o_l2p[i] = -1;
-  }
-  for (int e = tid; e < p.E; e += NT) o_cnt[e] = s.cnt[s.l2m[e]];
+  for (int n = wid; n < p.Np; n += NW) node_place<KR, KP>(p, s, n, wid, o_phy, o_l2p, o_cnt);
   if (tid == 0) status[b] = 0;
 }
 
-int pow2_at_least(int n) {
-  int v = 1;
-  while (v < n) v <<= 1;
-  return v;
+int regs_for(int n) {          // registers per lane to hold n sorted positions
+  return n <= 64 ? 1 : n <= 128 ? 2 : n <= 256 ? 4 : 8;
 }
 
-int log2_exact(int v) {
-  int l = 0;
-  while ((1 << l) < v) ++l;
-  return l;
+typedef void (*RbKernel)(const int64_t*, RbPlan, int32_t*, int32_t*, int32_t*, int32_t*);
+
+template <int KR>
+RbKernel pick_kp(int KP) {
+  switch (KP) {
+    case 1: return rebalance_kernel<KR, 1>;
+    case 2: return rebalance_kernel<KR, 2>;
+    case 4: return rebalance_kernel<KR, 4>;
+    default: return rebalance_kernel<KR, 8>;
+  }
+}
+
+RbKernel pick_kernel(int KR, int KP) {
+  switch (KR) {
+    case 1: return pick_kp<1>(KP);
+    case 2: return pick_kp<2>(KP);
+    case 4: return pick_kp<4>(KP);
+    default: return pick_kp<8>(KP);
+  }
 }
 
 }  // namespace
@@ -496,12 +713,13 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.E = E; p.P = P; p.Gp = Gp; p.Np = Np; p.RK = RK; p.X = X;
   p.S = E / Gp; p.En = E / Np; p.Pn = P / Np; p.Rn = p.Pn - p.En;
   p.RKn = RK / Np; p.ppr = P / RK; p.gpn = Gp / Np;
-  p.G2 = pow2_at_least(Gp < 2 ? 2 : Gp);
-  p.Pn2 = pow2_at_least(p.Pn < 2 ? 2 : p.Pn);
-  p.logPn2 = log2_exact(p.Pn2);
-  int waves = Np < 4 ? 4 : (Np > 16 ? 16 : Np);
+  if (p.En > 512 || p.RKn > 512 || Np > 512) return EPLB_E_LIMIT;
+  p.KR = regs_for(p.En);
+  p.KP = regs_for(p.RKn);
+  p.KN = Np <= 64 ? 1 : 8;
+  const int waves = Np < 4 ? 4 : (Np > 8 ? 8 : Np);
   p.threads = waves * 64;
-  p.pack_slots = (p.RKn > Np ? p.RKn : Np);
+  const int nscr = Np < waves ? Np : waves;        // waves that place nodes
   p.fd_S = fastdiv_make((uint32_t)p.S);
   p.fd_En = fastdiv_make((uint32_t)p.En);
   p.fd_X = fastdiv_make((uint32_t)X);
@@ -513,31 +731,28 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
     off += bytes;
     return (int32_t)at;
   };
+  const int64_t ordk_items = p.Pn > Gp ? p.Pn : Gp;
+  const int64_t rn1 = p.Rn > 0 ? p.Rn : 1;
   p.o_kexp = take(16ll * E, 16);
-  p.o_ikey = take(16ll * P, 16);
-  p.o_dn = take(16ll * Np, 16);
-  p.o_psum = take(16ll * waves * p.pack_slots, 16);
+  p.o_ordk = take(16ll * nscr * ordk_items, 16);
   p.o_w = take(8ll * E, 8);
   p.o_wl = take(8ll * E, 8);
   p.o_gsum = take(8ll * Gp, 8);
-  p.o_nsum = take(8ll * Np, 8);
   p.o_m2l = take(4ll * E, 4);
   p.o_l2m = take(4ll * E, 4);
   p.o_cnt = take(4ll * E, 4);
+  p.o_srt = take(4ll * E, 4);
   p.o_gnode = take(4ll * Gp, 4);
   p.o_gslot = take(4ll * Gp, 4);
-  p.o_gsort = take(4ll * p.G2, 4);
-  p.o_rep = take(4ll * Np * (p.Rn > 0 ? p.Rn : 1), 4);
-  p.o_sort = take(4ll * Np * p.Pn2, 4);
-  p.o_pid = take(4ll * P, 4);
-  p.o_emax = take(4ll * Np * kNumSmallPrimes, 4);
-  p.bigw = (p.Rn + 2 + 31) / 32;
-  p.bigcap = p.Rn / 130 + 1;
-  p.o_big = take(4ll * Np * p.bigcap, 4);
-  p.o_nbig = take(4ll * Np, 4);
-  p.o_pcnt = take(4ll * waves * p.pack_slots, 4);
+  p.o_gord = take(4ll * Gp, 4);
+  p.o_gres = take(4ll * Gp, 4);
+  p.o_rep = take(4ll * Np * rn1, 4);
+  p.o_posaux = take(12ll * nscr * p.En, 4);
+  p.o_ordr = take(4ll * nscr * p.Pn, 4);
+  p.o_ores = take(4ll * nscr * p.Pn, 4);
+  p.o_rcls = take(4ll * nscr * rn1, 4);
+  p.o_nflag = take(4ll * Np, 4);
   p.o_flags = take(16, 4);
-  p.o_bigf = take(4ll * Np * p.bigw, 4);
   off = (off + 15) / 16 * 16;
   if (off > kMaxLdsBytes) return EPLB_E_LIMIT;
   p.lds_bytes = (int32_t)off;
@@ -549,8 +764,8 @@ hipError_t launch_rebalance(const int64_t* load, int64_t B, const RbPlan& plan,
                             int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
                             int32_t* status, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  rebalance_kernel<<<(unsigned)B, plan.threads, plan.lds_bytes, stream>>>(load, plan, phy2log, log2phy,
-                                                                          logcnt, status);
+  pick_kernel(plan.KR, plan.KP)<<<(unsigned)B, plan.threads, plan.lds_bytes, stream>>>(
+      load, plan, phy2log, log2phy, logcnt, status);
   return hipGetLastError();
 }
 
