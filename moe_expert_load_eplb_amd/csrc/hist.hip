@@ -6,8 +6,9 @@
 // statistics of past steps (opening section of Part 2).  Three kernels on one
 // stream: clear the ring slot of this step, count, then sum the window.
 //
-// Counting is HBM-bound: 4 bytes read per routing id.  Each workgroup streams
-// one contiguous chunk of one layer with 16-byte loads and counts into
+// Counting is HBM-bound: 4 bytes read per routing id.  A few workgroups per
+// layer sweep the layer together with 16-byte non-temporal loads (all layers
+// at once: ~1.8 workgroups of 512 threads per CU in all) and count into
 // LDS-resident counters; a workgroup keeps `copies` private copies of the E
 // counters (row stride E + 1, so the copies of one expert fall in different
 // LDS banks) to spread the increments of a popular expert.  At the end each
@@ -18,8 +19,6 @@ namespace eplb {
 
 namespace {
 
-constexpr int kHistThreads = 256;
-constexpr int kUnroll = 4;
 
 __global__ __launch_bounds__(256) void hist_clear_kernel(int32_t* __restrict__ slot, int64_t LE,
                                                          int64_t* __restrict__ n_invalid, int64_t L) {
@@ -36,44 +35,50 @@ __device__ __forceinline__ void count_id(int32_t e, uint32_t E, int32_t* my, uin
   }
 }
 
-__global__ __launch_bounds__(kHistThreads) void hist_count_kernel(const int32_t* __restrict__ idx,
-                                                                   StreamSplit sp, int32_t E,
-                                                                   int32_t copies,
-                                                                   int32_t* __restrict__ slot,
-                                                                   int64_t* __restrict__ n_invalid) {
+// Workgroup c of `chunks` per layer takes the layer's 16-byte vectors
+// c*NT + tid + k*chunks*NT, so the workgroups of a layer sweep it together,
+// one contiguous window at a time.  Ids before the layer's first 16-byte
+// boundary and after its last one are counted by workgroup 0.
+__global__ __launch_bounds__(kStreamThreads) void hist_count_kernel(const int32_t* __restrict__ idx,
+                                                                     StreamSplit sp, int32_t E,
+                                                                     int32_t copies,
+                                                                     int32_t* __restrict__ slot,
+                                                                     int64_t* __restrict__ n_invalid) {
   extern __shared__ int32_t counters[];             // [copies][E + 1]
   const int64_t layer = blockIdx.x / sp.chunks;
   const int64_t chunk = blockIdx.x - layer * sp.chunks;
   const int stride = E + 1;
   const int tid = threadIdx.x;
 
-  for (int i = tid; i < copies * stride; i += kHistThreads) counters[i] = 0;
+  for (int i = tid; i < copies * stride; i += kStreamThreads) counters[i] = 0;
   __syncthreads();
 
-  const int64_t begin = chunk * sp.chunk;
-  const int64_t end = begin + sp.chunk < sp.per_layer ? begin + sp.chunk : sp.per_layer;
-  const int32_t* base = idx + layer * sp.per_layer + begin;
-  const int64_t n = end > begin ? end - begin : 0;
+  const int32_t* base = idx + layer * sp.per_layer;
+  const int64_t n = sp.per_layer;
   int32_t* my = counters + (tid & (copies - 1)) * stride;
   uint32_t inv = 0;
 
-  // Head ids up to the first 16-byte boundary, body as int4, then the tail.
   const int misalign = (int)(((uintptr_t)base >> 2) & 3);
   int64_t head = (4 - misalign) & 3;
   if (head > n) head = n;
-  if (tid < head) count_id(base[tid], (uint32_t)E, my, inv);
-  const i32x4* body = reinterpret_cast<const i32x4*>(base + head);
   const int64_t n4 = (n - head) >> 2;
-  for (int64_t v = tid; v < n4; v += (int64_t)kHistThreads * kUnroll) {
-    i32x4 x[kUnroll];
+  const int64_t tail0 = head + (n4 << 2);
+  if (chunk == 0) {
+    if (tid < head) count_id(base[tid], (uint32_t)E, my, inv);
+    if (tail0 + tid < n) count_id(base[tail0 + tid], (uint32_t)E, my, inv);
+  }
+  const i32x4* body = reinterpret_cast<const i32x4*>(base + head);
+  const int64_t step = (int64_t)sp.chunks * kStreamThreads;
+  for (int64_t v = chunk * kStreamThreads + tid; v < n4; v += step * kStreamUnroll) {
+    i32x4 x[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vv = v + (int64_t)u * kHistThreads;
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t vv = v + u * step;
       if (vv < n4) x[u] = __builtin_nontemporal_load(body + vv);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vv = v + (int64_t)u * kHistThreads;
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t vv = v + u * step;
       if (vv < n4) {
         count_id(x[u].x, (uint32_t)E, my, inv);
         count_id(x[u].y, (uint32_t)E, my, inv);
@@ -82,19 +87,18 @@ __global__ __launch_bounds__(kHistThreads) void hist_count_kernel(const int32_t*
       }
     }
   }
-  const int64_t tail0 = head + (n4 << 2);
-  if (tail0 + tid < n) count_id(base[tail0 + tid], (uint32_t)E, my, inv);
   __syncthreads();
 
   int32_t* out = slot + layer * E;
-  for (int e = tid; e < E; e += kHistThreads) {
+  for (int e = tid; e < E; e += kStreamThreads) {
     int32_t s = 0;
     for (int c = 0; c < copies; ++c) s += counters[c * stride + e];
     if (s) atomicAdd(&out[e], s);
   }
   // One 64-bit atomic per wave for the out-of-range ids.
   for (int off = 32; off > 0; off >>= 1) inv += __shfl_xor(inv, off);
-  if ((tid & 63) == 0 && inv) atomicAdd(reinterpret_cast<unsigned long long*>(&n_invalid[layer]), (unsigned long long)inv);
+  if ((tid & 63) == 0 && inv)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&n_invalid[layer]), (unsigned long long)inv);
 }
 
 __global__ __launch_bounds__(256) void window_sum_kernel(const int32_t* __restrict__ ring, int64_t LE,
@@ -116,19 +120,15 @@ int grid_for(int64_t n, int threads) {
 
 }  // namespace
 
-StreamSplit plan_stream(int64_t L, int64_t per_layer, int target_blocks, int64_t min_chunk) {
+StreamSplit plan_stream(int64_t L, int64_t per_layer) {
   StreamSplit s;
   s.per_layer = per_layer;
-  int64_t chunks = L > 0 ? (target_blocks + L - 1) / L : 1;
-  int64_t most = (per_layer + min_chunk - 1) / min_chunk;
-  if (chunks > most) chunks = most;
+  const int64_t n4 = per_layer / 4;
+  const int64_t per_block = (int64_t)kStreamThreads * kStreamUnroll;
+  int64_t chunks = L > 0 ? (kStreamBlocks + L / 2) / L : 1;
+  const int64_t useful = (n4 + per_block - 1) / per_block;     // every thread gets a vector
+  if (chunks > useful) chunks = useful;
   if (chunks < 1) chunks = 1;
-  int64_t chunk = (per_layer + chunks - 1) / chunks;
-  chunk = (chunk + 3) & ~(int64_t)3;
-  if (chunk < 4) chunk = 4;
-  chunks = (per_layer + chunk - 1) / chunk;
-  if (chunks < 1) chunks = 1;
-  s.chunk = chunk;
   s.chunks = (int32_t)chunks;
   return s;
 }
@@ -145,13 +145,12 @@ hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
 
   const int64_t per_layer = T * (int64_t)K;
   if (per_layer > 0) {
-    // ~8 workgroups per CU over 256 CUs; at least 16 Ki ids per workgroup.
-    StreamSplit sp = plan_stream(L, per_layer, 2048, 16384);
+    const StreamSplit sp = plan_stream(L, per_layer);
     int copies = 16;
     while (copies > 1 && (int64_t)copies * (E + 1) * 4 > 32 * 1024) copies >>= 1;
     const size_t lds = (size_t)copies * (E + 1) * sizeof(int32_t);
     const int64_t blocks = L * sp.chunks;
-    hist_count_kernel<<<(unsigned)blocks, kHistThreads, lds, stream>>>(idx, sp, E, copies, slot, n_invalid);
+    hist_count_kernel<<<(unsigned)blocks, kStreamThreads, lds, stream>>>(idx, sp, E, copies, slot, n_invalid);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

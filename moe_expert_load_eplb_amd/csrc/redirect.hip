@@ -6,9 +6,9 @@
 // gives each about half of its tokens; the round-robin by token row is the
 // rule this library fixes).  out[l][t][k] = log2phy[l][e][t mod logcnt[l][e]].
 //
-// HBM-bound: 4 bytes read and 4 bytes written per id.  Each workgroup streams
-// one contiguous chunk of one layer with 16-byte non-temporal loads and
-// stores.  The layer's tables are staged in LDS first: per expert its count
+// HBM-bound: 4 bytes read and 4 bytes written per id.  A few workgroups per
+// layer sweep the layer together (all layers at once) with 16-byte
+// non-temporal loads and stores.  The layer's tables are staged in LDS first: per expert its count
 // and the magic numbers of an exact division by it (so t mod c costs a
 // multiply-high, a shift and a multiply-subtract), and the log2phy rows.
 #include "eplb_internal.h"
@@ -17,8 +17,6 @@ namespace eplb {
 
 namespace {
 
-constexpr int kRedirThreads = 256;
-constexpr int kUnroll = 2;
 constexpr int kStageBytes = 48 * 1024;
 
 struct LayerTables {
@@ -40,12 +38,12 @@ __device__ __forceinline__ int32_t map_id(int32_t e, uint32_t t, const LayerTabl
 }
 
 template <bool kStaged>
-__global__ __launch_bounds__(kRedirThreads) void redirect_kernel(const int32_t* __restrict__ idx,
-                                                                  StreamSplit sp, FastDiv kdiv,
-                                                                  int32_t E, int32_t X,
-                                                                  const int32_t* __restrict__ log2phy,
-                                                                  const int32_t* __restrict__ logcnt,
-                                                                  int32_t* __restrict__ out) {
+__global__ __launch_bounds__(kStreamThreads) void redirect_kernel(const int32_t* __restrict__ idx,
+                                                                   StreamSplit sp, FastDiv kdiv,
+                                                                   int32_t E, int32_t X,
+                                                                   const int32_t* __restrict__ log2phy,
+                                                                   const int32_t* __restrict__ logcnt,
+                                                                   int32_t* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t layer = blockIdx.x / sp.chunks;
   const int64_t chunk = blockIdx.x - layer * sp.chunks;
@@ -54,7 +52,7 @@ __global__ __launch_bounds__(kRedirThreads) void redirect_kernel(const int32_t* 
   uint2* info = reinterpret_cast<uint2*>(smem);
   int32_t* stab = reinterpret_cast<int32_t*>(smem + (size_t)E * sizeof(uint2));
   const int32_t* gtab = log2phy + layer * (int64_t)E * X;
-  for (int e = tid; e < E; e += kRedirThreads) {
+  for (int e = tid; e < E; e += kStreamThreads) {
     const int32_t c = logcnt[layer * E + e];
     uint2 in = make_uint2(0u, 0u);
     if (c >= 1 && c <= X) {
@@ -64,43 +62,46 @@ __global__ __launch_bounds__(kRedirThreads) void redirect_kernel(const int32_t* 
     info[e] = in;
   }
   if (kStaged) {
-    for (int i = tid; i < E * X; i += kRedirThreads) stab[i] = gtab[i];
+    for (int i = tid; i < E * X; i += kStreamThreads) stab[i] = gtab[i];
   }
   __syncthreads();
   const LayerTables lt{info, kStaged ? stab : gtab, (uint32_t)E, X};
 
-  const int64_t begin = chunk * sp.chunk;
-  const int64_t end = begin + sp.chunk < sp.per_layer ? begin + sp.chunk : sp.per_layer;
-  const int64_t n = end > begin ? end - begin : 0;
-  const int32_t* src = idx + layer * sp.per_layer + begin;
-  int32_t* dst = out + layer * sp.per_layer + begin;
-  const uint32_t f0 = (uint32_t)begin;                 // id offset of src[0] within the layer
+  const int64_t n = sp.per_layer;
+  const int32_t* src = idx + layer * n;
+  int32_t* dst = out + layer * n;
+  const int64_t step = (int64_t)sp.chunks * kStreamThreads;
 
   const int mis_s = (int)(((uintptr_t)src >> 2) & 3);
   const int mis_d = (int)(((uintptr_t)dst >> 2) & 3);
   if (mis_s != mis_d) {
     // Source and destination disagree on 16-byte phase: plain 4-byte path.
-    for (int64_t i = tid; i < n; i += kRedirThreads)
-      dst[i] = map_id(src[i], fastdiv_apply(f0 + (uint32_t)i, kdiv), lt);
+    for (int64_t i = chunk * kStreamThreads + tid; i < n; i += step)
+      dst[i] = map_id(src[i], fastdiv_apply((uint32_t)i, kdiv), lt);
     return;
   }
   int64_t head = (4 - mis_s) & 3;
   if (head > n) head = n;
-  if (tid < head) dst[tid] = map_id(src[tid], fastdiv_apply(f0 + (uint32_t)tid, kdiv), lt);
+  const int64_t n4 = (n - head) >> 2;
+  const int64_t tail0 = head + (n4 << 2);
+  if (chunk == 0) {
+    if (tid < head) dst[tid] = map_id(src[tid], fastdiv_apply((uint32_t)tid, kdiv), lt);
+    if (tail0 + tid < n)
+      dst[tail0 + tid] = map_id(src[tail0 + tid], fastdiv_apply((uint32_t)(tail0 + tid), kdiv), lt);
+  }
   const i32x4* s4 = reinterpret_cast<const i32x4*>(src + head);
   i32x4* d4 = reinterpret_cast<i32x4*>(dst + head);
-  const int64_t n4 = (n - head) >> 2;
-  const uint32_t fb = f0 + (uint32_t)head;
-  for (int64_t v = tid; v < n4; v += (int64_t)kRedirThreads * kUnroll) {
-    i32x4 x[kUnroll];
+  const uint32_t fb = (uint32_t)head;            // id offset (within the layer) of s4[0]
+  for (int64_t v = chunk * kStreamThreads + tid; v < n4; v += step * kStreamUnroll) {
+    i32x4 x[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vv = v + (int64_t)u * kRedirThreads;
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t vv = v + u * step;
       if (vv < n4) x[u] = __builtin_nontemporal_load(s4 + vv);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vv = v + (int64_t)u * kRedirThreads;
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t vv = v + u * step;
       if (vv < n4) {
         const uint32_t f = fb + (uint32_t)(vv << 2);
         i32x4 y;
@@ -112,9 +113,6 @@ __global__ __launch_bounds__(kRedirThreads) void redirect_kernel(const int32_t* 
       }
     }
   }
-  const int64_t tail0 = head + (n4 << 2);
-  if (tail0 + tid < n)
-    dst[tail0 + tid] = map_id(src[tail0 + tid], fastdiv_apply(f0 + (uint32_t)(tail0 + tid), kdiv), lt);
 }
 
 }  // namespace
@@ -124,16 +122,16 @@ hipError_t launch_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
                            int32_t* out, hipStream_t stream) {
   const int64_t per_layer = T * (int64_t)K;
   if (L == 0 || per_layer == 0) return hipSuccess;
-  const StreamSplit sp = plan_stream(L, per_layer, 2048, 16384);
+  const StreamSplit sp = plan_stream(L, per_layer);
   const FastDiv kdiv = fastdiv_make((uint32_t)K);
   const int64_t blocks = L * sp.chunks;
   const size_t info_bytes = (size_t)E * sizeof(uint2);
   const size_t tab_bytes = (size_t)E * X * sizeof(int32_t);
   if (info_bytes + tab_bytes <= (size_t)kStageBytes) {
-    redirect_kernel<true><<<(unsigned)blocks, kRedirThreads, info_bytes + tab_bytes, stream>>>(
+    redirect_kernel<true><<<(unsigned)blocks, kStreamThreads, info_bytes + tab_bytes, stream>>>(
         idx, sp, kdiv, E, X, log2phy, logcnt, out);
   } else {
-    redirect_kernel<false><<<(unsigned)blocks, kRedirThreads, info_bytes, stream>>>(
+    redirect_kernel<false><<<(unsigned)blocks, kStreamThreads, info_bytes, stream>>>(
         idx, sp, kdiv, E, X, log2phy, logcnt, out);
   }
   return hipGetLastError();
