@@ -129,6 +129,19 @@ def main() -> int:
         e1.synchronize()
         reb_dev.append(e0.elapsed_time(e1) * 1e3)
 
+    # a plain device-to-device copy of one step's ids (torch), for comparison
+    # and as the known-size kernel that calibrates the HBM byte counters
+    cal = torch.empty_like(steps[0])
+    cal.copy_(steps[0])
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cal.copy_(steps[0])
+    c1.record(stream)
+    c1.synchronize()
+    copy_gbs = 2 * hist_bytes / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+    del cal
+
     avg = lambda xs: sum(xs) / len(xs)
     redir_gbs = redir_bytes / (avg(red_ms) * 1e-3) / 1e9
     hist_gbs = hist_bytes / (avg(hist_ms) * 1e-3) / 1e9
@@ -161,6 +174,7 @@ def main() -> int:
             "redirect_ms": round(avg(red_ms), 4), "redirect_GBps": round(redir_gbs, 1),
             "redirect_frac_of_peak": round(redir_gbs / HBM_PEAK_GBS, 4),
             "step_ms_events": round(avg(step_ms), 4),
+            "torch_d2d_copy_GBps": round(copy_gbs, 1),
         },
         "rebalance_58_layers": {
             "shape": "E=256 G=8 N=4 RK=32 P=288 (hierarchical), 58 problems",
@@ -175,7 +189,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(redir_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_from_profile("redirect_kernel", ids),
         },
     }
 
@@ -220,6 +234,24 @@ def cpu_baseline(args, work, idx_dev, load_dev, placement, step_bytes):
         "rebalance_58_layers_s": round(t2 - t1, 3),
         "cpu": _cpu_model(),
     }
+
+
+def traffic_from_profile(kernel: str, ids: int):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when that summary is missing or was taken on other kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "stream_58L_1Mtok_top8_hbm_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None or rec.get("sources_sha256") != h.hexdigest() or rec.get("ids_per_launch") != ids:
+        return None
+    return k["hbm_bytes_per_launch"]
 
 
 def _cpu_model() -> str:
