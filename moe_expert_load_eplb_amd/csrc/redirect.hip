@@ -93,24 +93,28 @@ __global__ __launch_bounds__(kStreamThreads) void redirect_kernel(const int32_t*
   i32x4* d4 = reinterpret_cast<i32x4*>(dst + head);
   const uint32_t fb = (uint32_t)head;            // id offset (within the layer) of s4[0]
   for (int64_t v = chunk * kStreamThreads + tid; v < n4; v += step * kStreamUnroll) {
+    // all loads of the iteration, then all lookups, then all stores
     i32x4 x[kStreamUnroll];
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) {
       const int64_t vv = v + u * step;
       if (vv < n4) x[u] = __builtin_nontemporal_load(s4 + vv);
     }
+    i32x4 y[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      if (v + u * step < n4) {          // t below 2^31 only for ids that exist
+        const uint32_t f = fb + (uint32_t)((v + u * step) << 2);
+        y[u].x = map_id(x[u].x, fastdiv_apply(f, kdiv), lt);
+        y[u].y = map_id(x[u].y, fastdiv_apply(f + 1, kdiv), lt);
+        y[u].z = map_id(x[u].z, fastdiv_apply(f + 2, kdiv), lt);
+        y[u].w = map_id(x[u].w, fastdiv_apply(f + 3, kdiv), lt);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) {
       const int64_t vv = v + u * step;
-      if (vv < n4) {
-        const uint32_t f = fb + (uint32_t)(vv << 2);
-        i32x4 y;
-        y.x = map_id(x[u].x, fastdiv_apply(f, kdiv), lt);
-        y.y = map_id(x[u].y, fastdiv_apply(f + 1, kdiv), lt);
-        y.z = map_id(x[u].z, fastdiv_apply(f + 2, kdiv), lt);
-        y.w = map_id(x[u].w, fastdiv_apply(f + 3, kdiv), lt);
-        __builtin_nontemporal_store(y, d4 + vv);
-      }
+      if (vv < n4) __builtin_nontemporal_store(y[u], d4 + vv);
     }
   }
 }
