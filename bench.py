@@ -5,6 +5,9 @@ One step = one pass of the whole path over one step of routing ids:
     eplb_rebalance  (58 DeepSeek-V3-shaped problems: 256 experts in 8 groups,
                      288 physical on 4 nodes x 8 ranks, hierarchical policy)
     eplb_redirect   (every (token, k) of the step -> a physical replica)
+Also reported: the serving-loop step (eplb_hist_redirect, which reads the ids
+once, then the rebalance for the next step) and the rebalance latency of the
+global-policy decode shape and of the 1024-problem skewed batch.
 on the streaming workload: 58 MoE layers x 2^20 tokens x top-8 int32 ids per
 step (1.95 GB), Zipf(1.1) expert popularity, a 10-step window.  Ten distinct
 steps are generated on the device up front and cycled; inputs are resident
@@ -129,6 +132,50 @@ def main() -> int:
         e1.synchronize()
         reb_dev.append(e0.elapsed_time(e1) * 1e3)
 
+    # serving-loop step: one fused pass (count this step + redirect it with the
+    # placement in force), then the rebalance that gives the next placement
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s_ = nwarm + args.steps + i
+        e = sevs[i]
+        e[0].record(stream)
+        eplb.hist_redirect(steps[s_ % W], E, ring, s_, log2phy, logcnt, load, n_invalid, out)
+        e[1].record(stream)
+        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    serve_wall = time.perf_counter() - t0
+    fused_ms = [e[0].elapsed_time(e[1]) for e in sevs]
+
+    # the other two rebalance shapes: 58-layer global policy, 1024 problems
+    def reb_device_us(ld, P, G, N, RK):
+        Xo = eplb.max_count(ld.shape[1], P, G, N)
+        outs = eplb.rebalance(ld, P, G, N, RK, Xo)
+        torch.cuda.synchronize()
+        assert int(outs[3].abs().sum()) == 0
+        ts = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            eplb.rebalance(ld, P, G, N, RK, Xo, out=outs)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return round(statistics.median(ts), 2)
+    gd = wl.GLOBAL_DECODE
+    gload = torch.from_numpy(wl.zipf_loads(gd.layers, gd.placement.E, gd.param,
+                                           gd.tokens * gd.topk * gd.window)).to(dev)
+    sk = wl.SKEWED_1024
+    sload = torch.from_numpy(wl.skewed_loads()).to(dev)
+    other = {
+        "global_decode_58L_e256_p320_5x8_us": reb_device_us(gload, gd.placement.P, gd.placement.G,
+                                                            gd.placement.N, gd.placement.RK),
+        "skewed_1024x_e512_p640_8x8_us": reb_device_us(sload, sk.placement.P, sk.placement.G,
+                                                       sk.placement.N, sk.placement.RK),
+    }
+
     # a plain device-to-device copy of one step's ids (torch), for comparison
     # and as the known-size kernel that calibrates the HBM byte counters
     cal = torch.empty_like(steps[0])
@@ -176,6 +223,15 @@ def main() -> int:
             "step_ms_events": round(avg(step_ms), 4),
             "torch_d2d_copy_GBps": round(copy_gbs, 1),
         },
+        "serving_step": {
+            "what": "eplb_hist_redirect (count step s, redirect it with the placement in force) + eplb_rebalance",
+            "ms_per_step": round(serve_wall * 1e3 / args.steps, 4),
+            "fused_ms": round(avg(fused_ms), 4),
+            "fused_GBps": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9, 1),
+            "fused_frac_of_peak": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_step": redir_bytes,
+        },
+        "rebalance_other_device_us_median": other,
         "rebalance_58_layers": {
             "shape": "E=256 G=8 N=4 RK=32 P=288 (hierarchical), 58 problems",
             "device_us_median": round(statistics.median(reb_dev), 2),

@@ -134,6 +134,22 @@ int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
                       const int32_t* log2phy, const int32_t* logcnt, int32_t X,
                       int32_t* out, void* stream);
 
+/*
+ * eplb_hist_redirect -- eplb_load_hist and eplb_redirect in one pass over idx.
+ *
+ * Follows the same passages as the two calls it combines.  Counts the step's
+ * ids into ring slot (step % W), sums the window into `load`, and writes the
+ * physical id of every (token, k) under the placement (log2phy, logcnt) given,
+ * typically the one computed from the window before this step.  Every output
+ * is identical to calling eplb_load_hist then eplb_redirect with the same
+ * arguments; each id is read once instead of twice.  Arguments, layouts,
+ * errors: as for those two calls (out must not overlap idx).
+ */
+int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                           int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
+                           const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
+                           void* stream);
+
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);
 

@@ -7,7 +7,7 @@ device pointers and the current HIP stream through the C ABI declared in
 PyTorch supplies device memory and streams.
 
 Importing this package loads the library; if it has not been built
-(``python -m moe_expert_load_eplb_amd.build``) the import fails loudly.
+(``python moe_expert_load_eplb_amd/build.py``) the import fails loudly.
 """
 from __future__ import annotations
 
@@ -30,15 +30,19 @@ EPLB_S_OK = 0
 EPLB_S_BAD_LOAD = 16
 EPLB_S_OVERFLOW = 17
 
-EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
-           "eplb_rebalance_lds_bytes")
+EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
+           "eplb_status_string", "eplb_rebalance_lds_bytes")
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
-                          "`python -m moe_expert_load_eplb_amd.build` (hipcc, gfx950)")
+                          "`python moe_expert_load_eplb_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
+    missing = [f for f in EXPORTS if not hasattr(lib, f)]
+    if missing:
+        raise ImportError(f"{_LIB_PATH} lacks {missing}: rebuild it with "
+                          "`python moe_expert_load_eplb_amd/build.py`")
     p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.eplb_load_hist.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p]
     lib.eplb_load_hist.restype = i32
@@ -46,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_rebalance.restype = i32
     lib.eplb_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, p, p]
     lib.eplb_redirect.restype = i32
+    lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
+    lib.eplb_hist_redirect.restype = i32
     lib.eplb_status_string.argtypes = [i32]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -169,3 +175,34 @@ def redirect(idx: torch.Tensor, log2phy: torch.Tensor, logcnt: torch.Tensor,
                            _dev(out, torch.int32, "out"), _stream(idx.device))
     _check(rc, "eplb_redirect")
     return out
+
+
+def hist_redirect(idx: torch.Tensor, E: int, ring: torch.Tensor, step: int,
+                  log2phy: torch.Tensor, logcnt: torch.Tensor, load: torch.Tensor | None = None,
+                  n_invalid: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """load_hist and redirect in one pass over idx (the placement given is the
+    one in force for this step).  Returns (load, n_invalid, out)."""
+    if idx.dim() != 3 or log2phy.dim() != 3 or logcnt.dim() != 2:
+        raise ValueError("idx [L, T, K], log2phy [L, E, X], logcnt [L, E] expected")
+    L, T, K = idx.shape
+    if ring.dim() != 3 or ring.shape[1] != L or ring.shape[2] != E:
+        raise ValueError(f"ring must be [W, {L}, {E}], got {tuple(ring.shape)}")
+    if tuple(log2phy.shape[:2]) != (L, E) or tuple(logcnt.shape) != (L, E):
+        raise ValueError("log2phy / logcnt do not match idx's layers and E")
+    W, X = ring.shape[0], log2phy.shape[2]
+    dev = idx.device
+    if load is None:
+        load = torch.empty((L, E), dtype=torch.int64, device=dev)
+    if n_invalid is None:
+        n_invalid = torch.empty((L,), dtype=torch.int64, device=dev)
+    if out is None:
+        out = torch.empty_like(idx)
+    if tuple(load.shape) != (L, E) or tuple(n_invalid.shape) != (L,) or out.shape != idx.shape:
+        raise ValueError("load [L, E], n_invalid [L], out like idx expected")
+    rc = lib.eplb_hist_redirect(_dev(idx, torch.int32, "idx"), L, T, K, E, _dev(ring, torch.int32, "ring"), W,
+                                int(step), _dev(load, torch.int64, "load"),
+                                _dev(n_invalid, torch.int64, "n_invalid"), _dev(log2phy, torch.int32, "log2phy"),
+                                _dev(logcnt, torch.int32, "logcnt"), X, _dev(out, torch.int32, "out"),
+                                _stream(dev))
+    _check(rc, "eplb_hist_redirect")
+    return load, n_invalid, out

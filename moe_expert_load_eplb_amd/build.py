@@ -1,9 +1,10 @@
 """Build libeplb.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m moe_expert_load_eplb_amd.build
+    python moe_expert_load_eplb_amd/build.py
 
 Compiles every source under csrc/ with hipcc into one shared library next to
-this file.  Always recompiles.
+this file.  Always recompiles.  Run it by path (not as ``-m``): importing the
+package would load the library being rebuilt.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libeplb.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip"]
+SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip", "fused.hip"]
 
 
 def hipcc() -> str:

@@ -61,6 +61,22 @@ int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                           int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
+                           const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
+                           void* stream) {
+  int32_t rc = check_stream_args(idx, L, T, K, E);
+  if (rc != EPLB_OK) return rc;
+  if (W < 1 || step < 0 || X < 1) return EPLB_E_ARG;
+  if (X > kMaxX) return EPLB_E_LIMIT;
+  if (L > 0 && (ring == nullptr || load == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
+  if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
+  if (L > 0 && T > 0 && (const void*)out == (const void*)idx) return EPLB_E_ARG;
+  hipError_t err = launch_hist_redirect(idx, L, T, K, E, ring, W, step, load, n_invalid, log2phy, logcnt, X,
+                                        out, (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);

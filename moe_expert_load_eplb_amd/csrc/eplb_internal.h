@@ -59,6 +59,59 @@ struct StreamSplit {
 
 StreamSplit plan_stream(int64_t L, int64_t per_layer);
 
+// ---------------------------------------------------------------- redirect helpers
+// A layer's redirect tables in LDS: per expert {magic, count << 8 | (shift + 1)}
+// (count 0 marks an unusable expert: its ids map to -1) and the [E][X]
+// log2phy rows (in LDS when staged, else read from global memory).
+struct LayerTables {
+  const uint2* info;       // per expert: {magic, count << 8 | (shift + 1)}, count 0 = invalid
+  const int32_t* tab;      // [E][X] log2phy rows (LDS or global)
+  uint32_t E;
+  int32_t X;
+};
+
+__device__ __forceinline__ int32_t map_id(int32_t e, uint32_t t, const LayerTables& lt) {
+  if ((uint32_t)e >= lt.E) return -1;
+  const uint2 in = lt.info[e];
+  const uint32_t c = in.y >> 8;
+  if (c == 0) return -1;
+  const int shift = (int)(in.y & 255u) - 1;
+  const uint32_t q = shift < 0 ? t : (uint32_t)(((u64)t * in.x) >> 32) >> shift;
+  const uint32_t r = t - q * c;
+  return lt.tab[e * lt.X + (int32_t)r];
+}
+
+
+template <bool kStaged>
+__device__ __forceinline__ void stage_layer_tables(const int32_t* __restrict__ cnt_row,
+                                                   const int32_t* __restrict__ l2p_rows, int E, int X,
+                                                   uint2* info, int32_t* stab) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int32_t c = cnt_row[e];
+    uint2 in = make_uint2(0u, 0u);
+    if (c >= 1 && c <= X) {
+      const FastDiv f = fastdiv_make((uint32_t)c);
+      in = make_uint2(f.mul, ((uint32_t)c << 8) | (uint32_t)(f.shift + 1));
+    }
+    info[e] = in;
+  }
+  if (kStaged) {
+    for (int i = threadIdx.x; i < E * X; i += blockDim.x) stab[i] = l2p_rows[i];
+  }
+}
+
+// Stage the tables in LDS when they fit in this many bytes.
+constexpr int kStageBytes = 48 * 1024;
+
+// One routing id into a workgroup's LDS counters, or into the invalid count.
+__device__ __forceinline__ void count_id(int32_t e, uint32_t E, int32_t* my, uint32_t& inv) {
+  if ((uint32_t)e < E) {
+    atomicAdd(&my[e], 1);
+  } else {
+    ++inv;
+  }
+}
+
 // ---------------------------------------------------------------- rebalance
 // Everything the rebalance kernel needs about one problem shape, derived on
 // the host: the effective policy, the per-node sizes, and the byte offsets of
@@ -83,6 +136,12 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
 hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                        int32_t* ring, int32_t W, int64_t step, int64_t* load,
                        int64_t* n_invalid, hipStream_t stream);
+hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
+hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
+hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                                int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
+                                const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
+                                hipStream_t stream);
 hipError_t launch_rebalance(const int64_t* load, int64_t B, const RbPlan& plan,
                             int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
                             int32_t* status, hipStream_t stream);

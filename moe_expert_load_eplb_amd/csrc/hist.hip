@@ -27,14 +27,6 @@ __global__ __launch_bounds__(256) void hist_clear_kernel(int32_t* __restrict__ s
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < L; i += stride) n_invalid[i] = 0;
 }
 
-__device__ __forceinline__ void count_id(int32_t e, uint32_t E, int32_t* my, uint32_t& inv) {
-  if ((uint32_t)e < E) {
-    atomicAdd(&my[e], 1);
-  } else {
-    ++inv;
-  }
-}
-
 // Workgroup c of `chunks` per layer takes the layer's 16-byte vectors
 // c*NT + tid + k*chunks*NT, so the workgroups of a layer sweep it together,
 // one contiguous window at a time.  Ids before the layer's first 16-byte
@@ -136,14 +128,23 @@ StreamSplit plan_stream(int64_t L, int64_t per_layer) {
   return s;
 }
 
+hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream) {
+  hist_clear_kernel<<<grid_for(LE > L ? LE : L, 256), 256, 0, stream>>>(slot, LE, n_invalid, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream) {
+  window_sum_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(ring, LE, W, load);
+  return hipGetLastError();
+}
+
 hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                        int32_t* ring, int32_t W, int64_t step, int64_t* load,
                        int64_t* n_invalid, hipStream_t stream) {
   if (L == 0) return hipSuccess;
   const int64_t LE = L * (int64_t)E;
   int32_t* slot = ring + (step % W) * LE;
-  hist_clear_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(slot, LE, n_invalid, L);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_hist_clear(slot, LE, n_invalid, L, stream);
   if (err != hipSuccess) return err;
 
   const int64_t per_layer = T * (int64_t)K;
@@ -157,8 +158,7 @@ hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  window_sum_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(ring, LE, W, load);
-  return hipGetLastError();
+  return launch_window_sum(ring, LE, W, load, stream);
 }
 
 }  // namespace eplb

@@ -17,25 +17,6 @@ namespace eplb {
 
 namespace {
 
-constexpr int kStageBytes = 48 * 1024;
-
-struct LayerTables {
-  const uint2* info;       // per expert: {magic, count << 8 | (shift + 1)}, count 0 = invalid
-  const int32_t* tab;      // [E][X] log2phy rows (LDS or global)
-  uint32_t E;
-  int32_t X;
-};
-
-__device__ __forceinline__ int32_t map_id(int32_t e, uint32_t t, const LayerTables& lt) {
-  if ((uint32_t)e >= lt.E) return -1;
-  const uint2 in = lt.info[e];
-  const uint32_t c = in.y >> 8;
-  if (c == 0) return -1;
-  const int shift = (int)(in.y & 255u) - 1;
-  const uint32_t q = shift < 0 ? t : (uint32_t)(((u64)t * in.x) >> 32) >> shift;
-  const uint32_t r = t - q * c;
-  return lt.tab[e * lt.X + (int32_t)r];
-}
 
 template <bool kStaged>
 __global__ __launch_bounds__(kStreamThreads) void redirect_kernel(const int32_t* __restrict__ idx,
@@ -52,18 +33,7 @@ __global__ __launch_bounds__(kStreamThreads) void redirect_kernel(const int32_t*
   uint2* info = reinterpret_cast<uint2*>(smem);
   int32_t* stab = reinterpret_cast<int32_t*>(smem + (size_t)E * sizeof(uint2));
   const int32_t* gtab = log2phy + layer * (int64_t)E * X;
-  for (int e = tid; e < E; e += kStreamThreads) {
-    const int32_t c = logcnt[layer * E + e];
-    uint2 in = make_uint2(0u, 0u);
-    if (c >= 1 && c <= X) {
-      const FastDiv f = fastdiv_make((uint32_t)c);
-      in = make_uint2(f.mul, ((uint32_t)c << 8) | (uint32_t)(f.shift + 1));
-    }
-    info[e] = in;
-  }
-  if (kStaged) {
-    for (int i = tid; i < E * X; i += kStreamThreads) stab[i] = gtab[i];
-  }
+  stage_layer_tables<kStaged>(logcnt + layer * E, gtab, E, X, info, stab);
   __syncthreads();
   const LayerTables lt{info, kStaged ? stab : gtab, (uint32_t)E, X};
 

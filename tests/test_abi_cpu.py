@@ -37,6 +37,7 @@ def lib():
     lib.eplb_load_hist.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p]
     lib.eplb_rebalance.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, p, p, p]
     lib.eplb_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, p, p]
+    lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
@@ -129,6 +130,15 @@ def test_stream_validation(lib):
     assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, None, FAKE, 9, FAKE, None) == 1
     assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, FAKE, FAKE, 9, FAKE, None) == 1     # out == idx
     assert lib.eplb_redirect(FAKE, 2, (1 << 31) // 8, 8, 256, FAKE, FAKE, 9, FAKE + 64, None) == 6
+    # fused: the union of both calls' rules
+    hr = lambda *a: lib.eplb_hist_redirect(*a)
+    good = [FAKE, 2, 10, 8, 256, FAKE, 4, 0, FAKE, FAKE, FAKE, FAKE, 9, FAKE + 64, None]
+    for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (6, 0, 1), (7, -1, 1), (12, 0, 1), (12, 70000, 5),
+                           (4, 4097, 5), (2, 1 << 28, 6), (0, None, 1), (5, None, 1), (8, None, 1), (9, None, 1),
+                           (10, None, 1), (11, None, 1), (13, None, 1), (13, FAKE, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert hr(*args) == code, (pos, bad)
     assert ok
 
 

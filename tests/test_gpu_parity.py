@@ -339,3 +339,101 @@ def test_repeatable():
     b = [host(t) for t in eplb.rebalance(gpu(load), 288, 8, 4, 32)]
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- fused statistics + redirect
+
+@pytest.mark.parametrize("L,T,K,E", [(3, 20001, 3, 16), (2, 7, 1, 5), (5, 4097, 8, 256),
+                                     (1, 33333, 2, 4096), (4, 1, 3, 3)])
+def test_fused_ragged(L, T, K, E):
+    """One pass gives the oracle's counts, window, invalid counts and
+    redirect, on misaligned layers, ragged tails, invalid ids and counts."""
+    rng = np.random.default_rng(L * T + K + 7)
+    idx_h = rng.integers(-3, E + 3, size=(L, T, K)).astype(np.int32)
+    X = 4
+    logcnt = rng.integers(-1, X + 2, size=(L, E)).astype(np.int32)
+    log2phy = rng.integers(0, 1000, size=(L, E, X)).astype(np.int32)
+    W = 3
+    ring = torch.zeros((W, L, E), dtype=torch.int32, device=DEV)
+    ring[0] = 2
+    note(f"hist_redirect L={L} T={T} K={K} E={E}")
+    load, bad, out = eplb.hist_redirect(gpu(idx_h), E, ring, 7, gpu(log2phy), gpu(logcnt))   # slot 1
+    torch.cuda.synchronize()
+    cnt, invl = ora.load_hist(idx_h, E)
+    assert_same("counts", host(ring[1]).astype(np.int64), cnt)
+    assert_same("invalid", host(bad), invl)
+    assert_same("window", host(load), cnt + 2)
+    assert_same("redirect", host(out), ora.redirect(idx_h, log2phy, logcnt))
+    # an output buffer on a different 16-byte phase than the input
+    big = torch.empty(L * T * K + 1, dtype=torch.int32, device=DEV)
+    out2 = big[1:].view(L, T, K)
+    eplb.hist_redirect(gpu(idx_h), E, ring, 7, gpu(log2phy), gpu(logcnt), out=out2)
+    torch.cuda.synchronize()
+    assert_same("redirect misaligned out", host(out2), ora.redirect(idx_h, log2phy, logcnt))
+    assert_same("counts again", host(ring[1]).astype(np.int64), cnt)
+
+
+@pytest.mark.parametrize("work", [wl.TINY_HIER, wl.DSV3_PREFILL], ids=lambda w: w.name)
+def test_fused_serving_loop(work):
+    """A serving loop: step s is redirected with the placement from the window
+    before s (step 0 with the identity placement of the first rebalance of an
+    all-zero window) and counted into the window; the placement is then
+    recomputed.  Every output matches the oracle run the same way."""
+    pl = work.placement
+    L, E, W = work.layers, pl.E, work.window
+    X = pl.max_count
+    nsteps = 3
+    steps = [wl.routing_step(work, s, tokens=min(work.tokens, 4096)) for s in range(nsteps)]
+    ring = torch.zeros((W, L, E), dtype=torch.int32, device=DEV)
+    load = torch.zeros((L, E), dtype=torch.int64, device=DEV)
+    hists = []
+    ref_load = np.zeros((L, E), dtype=np.int64)
+    for s, idx_h in enumerate(steps):
+        note(f"serving loop {work.name} step {s}")
+        phy2log, log2phy, logcnt, status = eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X)
+        ref = ora.rebalance(ref_load, pl.P, pl.G, pl.N, pl.RK, X)
+        assert_same(f"step {s} log2phy", host(log2phy), ref["log2phy"])
+        load, bad, out = eplb.hist_redirect(gpu(idx_h), E, ring, s, log2phy, logcnt)
+        torch.cuda.synchronize()
+        cnt, invl = ora.load_hist(idx_h, E)
+        hists.append(cnt)
+        ref_load = ora.window_load(hists, W)
+        assert_same(f"step {s} window", host(load), ref_load)
+        assert_same(f"step {s} redirect", host(out), ora.redirect(idx_h, ref["log2phy"], ref["logcnt"]))
+
+
+def test_fused_full_size():
+    """58 x 2^20 x 8 ids: whole-step counts against the oracle, redirect on
+    sampled layers against the oracle and by its properties on every id."""
+    work = wl.STREAM_1M
+    pl = work.placement
+    L, T, K, E, W = work.layers, work.tokens, work.topk, pl.E, work.window
+    idx = torch.empty((L, T, K), dtype=torch.int32, device=DEV)
+    wl.routing_step_device(work, 0, DEV, out=idx)
+    idx_h = host(idx)
+    cnt0, _ = ora.load_hist(idx_h, E)
+    (phy2log, log2phy, logcnt, status), ref = rebalance_both(cnt0, pl.P, pl.G, pl.N, pl.RK)
+    wl.routing_step_device(work, 1, DEV, out=idx)
+    idx_h = host(idx)
+    ring = torch.zeros((W, L, E), dtype=torch.int32, device=DEV)
+    ring[0] = gpu(cnt0.astype(np.int32))
+    note("stream hist_redirect step 1")
+    load, bad, out = eplb.hist_redirect(idx, E, ring, 1, gpu(log2phy), gpu(logcnt))
+    torch.cuda.synchronize()
+    cnt1, invl = ora.load_hist(idx_h, E)
+    assert_same("counts", host(ring[1]).astype(np.int64), cnt1)
+    assert_same("window", host(load), cnt0 + cnt1)
+    assert int(host(bad).sum()) == 0
+    p2l = gpu(phy2log).long()
+    cnt_t = gpu(logcnt).long()
+    l2p = gpu(log2phy).long()
+    t = torch.arange(T, device=DEV).unsqueeze(1)
+    for l in range(L):
+        o = out[l].long()
+        e = idx[l].long()
+        assert bool((p2l[l][o] == e).all())
+        assert bool((l2p[l][e, t % cnt_t[l][e]] == o).all())
+    out_h = host(out)
+    for l in (0, 31, 57):
+        assert_same(f"redirect layer {l}", out_h[l:l + 1],
+                    ora.redirect(idx_h[l:l + 1], ref["log2phy"][l:l + 1], ref["logcnt"][l:l + 1]))
