@@ -49,11 +49,11 @@ namespace {
 // ---------------------------------------------------------------- prime powers
 // Every prime power q = p^k (k >= 1) up to kMaxCount, ascending, with its
 // prime p and the magic numbers of a division by q.
-struct PrimePowers {
-  uint16_t q[2048];
-  uint16_t p[2048];
+struct PrimePowers {           // 32-bit fields: read with scalar loads
+  uint32_t q[2048];
+  uint32_t p[2048];
   uint32_t mul[2048];
-  int8_t shift[2048];
+  int32_t shift[2048];
   int count;
 };
 
@@ -74,10 +74,10 @@ constexpr PrimePowers make_prime_powers() {
     if (r == 1) {                            // q is a power of p
       int l = 0;
       while ((1 << l) < q) ++l;
-      t.q[n] = (uint16_t)q;
-      t.p[n] = (uint16_t)p;
+      t.q[n] = (uint32_t)q;
+      t.p[n] = (uint32_t)p;
       t.mul[n] = (uint32_t)((((unsigned long long)1) << (31 + l)) / (unsigned long long)q + 1);
-      t.shift[n] = (int8_t)(l - 1);
+      t.shift[n] = l - 1;
       ++n;
     }
   }
@@ -90,8 +90,18 @@ __device__ __constant__ PrimePowers kPrimePowers = make_prime_powers();
 // ---------------------------------------------------------------- lane helpers
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int shl1(int x) {           // lane i <- lane i + 1
-  return __builtin_amdgcn_update_dpp(0, x, 0x130, 0xF, 0xF, false);
+__device__ __forceinline__ int shl1(int x) {           // lane i <- lane i + 1 (lane 63 <- 0)
+  return __builtin_amdgcn_mov_dpp(x, 0x130, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int shr1(int x) {           // lane i <- lane i - 1 (lane 0 <- 0)
+  return __builtin_amdgcn_mov_dpp(x, 0x138, 0xF, 0xF, true);
+}
+// Per-step records of a chain: each step shifts the record register up one
+// lane and puts its value in lane 0 (no branch on the chain); after n steps
+// lane i holds step n-1-i.
+__device__ __forceinline__ int push_record(int rec, int x) {
+  const int v = shr1(rec);
+  return lane_id() == 0 ? x : v;
 }
 __device__ __forceinline__ int rdl(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 __device__ __forceinline__ u64 rdl64(u64 x, int l) {
@@ -176,13 +186,18 @@ __device__ __forceinline__ int wave_incl_max(int v) {
 }
 
 // ---------------------------------------------------------------- greedy packing
-// n items, visited in the order of keys[] (item t's key: KW 64-bit words at
-// keys[t * stride], least significant first), go into m packs of `cap` items:
+// n items, visited in order (item t's key: key_of(t, w) for its KW 64-bit
+// words, least significant first), go into m packs of `cap` items:
 // each into the pack with the smallest sum among packs with room, lowest pack
 // index on ties.  res[t] = pack * cap + arrival position of item t.
-// The packs stay sorted across the K registers of the wave (m <= 64 * K).
-template <int K, int KW>
-__device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, int32_t* res) {
+// The packs stay sorted across the K registers of the wave (m <= 64 * K);
+// the element at position 0 is also kept in scalar registers.  Each step
+// reads the element at position 1 before the update: after it, position 0
+// holds either that element (the updated pack moved back, q > 0) or the
+// updated pack itself (q == 0), so the next step starts without waiting for
+// the vector update.
+template <int K, int KW, class KeyOf>
+__device__ void pack_sorted(KeyOf key_of, int n, int m, int cap, int32_t* res) {
   const int lane = lane_id();
   u64 s[KW][K];
   int ic[K];                                   // pack index << 16 | items in it
@@ -193,24 +208,30 @@ __device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, 
     for (int w = 0; w < KW; ++w) s[w][r] = pos < m ? 0ull : ~0ull;
     ic[r] = pos < m ? (pos << 16) : (0x7fff << 16);
   }
+  u64 s0[KW];
+#pragma unroll
+  for (int w = 0; w < KW; ++w) s0[w] = 0;
+  int ic0 = 0;                                 // pack 0, empty
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     u64 kk[KW];
 #pragma unroll
-    for (int w = 0; w < KW; ++w) kk[w] = lane < tn ? keys[(int64_t)(t0 + lane) * stride + w] : 0ull;
+    for (int w = 0; w < KW; ++w) kk[w] = lane < tn ? key_of(t0 + lane, w) : 0ull;
     int rec = 0;
     for (int j = 0; j < tn; ++j) {
-      const int ic0 = rdl(ic[0], 0);
+      u64 s1[KW];
+#pragma unroll
+      for (int w = 0; w < KW; ++w) s1[w] = rdl64(s[w][0], 1);
+      const int ic1 = rdl(ic[0], 1);
       const int c0 = ic0 & 0xffff;
       const int id0 = ic0 & ~0xffff;
-      if (lane == j) rec = (ic0 >> 16) * cap + c0;
+      rec = push_record(rec, (ic0 >> 16) * cap + c0);
       u64 nk[KW];
       u64 carry = 0;
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
-        const u64 a = rdl64(s[w][0], 0);
-        const u64 t = a + rdl64(kk[w], j);
-        const u64 c1 = t < a ? 1ull : 0ull;
+        const u64 t = s0[w] + rdl64(kk[w], j);
+        const u64 c1 = t < s0[w] ? 1ull : 0ull;
         nk[w] = t + carry;
         carry = c1 | (nk[w] < t ? 1ull : 0ull);
       }
@@ -223,10 +244,11 @@ __device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, 
       int q = 0;
 #pragma unroll
       for (int r = 0; r < K; ++r) {
+        if (r > 0 && q < 64 * r - 1) break;       // sorted: nothing further is below
         bool lt = (ic[r] & ~0xffff) < id0;        // decides equal sums
 #pragma unroll
         for (int w = 0; w < KW; ++w) lt = (s[w][r] < nk[w]) || (s[w][r] == nk[w] && lt);
-        u64 mask = ballot(lt);
+        u64 mask = __builtin_amdgcn_ballot_w64(lt);
         if (r == 0) mask &= ~1ull;
         q += __popcll(mask);
       }
@@ -244,8 +266,69 @@ __device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, 
         for (int w = 0; w < KW; ++w) s[w][r] = below ? sd[w][r] : (at ? nk[w] : s[w][r]);
         ic[r] = below ? icd[r] : (at ? nic : ic[r]);
       }
+      if (q > 0) {
+#pragma unroll
+        for (int w = 0; w < KW; ++w) s0[w] = s1[w];
+        ic0 = ic1;
+      } else {
+#pragma unroll
+        for (int w = 0; w < KW; ++w) s0[w] = nk[w];
+        ic0 = nic;
+      }
     }
-    if (lane < tn) res[t0 + lane] = rec;
+    if (lane < tn) res[t0 + tn - 1 - lane] = rec;
+  }
+}
+
+// The same packing with each pack in ONE 64-bit word, sum << 16 | pack << 8 |
+// items, for sums below 2^48, at most 256 packs and at most 255 items per
+// pack; a full pack is all ones.  Words of different packs differ in the pack
+// bits, so one unsigned compare orders packs by (sum, index), and one add of
+// a pre-shifted key (key_of(t) = key << 16 | 1) both adds an item and
+// counts it.  A lone
+// wavefront issues about one instruction per four cycles, so the step's
+// instruction count is its latency; this form has about half the
+// instructions of the general one.  res[t] = pack * cap + arrival position.
+template <int K, class KeyOf>
+__device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+  const int lane = lane_id();
+  u64 w[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    w[r] = pos < m ? ((u64)pos << 8) : ~0ull;
+  }
+  u64 w0 = 0;                                  // pack 0, empty
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int tn = n - t0 < 64 ? n - t0 : 64;
+    const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
+    int rec = 0;
+    for (int j = 0; j < tn; ++j) {
+      const u64 w1 = rdl64(w[0], 1);           // position 1 before this step's update
+      rec = push_record(rec, (int)((w0 >> 8) & 0xff) * cap + (int)(w0 & 0xff));
+      u64 nw = w0 + rdl64(kk, j);
+      if ((int)(nw & 0xff) == cap) nw = ~0ull;
+      int q = __popcll(__builtin_amdgcn_ballot_w64(w[0] < nw) & ~1ull);
+#pragma unroll
+      for (int r = 1; r < K; ++r) {
+        if (q < 64 * r - 1) break;             // sorted: later registers hold nothing below nw
+        q += __popcll(__builtin_amdgcn_ballot_w64(w[r] < nw));
+      }
+      if (K == 1 || q < 64) {
+        const u64 d = shl1_64(w[0]);
+        w[0] = lane < q ? d : (lane == q ? nw : w[0]);
+      } else {
+        u64 wd[K];
+        shift_down64<K>(w, wd);
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          const int pos = r * 64 + lane;
+          w[r] = pos < q ? wd[r] : (pos == q ? nw : w[r]);
+        }
+      }
+      w0 = q > 0 ? w1 : nw;
+    }
+    if (lane < tn) res[t0 + tn - 1 - lane] = rec;
   }
 }
 
@@ -254,46 +337,59 @@ __device__ void pack_sorted(const u64* keys, int stride, int n, int m, int cap, 
 // (u, ci) (ci = count << 16 | local index); positions >= En hold the
 // sentinel (0, 1 << 16 | 0xffff), which never moves ahead of an expert.
 // Rn times: the expert at position 0 (highest load per replica, lowest index
-// on ties) gets a replica and moves to its new place.
+// on ties) gets a replica and moves to its new place.  As in pack_sorted,
+// position 0 is also kept in scalar registers and the next one is chosen
+// from position 1 read before the update.
 // rep[r] = local index | rank << 16 of the r-th replica created.
 template <int K>
 __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep) {
   const int lane = lane_id();
+  u64 u0 = rdl64(u[0], 0);
+  int ci0 = rdl(ci[0], 0);
   for (int r0 = 0; r0 < Rn; r0 += 64) {
     const int tn = Rn - r0 < 64 ? Rn - r0 : 64;
     int rec = 0;
     for (int j = 0; j < tn; ++j) {
-      const u64 u0 = rdl64(u[0], 0);
-      const int ci0 = rdl(ci[0], 0);
+      const u64 u1 = rdl64(u[0], 1);
+      const int ci1 = rdl(ci[0], 1);
       const int c0 = ci0 >> 16;
       const int i0 = ci0 & 0xffff;
-      if (lane == j) rec = i0 | (c0 << 16);
+      rec = push_record(rec, i0 | (c0 << 16));
       const int nc = c0 + 1;
       const int nci = (nc << 16) | i0;
       int q = 0;
 #pragma unroll
       for (int r = 0; r < K; ++r) {
+        if (r > 0 && q < 64 * r - 1) break;       // sorted: nothing further comes first
         const u64 lhs = u[r] * (u64)(uint32_t)nc;             // u_p / c_p  vs  u0 / nc
         const u64 rhs = u0 * (u64)(uint32_t)(ci[r] >> 16);
         const bool before = lhs > rhs || (lhs == rhs && (ci[r] & 0xffff) < i0);
-        u64 mask = ballot(before);
+        u64 mask = __builtin_amdgcn_ballot_w64(before);
         if (r == 0) mask &= ~1ull;
         q += __popcll(mask);
       }
-      u64 ud[K];
-      int cid[K];
-      shift_down64<K>(u, ud);
-      shift_down<K>(ci, cid);
+      if (K == 1 || q < 64) {                     // only register 0 moves
+        const u64 ud = shl1_64(u[0]);
+        const int cid = shl1(ci[0]);
+        u[0] = lane < q ? ud : (lane == q ? u0 : u[0]);
+        ci[0] = lane < q ? cid : (lane == q ? nci : ci[0]);
+      } else {
+        u64 ud[K];
+        int cid[K];
+        shift_down64<K>(u, ud);
+        shift_down<K>(ci, cid);
 #pragma unroll
-      for (int r = 0; r < K; ++r) {
-        const int pos = r * 64 + lane;
-        const bool below = pos < q;
-        const bool at = pos == q;
-        u[r] = below ? ud[r] : (at ? u0 : u[r]);
-        ci[r] = below ? cid[r] : (at ? nci : ci[r]);
+        for (int r = 0; r < K; ++r) {
+          const int pos = r * 64 + lane;
+          const bool below = pos < q;
+          const bool at = pos == q;
+          u[r] = below ? ud[r] : (at ? u0 : u[r]);
+          ci[r] = below ? cid[r] : (at ? nci : ci[r]);
+        }
       }
+      if (q > 0) { u0 = u1; ci0 = ci1; } else { ci0 = nci; }
     }
-    if (lane < tn) rep[r0 + lane] = rec;
+    if (lane < tn) rep[r0 + tn - 1 - lane] = rec;
   }
 }
 
@@ -304,9 +400,7 @@ struct Smem {
   u64* w;          // [E]   loads, logical order
   u64* wl;         // [E]   loads, mlog order (node n: [n*En, n*En+En))
   u64* gsum;       // [Gp]
-  u64* ordk;       // [nscr][max(Pn, Gp)][2]  per-wave item keys in visiting order
   int32_t* m2l;    // [E]
-  int32_t* l2m;    // [E]
   int32_t* cnt;    // [E]   replica count per mlog expert
   int32_t* srt;    // [E]   per node: local expert index at each sorted position
   int32_t* gnode;  // [Gp]
@@ -315,10 +409,10 @@ struct Smem {
   int32_t* gres;   // [Gp]  packing result per visiting rank
   int32_t* rep;    // [Np][Rn]
   int32_t* posaux; // [nscr][3 * En]  per wave: class start, item offset, position of expert
-  int32_t* ordr;   // [nscr][Pn]  per wave: item (logical expert | rank << 16) in visiting order
+  int32_t* ordr;   // [nscr][Pn]  per wave: item (local expert | rank << 16) in visiting order
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
   int32_t* rcls;   // [nscr][Rn]  per wave: class of each replica
-  int32_t* nflag;  // [Np]  1 when the node's sums fit 64 bits
+  int32_t* nflag;  // [Np]  step-3 key form: 2 one word per pack, 1 64-bit sums, 0 128-bit sums
   int32_t* flags;  // [4]
 };
 
@@ -328,9 +422,7 @@ __device__ Smem carve(unsigned char* base, const RbPlan& p) {
   s.w = (u64*)(base + p.o_w);
   s.wl = (u64*)(base + p.o_wl);
   s.gsum = (u64*)(base + p.o_gsum);
-  s.ordk = (u64*)(base + p.o_ordk);
   s.m2l = (int32_t*)(base + p.o_m2l);
-  s.l2m = (int32_t*)(base + p.o_l2m);
   s.cnt = (int32_t*)(base + p.o_cnt);
   s.srt = (int32_t*)(base + p.o_srt);
   s.gnode = (int32_t*)(base + p.o_gnode);
@@ -427,7 +519,8 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   const u128 total = mul_u128_u64(D, sum, ovf);
   if (lane == 0) {
     if (ovf || (total >> 127) != 0) s.flags[0] = EPLB_S_OVERFLOW;
-    s.nflag[n] = (u64)(total >> 64) == 0 ? 1 : 0;
+    // key width for step 3: one word per pack, 64-bit sums, or 128-bit sums
+    s.nflag[n] = (total >> 48) == 0 && p.RKn <= 256 && p.ppr <= 255 ? 2 : ((u64)(total >> 64) == 0 ? 1 : 0);
   }
 #pragma unroll
   for (int r = 0; r < K; ++r) {
@@ -463,12 +556,11 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
   } else {
     int32_t* ordr = s.ordr + ws * Pn;
     int32_t* ores = s.ores + ws * Pn;
-    u64* ordk = s.ordk + (int64_t)ws * (Pn > p.Gp ? Pn : p.Gp) * 2;
     int32_t* cstart = s.posaux + ws * 3 * En;   // class start of each position
     int32_t* coff = cstart + En;                 // item offset of each position
     int32_t* posof = coff + En;                  // position of each local expert
     int32_t* rcls = s.rcls + ws * (Rn > 0 ? Rn : 1);
-    const bool wide = s.nflag[n] == 0;
+    const int width = s.nflag[n];
 
     // positions in the final order: (u, c, local index)
     u64 u[K];
@@ -515,36 +607,35 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
       const int pos = r * 64 + lane;
       if (pos < En) {
         const int st = cstart[pos];
-        const int rank = coff[st] + (pos - st);
-        ordr[rank] = m2l[li[r]];
-        const u128 key = s.kexp[n * En + li[r]];
-        ordk[rank * 2] = (u64)key;
-        ordk[rank * 2 + 1] = (u64)(key >> 64);
+        ordr[coff[st] + (pos - st)] = li[r];
       }
     }
     for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]];
     wave_lds_sync();
     for (int rr = lane; rr < Rn; rr += 64) {   // replicas
-      const int v = rep[rr];
       const int cls = rcls[rr];
       int before = 0;
       for (int r2 = 0; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
       int size = 1;
       while (cls + size < En && cstart[cls + size] == cls) ++size;
-      const int rank = coff[cls] + size + before;
-      const int li_r = v & 0xffff;
-      ordr[rank] = m2l[li_r] | (v & ~0xffff);
-      const u128 key = s.kexp[n * En + li_r];
-      ordk[rank * 2] = (u64)key;
-      ordk[rank * 2 + 1] = (u64)(key >> 64);
+      ordr[coff[cls] + size + before] = rep[rr];   // local index | rank << 16
     }
     wave_lds_sync();
-    if (wide) pack_sorted<KP, 2>(ordk, 2, Pn, p.RKn, p.ppr, ores);
-    else pack_sorted<KP, 1>(ordk, 2, Pn, p.RKn, p.ppr, ores);
+    const u128* kexp = s.kexp + n * En;
+    if (width == 2) {
+      auto key = [=](int t) { return ((u64)kexp[ordr[t] & 0xffff] << 16) | 1ull; };
+      pack_words<KP>(key, Pn, p.RKn, p.ppr, ores);
+    } else if (width == 1) {
+      auto key = [=](int t, int) { return (u64)kexp[ordr[t] & 0xffff]; };
+      pack_sorted<KP, 1>(key, Pn, p.RKn, p.ppr, ores);
+    } else {
+      auto key = [=](int t, int w) { const u128 k = kexp[ordr[t] & 0xffff]; return w ? (u64)(k >> 64) : (u64)k; };
+      pack_sorted<KP, 2>(key, Pn, p.RKn, p.ppr, ores);
+    }
     wave_lds_sync();
     for (int t = lane; t < Pn; t += 64) {
       const int v = ordr[t];
-      const int e = v & 0xffff;
+      const int e = m2l[v & 0xffff];
       const int rk = v >> 16;
       const int pid = n * Pn + ores[t];
       o_phy[pid] = e;
@@ -563,7 +654,8 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
 // ---------------------------------------------------------------- kernel
 
 template <int KR, int KP>
-__global__ __launch_bounds__(512) void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 512), amdgpu_waves_per_eu(KR * KP <= 2 ? 8 : 1)))
+void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
                                                          int32_t* __restrict__ phy2log,
                                                          int32_t* __restrict__ log2phy,
                                                          int32_t* __restrict__ logcnt,
@@ -615,10 +707,21 @@ __global__ __launch_bounds__(512) void rebalance_kernel(const int64_t* __restric
     }
     __syncthreads();
     if (wid == 0) {
-      for (int t = lane; t < p.Gp; t += 64) s.ordk[t] = s.gsum[s.gord[t]];
-      wave_lds_sync();
-      if (p.KN == 1) pack_sorted<1, 1>(s.ordk, 1, p.Gp, p.Np, p.gpn, s.gres);
-      else pack_sorted<8, 1>(s.ordk, 1, p.Gp, p.Np, p.gpn, s.gres);
+      u64 tot = 0;
+      for (int g = lane; g < p.Gp; g += 64) tot += s.gsum[g];
+      tot = wave_sum64(tot);
+      const bool words = (tot >> 48) == 0 && p.Np <= 256 && p.gpn <= 255;
+      const u64* gsum = s.gsum;
+      const int32_t* gord = s.gord;
+      if (words) {
+        auto key = [=](int t) { return (gsum[gord[t]] << 16) | 1ull; };
+        if (p.KN == 1) pack_words<1>(key, p.Gp, p.Np, p.gpn, s.gres);
+        else pack_words<8>(key, p.Gp, p.Np, p.gpn, s.gres);
+      } else {
+        auto key = [=](int t, int) { return gsum[gord[t]]; };
+        if (p.KN == 1) pack_sorted<1, 1>(key, p.Gp, p.Np, p.gpn, s.gres);
+        else pack_sorted<8, 1>(key, p.Gp, p.Np, p.gpn, s.gres);
+      }
       wave_lds_sync();
       for (int t = lane; t < p.Gp; t += 64) {
         const int g = s.gord[t];
@@ -636,7 +739,6 @@ __global__ __launch_bounds__(512) void rebalance_kernel(const int64_t* __restric
     const int j = e - g * p.S;
     const int m = (s.gnode[g] * p.gpn + s.gslot[g]) * p.S + j;
     s.m2l[m] = e;
-    s.l2m[e] = m;
     s.wl[m] = s.w[e];
   }
   __syncthreads();
@@ -731,26 +833,30 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
     off += bytes;
     return (int32_t)at;
   };
-  const int64_t ordk_items = p.Pn > Gp ? p.Pn : Gp;
   const int64_t rn1 = p.Rn > 0 ? p.Rn : 1;
   p.o_kexp = take(16ll * E, 16);
-  p.o_ordk = take(16ll * nscr * ordk_items, 16);
-  p.o_w = take(8ll * E, 8);
   p.o_wl = take(8ll * E, 8);
-  p.o_gsum = take(8ll * Gp, 8);
   p.o_m2l = take(4ll * E, 4);
-  p.o_l2m = take(4ll * E, 4);
   p.o_cnt = take(4ll * E, 4);
   p.o_srt = take(4ll * E, 4);
+  p.o_rep = take(4ll * Np * rn1, 4);
+  // Two overlaid regions: the loads and step-1 arrays die once the mlog
+  // order is built; the per-wave step-3 scratch is used only after that.
+  const int64_t base = (off + 15) / 16 * 16;
+  off = base;
+  p.o_w = take(8ll * E, 8);
+  p.o_gsum = take(8ll * Gp, 8);
   p.o_gnode = take(4ll * Gp, 4);
   p.o_gslot = take(4ll * Gp, 4);
   p.o_gord = take(4ll * Gp, 4);
   p.o_gres = take(4ll * Gp, 4);
-  p.o_rep = take(4ll * Np * rn1, 4);
+  const int64_t end1 = off;
+  off = base;
   p.o_posaux = take(12ll * nscr * p.En, 4);
   p.o_ordr = take(4ll * nscr * p.Pn, 4);
   p.o_ores = take(4ll * nscr * p.Pn, 4);
   p.o_rcls = take(4ll * nscr * rn1, 4);
+  if (off < end1) off = end1;
   p.o_nflag = take(4ll * Np, 4);
   p.o_flags = take(16, 4);
   off = (off + 15) / 16 * 16;
