@@ -345,3 +345,58 @@ def redirect_loop(idx, log2phy, logcnt) -> list:
                     if 1 <= c <= X:
                         out[l][t][k] = int(log2phy[l][e][t % c])
     return out
+
+
+# --------------------------------------------------------------------------
+# Load estimate by exponential moving average, and placement quality
+# --------------------------------------------------------------------------
+
+def ema_update(ema: np.ndarray, cnt: np.ndarray, shift: int) -> np.ndarray:
+    """One step of an integer exponential moving average of the load.
+
+    The pages predict load with a moving average over history ([EPLB-ru],
+    opening section).  This variant keeps, per (layer, expert), an integer
+    ema <- ema - floor(ema / 2^shift) + cnt, a decay of 1 - 2^-shift per step
+    in exact integer arithmetic (steady state: about 2^shift x the per-step
+    count).  shift = 0 keeps only the latest step.
+    """
+    ema = [int(x) for x in np.asarray(ema, dtype=np.int64).ravel().tolist()]
+    cnt = [int(x) for x in np.asarray(cnt, dtype=np.int64).ravel().tolist()]
+    out = [e - (e >> shift) + c for e, c in zip(ema, cnt)]
+    return np.array(out, dtype=np.int64)
+
+
+def placement_load(load, phy2log, logcnt, RK: int):
+    """Exact load of every rank (GPU) under a placement, and max / mean.
+
+    A rank's load is the sum over its physical experts of load[e] / logcnt[e]
+    (each replica takes an equal share of its expert's tokens; [EPLB-ru]
+    glossary), as in the translator's hands-on exercise 2 after the annotated
+    source (add up weight / logcnt per GPU, compare max / mean between the
+    policies) and the check of the worked example under "Интерфейс и пример".
+    Returns (rank_loads as Fractions [B][RK], imbalance [B] as Fractions
+    max / mean, 1 when every load is 0; both None for a problem whose maps name
+    an expert outside [0, E) or a count below 1, or with a load outside
+    [0, 2^40] as for the rebalance).
+    """
+    load = np.asarray(load)
+    phy2log = np.asarray(phy2log)
+    logcnt = np.asarray(logcnt)
+    B, E = load.shape
+    P = phy2log.shape[1]
+    ppr = P // RK
+    ranks, imb = [], []
+    for b in range(B):
+        w = [int(x) for x in load[b].tolist()]
+        c = [int(x) for x in logcnt[b].tolist()]
+        phy = [int(x) for x in phy2log[b].tolist()]
+        if any(x < 0 or x > LOAD_MAX for x in w) or any(not (0 <= e < E) or c[e] < 1 for e in phy):
+            ranks.append(None)
+            imb.append(None)
+            continue
+        r = [sum((Fraction(w[phy[g * ppr + s]], c[phy[g * ppr + s]]) for s in range(ppr)), Fraction(0))
+             for g in range(RK)]
+        mean = Fraction(sum(w), RK)
+        ranks.append(r)
+        imb.append(Fraction(1) if mean == 0 else max(r) / mean)
+    return ranks, imb

@@ -367,8 +367,73 @@ def pin_redirect(o):
                 assert list(r["log2phy"][l, e, :c]).index(p) == t % c
 
 
+def pin_ema(o):
+    """EMA: shift 0 keeps the latest counts; a plain loop agrees; from zero
+    with constant counts c the estimate rises monotonically and settles where
+    floor(e / 2^s) = c, i.e. in [c * 2^s, c * 2^s + 2^s); a hand-worked
+    sequence for shift 2."""
+    rng = np.random.default_rng(19)
+    cnt = rng.integers(0, 1000, size=(3, 7))
+    ema = rng.integers(0, 10**6, size=(3, 7))
+    assert (o.ema_update(ema, cnt, 0).reshape(3, 7) == cnt).all()
+    for s in (1, 3, 10):
+        got = o.ema_update(ema, cnt, s).reshape(3, 7)
+        want = [[int(ema[i, j]) - (int(ema[i, j]) >> s) + int(cnt[i, j]) for j in range(7)] for i in range(3)]
+        assert got.tolist() == want
+    for c, s in ((5, 2), (1000, 4), (0, 3), (1, 1)):
+        e = np.zeros(1, dtype=np.int64)
+        prev = -1
+        for _ in range(400):
+            e = o.ema_update(e, np.array([c]), s)
+            assert int(e[0]) >= prev
+            prev = int(e[0])
+        assert c << s <= int(e[0]) < (c << s) + (1 << s) or (c == 0 and int(e[0]) == 0)
+    e = np.zeros(1, dtype=np.int64)
+    seq = []
+    for c in (8, 8, 0, 4):
+        e = o.ema_update(e, np.array([c]), 2)
+        seq.append(int(e[0]))
+    assert seq == [8, 14, 11, 13]      # 0-0+8; 8-2+8; 14-3+0; 11-2+4
+
+
+def pin_placement_load(o):
+    """Per-GPU loads of the worked example's layer 0: range 86.5..156, mean
+    ~129 (hierarchical); 95.5..138.5 with num_groups = 3 (global); the sum of
+    rank loads equals the total load; a bad map gives None."""
+    w, r = _example(o)
+    ranks, imb = o.placement_load(w, r["phy2log"], r["logcnt"], 8)
+    g = GOLDEN["layer0_gpu_load_hierarchical"]
+    assert min(ranks[0]) == Fraction(g["min"]) and max(ranks[0]) == Fraction(g["max"])
+    assert round(sum(ranks[0]) / 8) == g["mean_rounded"]
+    assert imb[0] == Fraction(g["max"]) / (Fraction(int(w[0].sum()), 8))
+    for b in range(2):
+        assert sum(ranks[b]) == int(w[b].sum())
+    gg = GOLDEN["layer0_gpu_load_global_groups3"]
+    w, r = _example(o, groups=gg["num_groups"], X=5)
+    ranks, _ = o.placement_load(w, r["phy2log"], r["logcnt"], 8)
+    assert min(ranks[0]) == Fraction(gg["min"]) and max(ranks[0]) == Fraction(gg["max"])
+    bad = r["phy2log"].copy()
+    bad[1, 3] = 12
+    ranks, imb = o.placement_load(w, bad, r["logcnt"], 8)
+    assert ranks[1] is None and imb[1] is None and ranks[0] is not None
+    cnt0 = r["logcnt"].copy()
+    cnt0[0, int(r["phy2log"][0, 0])] = 0
+    assert o.placement_load(w, r["phy2log"], cnt0, 8)[1][0] is None
+    for v in (-1, (1 << 40) + 1):
+        wb = w.copy()
+        wb[0, 5] = v
+        assert o.placement_load(wb, r["phy2log"], r["logcnt"], 8)[1][0] is None
+    wb = w.copy()
+    wb[0, 5] = 1 << 40
+    assert o.placement_load(wb, r["phy2log"], r["logcnt"], 8)[1][0] is not None
+    z = np.zeros((1, 12), dtype=np.int64)
+    rz = o.rebalance(z, 16, 4, 2, 8, 3)
+    _, imb = o.placement_load(z, rz["phy2log"], rz["logcnt"], 8)
+    assert imb[0] == 1
+
+
 ALL_PINS = [pin_golden_phy2log, pin_golden_layer0, pin_golden_gpu_loads, pin_dsv3_shape,
             pin_replication_bruteforce, pin_replication_dhondt, pin_packing_closed_forms,
             pin_identity_cases, pin_degenerate_loads, pin_exact_arithmetic, pin_invariants_random,
             pin_status_rules,
-            pin_hist_bruteforce, pin_window, pin_redirect]
+            pin_hist_bruteforce, pin_window, pin_redirect, pin_ema, pin_placement_load]

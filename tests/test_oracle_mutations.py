@@ -40,6 +40,10 @@ MUTANTS = {
     "hist_drops_expert_zero": ("ok = (flat >= 0) & (flat < E)", "ok = (flat > 0) & (flat < E)"),
     "window_oldest_steps": ("recent = step_hists[-W:]", "recent = step_hists[:W]"),
     "redirect_by_k": ("t = np.arange(T, dtype=np.int64)[:, None]", "t = np.arange(K, dtype=np.int64)[None, :]"),
+    "ema_rounds_up": ("out = [e - (e >> shift) + c for e, c in zip(ema, cnt)]",
+                      "out = [e - (-(-e >> shift)) + c for e, c in zip(ema, cnt)]"),
+    "rank_load_ignores_count": ("r = [sum((Fraction(w[phy[g * ppr + s]], c[phy[g * ppr + s]])",
+                                "r = [sum((Fraction(w[phy[g * ppr + s]], 1)"),
 }
 
 
