@@ -4,7 +4,9 @@
  * Three calls make up the path: a per-layer expert-load histogram of top-k
  * routing ids summed over a window of steps, the batched rebalance that turns
  * loads into a replica placement (phy2log / log2phy / logcnt), and the
- * redirect of routed logical ids to physical replicas.
+ * redirect of routed logical ids to physical replicas.  Around them: the
+ * histogram and redirect fused in one pass, a moving-average load estimate,
+ * and the per-rank load of a placement (its max / mean).
  *
  * What each call computes is defined by the EPLB README and its annotated
  * source on the translation page «DualPipe и EPLB: конвейер в обе стороны и
@@ -149,6 +151,64 @@ int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
                            int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
                            const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
                            void* stream);
+
+/*
+ * eplb_load_ema -- expert load of one step, and an integer moving average.
+ *
+ * Follows: the opening section of Part 2 (load is predicted from historical
+ * statistics, a moving average being the usual way) and the glossary (load =
+ * tokens routed to the expert).  An alternative to the window of
+ * eplb_load_hist that keeps one int64 per expert instead of W histograms:
+ *     ema[l][e] <- ema[l][e] - floor(ema[l][e] / 2^shift) + count[l][e]
+ * a decay of 1 - 2^-shift per step in exact integer arithmetic.  From zero
+ * with a steady count c it rises to [c * 2^shift, (c + 1) * 2^shift), so for
+ * eplb_rebalance (loads <= 2^40) keep count * 2^shift below 2^40.
+ *
+ *   idx        [L][T][K] int32   logical ids (as for eplb_load_hist)
+ *   count      [L][E] int32      out: this step's histogram
+ *   shift                        0 .. 62 (0 keeps only the latest step)
+ *   ema        [L][E] int64      in/out: the estimate; zero it once before
+ *                                the first step; values must stay below 2^62
+ *   n_invalid  [L] int64         out: ids of layer l outside [0, E)
+ *
+ * Errors: as for eplb_load_hist; EPLB_E_ARG also for shift outside 0 .. 62.
+ */
+int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                      int32_t* count, int32_t shift, int64_t* ema, int64_t* n_invalid, void* stream);
+
+/*
+ * eplb_placement_load -- load of every rank under a placement, and max / mean.
+ *
+ * Follows: the glossary of Part 2 (each copy of an expert takes an equal
+ * share of its tokens), the translator's hands-on exercise 2 after the
+ * annotated source (sum weight / logcnt over the experts of each GPU and
+ * compare max / mean between the policies) and the check of the worked
+ * example under "Интерфейс и пример" (GPU loads 86.5 .. 156, mean 129).
+ *     rank_load[b][r] = sum over s < P/RK of load[b][e] / logcnt[b][e],
+ *                       e = phy2log[b][r * (P/RK) + s]
+ *     imbalance[b]    = max_r rank_load[b][r] / (sum_e load[b][e] / RK),
+ *                       1 when every load is 0
+ * Works for any placement, also one computed from older loads (to decide
+ * whether to rebalance).  Double precision: each rank load is within
+ * (P/RK + 1) * 2^-53 relative of the exact rational, imbalance within
+ * (P/RK + 3) * 2^-53.  logcnt is not checked against phy2log.
+ *
+ *   load       [B][E] int64      token counts, 0 .. 2^40
+ *   phy2log    [B][P] int32      logical expert of each physical slot
+ *   logcnt     [B][E] int32      replicas per logical expert
+ *   B, E, P, RK                  problems (>= 0), logical experts, physical
+ *                                experts, ranks (>= 1; RK divides P)
+ *   rank_load  [B][RK] double    out
+ *   imbalance  [B] double        out
+ * A problem with a load outside [0, 2^40], a phy2log entry outside [0, E) or
+ * a referenced count below 1 gets NaN in all its outputs.
+ *
+ * Errors: EPLB_E_ARG (a size out of range or a NULL array), EPLB_E_DIV
+ * (P % RK != 0), EPLB_E_HIP.
+ */
+int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
+                            int64_t B, int32_t E, int32_t P, int32_t RK,
+                            double* rank_load, double* imbalance, void* stream);
 
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);

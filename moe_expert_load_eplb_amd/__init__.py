@@ -31,7 +31,7 @@ EPLB_S_BAD_LOAD = 16
 EPLB_S_OVERFLOW = 17
 
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
-           "eplb_status_string", "eplb_rebalance_lds_bytes")
+           "eplb_load_ema", "eplb_placement_load", "eplb_status_string", "eplb_rebalance_lds_bytes")
 
 
 def _load() -> ctypes.CDLL:
@@ -52,6 +52,10 @@ def _load() -> ctypes.CDLL:
     lib.eplb_redirect.restype = i32
     lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
     lib.eplb_hist_redirect.restype = i32
+    lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
+    lib.eplb_load_ema.restype = i32
+    lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
+    lib.eplb_placement_load.restype = i32
     lib.eplb_status_string.argtypes = [i32]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -206,3 +210,59 @@ def hist_redirect(idx: torch.Tensor, E: int, ring: torch.Tensor, step: int,
                                 _stream(dev))
     _check(rc, "eplb_hist_redirect")
     return load, n_invalid, out
+
+
+def load_ema(idx: torch.Tensor, E: int, ema: torch.Tensor, shift: int,
+             count: torch.Tensor | None = None, n_invalid: torch.Tensor | None = None):
+    """Count one step's routing ids and fold them into an integer moving
+    average: ema <- ema - (ema >> shift) + count, in place.
+
+    idx [L, T, K] int32; ema [L, E] int64 (zeroed once by the caller).
+    Returns (ema, count [L, E] int32, n_invalid [L] int64).
+    """
+    if idx.dim() != 3:
+        raise ValueError("idx must be [L, T, K]")
+    L, T, K = idx.shape
+    if tuple(ema.shape) != (L, E):
+        raise ValueError(f"ema must be [{L}, {E}], got {tuple(ema.shape)}")
+    dev = idx.device
+    if count is None:
+        count = torch.empty((L, E), dtype=torch.int32, device=dev)
+    if n_invalid is None:
+        n_invalid = torch.empty((L,), dtype=torch.int64, device=dev)
+    if tuple(count.shape) != (L, E) or tuple(n_invalid.shape) != (L,):
+        raise ValueError("count must be [L, E] and n_invalid [L]")
+    rc = lib.eplb_load_ema(_dev(idx, torch.int32, "idx"), L, T, K, E, _dev(count, torch.int32, "count"),
+                           int(shift), _dev(ema, torch.int64, "ema"), _dev(n_invalid, torch.int64, "n_invalid"),
+                           _stream(dev))
+    _check(rc, "eplb_load_ema")
+    return ema, count, n_invalid
+
+
+def placement_load(load: torch.Tensor, phy2log: torch.Tensor, logcnt: torch.Tensor, RK: int,
+                   out: tuple | None = None):
+    """Load of every rank under a placement and its max / mean.
+
+    load [B, E] int64, phy2log [B, P] int32, logcnt [B, E] int32.
+    Returns (rank_load [B, RK] float64, imbalance [B] float64); NaN marks a
+    problem with an invalid load or map.
+    """
+    if load.dim() != 2 or phy2log.dim() != 2 or logcnt.dim() != 2:
+        raise ValueError("load [B, E], phy2log [B, P], logcnt [B, E] expected")
+    B, E = load.shape
+    P = phy2log.shape[1]
+    if phy2log.shape[0] != B or tuple(logcnt.shape) != (B, E):
+        raise ValueError("phy2log / logcnt do not match load")
+    dev = load.device
+    if out is None:
+        out = (torch.empty((B, RK), dtype=torch.float64, device=dev),
+               torch.empty((B,), dtype=torch.float64, device=dev))
+    rank_load, imbalance = out
+    if tuple(rank_load.shape) != (B, RK) or tuple(imbalance.shape) != (B,):
+        raise ValueError("outputs must be [B, RK] and [B]")
+    rc = lib.eplb_placement_load(_dev(load, torch.int64, "load"), _dev(phy2log, torch.int32, "phy2log"),
+                                 _dev(logcnt, torch.int32, "logcnt"), B, E, P, int(RK),
+                                 _dev(rank_load, torch.float64, "rank_load"),
+                                 _dev(imbalance, torch.float64, "imbalance"), _stream(dev))
+    _check(rc, "eplb_placement_load")
+    return rank_load, imbalance

@@ -77,6 +77,29 @@ int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                      int32_t* count, int32_t shift, int64_t* ema, int64_t* n_invalid, void* stream) {
+  int32_t rc = check_stream_args(idx, L, T, K, E);
+  if (rc != EPLB_OK) return rc;
+  if (shift < 0 || shift > 62) return EPLB_E_ARG;
+  if (L > 0 && (count == nullptr || ema == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
+  hipError_t err = launch_load_ema(idx, L, T, K, E, count, shift, ema, n_invalid, (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
+int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
+                            int64_t B, int32_t E, int32_t P, int32_t RK,
+                            double* rank_load, double* imbalance, void* stream) {
+  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || P < 1 || RK < 1) return EPLB_E_ARG;
+  if (P % RK != 0) return EPLB_E_DIV;
+  if (B > 0 && (load == nullptr || phy2log == nullptr || logcnt == nullptr || rank_load == nullptr ||
+                imbalance == nullptr))
+    return EPLB_E_ARG;
+  hipError_t err = launch_placement_load(load, phy2log, logcnt, B, E, P, RK, rank_load, imbalance,
+                                         (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);

@@ -136,6 +136,12 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
 hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                        int32_t* ring, int32_t W, int64_t step, int64_t* load,
                        int64_t* n_invalid, hipStream_t stream);
+hipError_t launch_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                           int32_t* cnt, int32_t shift, int64_t* ema, int64_t* n_invalid,
+                           hipStream_t stream);
+hipError_t launch_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
+                                 int64_t B, int32_t E, int32_t P, int32_t RK, double* rank_load,
+                                 double* imbalance, hipStream_t stream);
 hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
 hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
 hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,

@@ -1,10 +1,12 @@
-// Expert-load histogram of top-k routing ids, and its sum over a window of steps.
+// Expert-load histogram of top-k routing ids, and the load estimate built from
+// it: the sum over a window of steps, or an integer moving average.
 //
 // The load of a logical expert is the number of tokens the router sent to it
 // during the observation period (glossary of Part 2 of the EPLB README
 // translation, «DualPipe и EPLB», ai.flicky.cc); the prediction uses the
-// statistics of past steps (opening section of Part 2).  Three kernels on one
-// stream: clear the ring slot of this step, count, then sum the window.
+// statistics of past steps, a moving average for instance (opening section of
+// Part 2).  Three kernels on one stream: clear this step's counts, count, then
+// sum the window (or update the moving average).
 //
 // Counting is HBM-bound: 4 bytes read per routing id.  A few workgroups per
 // layer sweep the layer together with 16-byte non-temporal loads (all layers
@@ -103,6 +105,18 @@ __global__ __launch_bounds__(256) void window_sum_kernel(const int32_t* __restri
   }
 }
 
+// One step of the integer moving average: ema <- ema - floor(ema / 2^shift) + cnt.
+// Unsigned arithmetic keeps a wrap (values near 2^63, outside the documented
+// range) defined; >> of the signed value is the floor for negative values too.
+__global__ __launch_bounds__(256) void ema_update_kernel(const int32_t* __restrict__ cnt, int64_t LE,
+                                                         int32_t shift, int64_t* __restrict__ ema) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) {
+    const int64_t e = ema[i];
+    ema[i] = (int64_t)((u64)e - (u64)(e >> shift) + (u64)(int64_t)cnt[i]);
+  }
+}
+
 int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
   if (g < 1) g = 1;
@@ -138,12 +152,15 @@ hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
-                       int32_t* ring, int32_t W, int64_t step, int64_t* load,
-                       int64_t* n_invalid, hipStream_t stream) {
-  if (L == 0) return hipSuccess;
+hipError_t launch_ema_update(const int32_t* cnt, int64_t LE, int32_t shift, int64_t* ema, hipStream_t stream) {
+  ema_update_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(cnt, LE, shift, ema);
+  return hipGetLastError();
+}
+
+// Clear `slot` ([L][E]) and `n_invalid`, then count the step's ids into them.
+hipError_t launch_count(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                        int32_t* slot, int64_t* n_invalid, hipStream_t stream) {
   const int64_t LE = L * (int64_t)E;
-  int32_t* slot = ring + (step % W) * LE;
   hipError_t err = launch_hist_clear(slot, LE, n_invalid, L, stream);
   if (err != hipSuccess) return err;
 
@@ -156,9 +173,27 @@ hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
     const int64_t blocks = L * sp.chunks;
     hist_count_kernel<<<(unsigned)blocks, kStreamThreads, lds, stream>>>(idx, sp, E, copies, slot, n_invalid);
     err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
+  return err;
+}
+
+hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                       int32_t* ring, int32_t W, int64_t step, int64_t* load,
+                       int64_t* n_invalid, hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  const int64_t LE = L * (int64_t)E;
+  hipError_t err = launch_count(idx, L, T, K, E, ring + (step % W) * LE, n_invalid, stream);
+  if (err != hipSuccess) return err;
   return launch_window_sum(ring, LE, W, load, stream);
+}
+
+hipError_t launch_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                           int32_t* cnt, int32_t shift, int64_t* ema, int64_t* n_invalid,
+                           hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  hipError_t err = launch_count(idx, L, T, K, E, cnt, n_invalid, stream);
+  if (err != hipSuccess) return err;
+  return launch_ema_update(cnt, L * (int64_t)E, shift, ema, stream);
 }
 
 }  // namespace eplb

@@ -38,6 +38,8 @@ def lib():
     lib.eplb_rebalance.argtypes = [p, i64, i32, i32, i32, i32, i32, i32, p, p, p, p, p]
     lib.eplb_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, p, p]
     lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
+    lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
+    lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
@@ -47,7 +49,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
-                          "eplb_rebalance_lds_bytes"}
+                          "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
+                          "eplb_placement_load"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -140,6 +143,23 @@ def test_stream_validation(lib):
         args[pos] = bad
         assert hr(*args) == code, (pos, bad)
     assert ok
+
+
+def test_ema_and_quality_validation(lib):
+    good = [FAKE, 2, 10, 8, 256, FAKE, 4, FAKE, FAKE, None]
+    for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (6, -1, 1),
+                           (6, 63, 1), (0, None, 1), (5, None, 1), (7, None, 1), (8, None, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_load_ema(*args) == code, (pos, bad)
+    assert lib.eplb_load_ema(None, 0, 10, 8, 256, None, 62, None, None, None) == 0   # L = 0: nothing to do
+    good = [FAKE, FAKE, FAKE, 58, 256, 288, 32, FAKE, FAKE, None]
+    for pos, bad, code in [(3, -1, 1), (3, 1 << 31, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (6, 5, 2),
+                           (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_placement_load(*args) == code, (pos, bad)
+    assert lib.eplb_placement_load(None, None, None, 0, 256, 288, 32, None, None, None) == 0
 
 
 def test_fastdiv_magic_numbers():
