@@ -6,8 +6,10 @@ One step = one pass of the whole path over one step of routing ids:
                      288 physical on 4 nodes x 8 ranks, hierarchical policy)
     eplb_redirect   (every (token, k) of the step -> a physical replica)
 Also reported: the serving-loop step (eplb_hist_redirect, which reads the ids
-once, then the rebalance for the next step) and the rebalance latency of the
-global-policy decode shape and of the 1024-problem skewed batch.
+once, then the rebalance for the next step), the moving-average estimator
+(eplb_load_ema), the per-rank load and max/mean of the placement
+(eplb_placement_load), and the rebalance latency of the global-policy decode
+shape and of the 1024-problem skewed batch.
 on the streaming workload: 58 MoE layers x 2^20 tokens x top-8 int32 ids per
 step (1.95 GB), Zipf(1.1) expert popularity, a 10-step window.  Ten distinct
 steps are generated on the device up front and cycled; inputs are resident
@@ -149,6 +151,30 @@ def main() -> int:
     serve_wall = time.perf_counter() - t0
     fused_ms = [e[0].elapsed_time(e[1]) for e in sevs]
 
+    # the moving-average estimator instead of the window (count + EMA update),
+    # and the per-rank load / imbalance of the placement in force
+    ema = torch.zeros((L, E), dtype=torch.int64, device=dev)
+    count = torch.empty((L, E), dtype=torch.int32, device=dev)
+    for s_ in range(3):
+        eplb.load_ema(steps[s_ % W], E, ema, 4, count, n_invalid)
+    eevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        eevs[i][0].record(stream)
+        eplb.load_ema(steps[i % W], E, ema, 4, count, n_invalid)
+        eevs[i][1].record(stream)
+    rank_load = torch.empty((L, pl.RK), dtype=torch.float64, device=dev)
+    imbalance = torch.empty((L,), dtype=torch.float64, device=dev)
+    eplb.placement_load(load, phy2log, logcnt, pl.RK, out=(rank_load, imbalance))
+    qevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
+    for e in qevs:
+        e[0].record(stream)
+        eplb.placement_load(load, phy2log, logcnt, pl.RK, out=(rank_load, imbalance))
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ema_ms = [e[0].elapsed_time(e[1]) for e in eevs]
+    quality_us = [e[0].elapsed_time(e[1]) * 1e3 for e in qevs]
+    imb = imbalance.cpu()
+
     # the other two rebalance shapes: 58-layer global policy, 1024 problems
     def reb_device_us(ld, P, G, N, RK):
         Xo = eplb.max_count(ld.shape[1], P, G, N)
@@ -230,6 +256,18 @@ def main() -> int:
             "fused_GBps": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9, 1),
             "fused_frac_of_peak": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_step": redir_bytes,
+        },
+        "load_ema": {
+            "what": "eplb_load_ema (count the step, ema <- ema - (ema >> 4) + count)",
+            "ms": round(avg(ema_ms), 4),
+            "GBps": round(hist_bytes / (avg(ema_ms) * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(hist_bytes / (avg(ema_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "placement_quality": {
+            "what": "eplb_placement_load: per-rank load and max/mean of the placement in force, 58 problems",
+            "device_us_median": round(statistics.median(quality_us), 2),
+            "imbalance_mean": round(float(imb.mean()), 4),
+            "imbalance_max": round(float(imb.max()), 4),
         },
         "rebalance_other_device_us_median": other,
         "rebalance_58_layers": {
