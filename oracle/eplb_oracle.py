@@ -400,3 +400,105 @@ def placement_load(load, phy2log, logcnt, RK: int):
         ranks.append(r)
         imb.append(Fraction(1) if mean == 0 else max(r) / mean)
     return ranks, imb
+
+
+# --------------------------------------------------------------------------
+# Rearrangement plan: from the placement in force to a new one
+# --------------------------------------------------------------------------
+
+STATUS_BAD_MAP = 18
+
+
+def rearrange_plan(old_phy2log, new_phy2log, new_log2phy, RK: int, N: int) -> dict:
+    """Which expert weights to copy where when a new placement replaces the
+    one in force, keeping in place every replica that can stay.
+
+    The pages stop at the placement: the rebalance assigns replicas to GPUs
+    ([EPLB-ru], opening section and "Алгоритм") and says nothing of moving
+    weights.  This plan takes the plainest route.  Positions within a rank
+    (GPU) are interchangeable, so the new placement is kept rank for rank and
+    only permuted inside each rank:
+
+    * rank r holds slots [r*ppr, (r+1)*ppr), ppr = P / RK;
+    * for each expert e, the first m old slots of the rank holding e stay
+      (kept), m = min(copies of e in the old rank, copies in the new rank),
+      matched in order to the first m new slots of the rank holding e;
+    * the other new slots of the rank, in ascending order, take the other old
+      slots of the rank (the freed ones), in ascending order;
+    * a freed slot then fetches its new expert from an old slot holding it:
+      one on the same rank if any (kept, so never overwritten), else one on
+      the same node (node of slot s = s // (P / N)), else any; the lowest
+      slot in that class.  Every source refers to the OLD placement.
+
+    The number of fetches, ppr minus the multiset overlap per rank, is the
+    least any within-rank permutation of the new placement allows.
+
+    Returns int32 arrays: phy2log [B][P] (the new placement, permuted within
+    ranks), log2phy [B][E][X] (the new log2phy through the same permutation,
+    replica order kept), src [B][P] (old slot to copy from, -1 when the slot is
+    kept), moves [B][3] (fetches from the same rank, the same node, another
+    node), status [B] (STATUS_OK, or STATUS_BAD_MAP when an old or new entry
+    lies outside [0, E), a log2phy entry outside [-1, P), or a new expert has
+    no old replica; all outputs of such a problem are -1).
+    """
+    old_phy2log = np.asarray(old_phy2log)
+    new_phy2log = np.asarray(new_phy2log)
+    new_log2phy = np.asarray(new_log2phy)
+    B, P = new_phy2log.shape
+    E, X = new_log2phy.shape[1], new_log2phy.shape[2]
+    ppr = P // RK
+    per_node = P // N
+    out = {"phy2log": np.full((B, P), -1, dtype=np.int32),
+           "log2phy": np.full((B, E, X), -1, dtype=np.int32),
+           "src": np.full((B, P), -1, dtype=np.int32),
+           "moves": np.full((B, 3), -1, dtype=np.int32),
+           "status": np.zeros(B, dtype=np.int32)}
+    for b in range(B):
+        old = [int(x) for x in old_phy2log[b].tolist()]
+        new = [int(x) for x in new_phy2log[b].tolist()]
+        l2p = [[int(x) for x in row] for row in new_log2phy[b].tolist()]
+        if (any(not (0 <= e < E) for e in old + new) or any(not (-1 <= s < P) for row in l2p for s in row)
+                or not set(new) <= set(old)):
+            out["status"][b] = STATUS_BAD_MAP
+            continue
+        perm = [None] * P                       # new slot -> slot in the plan
+        kept = [False] * P                      # old slot stays as it is
+        for r in range(RK):
+            slots = range(r * ppr, (r + 1) * ppr)
+            used_old = set()
+            matched_new = set()
+            for e in sorted(set(new[s] for s in slots)):
+                old_e = [s for s in slots if old[s] == e]
+                new_e = [s for s in slots if new[s] == e]
+                for q, p in zip(old_e, new_e):
+                    perm[p] = q
+                    kept[q] = True
+                    used_old.add(q)
+                    matched_new.add(p)
+            freed = [s for s in slots if s not in used_old]
+            waiting = [s for s in slots if s not in matched_new]
+            for q, p in zip(freed, waiting):
+                perm[p] = q
+        plan = [None] * P
+        for p in range(P):
+            plan[perm[p]] = new[p]
+        src = [-1] * P
+        moves = [0, 0, 0]
+        for s in range(P):
+            if kept[s]:
+                continue
+            holders = [q for q in range(P) if old[q] == plan[s]]
+            same_rank = [q for q in holders if q // ppr == s // ppr]
+            same_node = [q for q in holders if q // per_node == s // per_node]
+            if same_rank:
+                src[s], cls = same_rank[0], 0
+            elif same_node:
+                src[s], cls = same_node[0], 1
+            else:
+                src[s], cls = holders[0], 2
+            moves[cls] += 1
+        out["phy2log"][b] = plan
+        out["log2phy"][b] = [[perm[s] if s >= 0 else -1 for s in row] for row in l2p]
+        out["src"][b] = src
+        out["moves"][b] = moves
+    return out

@@ -432,8 +432,148 @@ def pin_placement_load(o):
     assert imb[0] == 1
 
 
+def _valid_l2p(new, E, X):
+    """log2phy of a placement: slots of each expert in ascending order."""
+    B, P = new.shape
+    l2p = np.full((B, E, X), -1, dtype=np.int64)
+    for b in range(B):
+        seen = [0] * E
+        for s in range(P):
+            e = int(new[b, s])
+            l2p[b, e, seen[e]] = s
+            seen[e] += 1
+    return l2p
+
+
+def pin_rearrange_hand(o):
+    """Two cases worked by hand.  (a) P=6, 2 ranks of 3, 2 nodes:
+    old [0 1 2 | 3 4 0], new [2 0 0 | 4 1 3].  Rank 0 keeps 0 (slot 0, matched
+    to new slot 1) and 2 (slot 2, new slot 0); the second 0 (new slot 2) goes
+    to the freed slot 1 and is copied from slot 0 on the same rank.  Rank 1
+    keeps 4 and 3; expert 1 goes to slot 5, copied from slot 1 on the other
+    node.  (b) old [0 1 2 | 3 4 1], new [3 4 0 | 1 2 0]: two freed slots per
+    rank, filled in ascending order (rank 0: 3 then 4 into slots 1, 2)."""
+    r = o.rearrange_plan(np.array([[0, 1, 2, 3, 4, 0]]), np.array([[2, 0, 0, 4, 1, 3]]),
+                         np.array([[[1, 2], [4, -1], [0, -1], [5, -1], [3, -1]]]), 2, 2)
+    assert r["status"].tolist() == [0]
+    assert r["phy2log"].tolist() == [[0, 0, 2, 3, 4, 1]]
+    assert r["src"].tolist() == [[-1, 0, -1, -1, -1, 1]]
+    assert r["moves"].tolist() == [[1, 0, 1]]
+    assert r["log2phy"].tolist() == [[[0, 1], [5, -1], [2, -1], [3, -1], [4, -1]]]
+    old, new = np.array([[0, 1, 2, 3, 4, 1]]), np.array([[3, 4, 0, 1, 2, 0]])
+    l2p = np.array([[[2, 5], [3, -1], [4, -1], [0, -1], [1, -1]]])
+    for N, moves in ((1, [0, 4, 0]), (2, [0, 0, 4])):
+        r = o.rearrange_plan(old, new, l2p, 2, N)
+        assert r["phy2log"].tolist() == [[0, 3, 4, 2, 0, 1]]
+        assert r["src"].tolist() == [[-1, 3, 4, 2, 0, -1]]
+        assert r["moves"].tolist() == [moves]
+        assert r["log2phy"].tolist() == [[[0, 4], [5, -1], [3, -1], [1, -1], [2, -1]]]
+
+
+def pin_rearrange_identity_and_permutation(o):
+    """A placement against itself moves nothing; against a shuffle of its
+    slots within each rank it moves nothing and the plan is the old one."""
+    w, r = _example(o)
+    p2l, l2p = r["phy2log"], r["log2phy"]
+    q = o.rearrange_plan(p2l, p2l, l2p, 8, 2)
+    assert (q["phy2log"] == p2l).all() and (q["log2phy"] == l2p).all()
+    assert (q["src"] == -1).all() and (q["moves"] == 0).all() and (q["status"] == 0).all()
+    rng = np.random.default_rng(4)
+    shuf = p2l.copy()
+    for b in range(2):
+        for g in range(8):
+            shuf[b, 2 * g:2 * g + 2] = rng.permutation(shuf[b, 2 * g:2 * g + 2])
+    q = o.rearrange_plan(p2l, shuf, _valid_l2p(shuf, 12, 3), 8, 2)
+    assert (q["phy2log"] == p2l).all() and (q["moves"] == 0).all() and (q["src"] == -1).all()
+
+
+def _check_plan(o, old, new, RK, N, q):
+    """Properties any correct plan has, each checked by brute force."""
+    import itertools
+    B, P = new.shape
+    E = q["log2phy"].shape[1]
+    ppr, per_node = P // RK, P // N
+    for b in range(B):
+        plan = q["phy2log"][b]
+        for r in range(RK):
+            sl = slice(r * ppr, (r + 1) * ppr)
+            assert sorted(plan[sl].tolist()) == sorted(new[b, sl].tolist())      # within-rank permutation
+        for e in range(E):
+            got = sorted(x for x in q["log2phy"][b, e].tolist() if x >= 0)
+            assert got == [s for s in range(P) if plan[s] == e]
+        fetch = [0, 0, 0]
+        for s in range(P):
+            if q["src"][b, s] < 0:
+                assert plan[s] == old[b, s]
+                continue
+            src = int(q["src"][b, s])
+            holders = [x for x in range(P) if old[b, x] == plan[s]]
+            assert src in holders
+            classes = [[x for x in holders if x // ppr == s // ppr],
+                       [x for x in holders if x // per_node == s // per_node], holders]
+            cls = next(i for i, c in enumerate(classes) if c)
+            assert src == min(classes[cls])
+            fetch[cls] += 1
+            if cls == 0:
+                assert q["src"][b, src] == -1          # a same-rank source is kept, never overwritten
+        assert q["moves"][b].tolist() == fetch
+        # fewest fetches: ppr minus the multiset overlap of each rank
+        from collections import Counter
+        least = sum(ppr - sum((Counter(old[b, r * ppr:(r + 1) * ppr].tolist())
+                               & Counter(new[b, r * ppr:(r + 1) * ppr].tolist())).values()) for r in range(RK))
+        assert sum(fetch) == least
+        if ppr <= 3 and RK <= 3:                       # and no within-rank permutation does better
+            best = min(sum(int(a != c) for a, c in zip(sum((list(x) for x in combo), []), old[b].tolist()))
+                       for combo in itertools.product(*[itertools.permutations(new[b, r * ppr:(r + 1) * ppr].tolist())
+                                                       for r in range(RK)]))
+            assert best == sum(fetch)
+
+
+def pin_rearrange_properties(o):
+    """Random old/new placements (every new expert present in the old one):
+    within-rank permutation, consistent log2phy, sources hold the expert and
+    are the lowest of the nearest class, fewest fetches (closed form, and
+    brute force over all within-rank permutations on tiny cases)."""
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        RK = int(rng.integers(1, 4)) if trial < 25 else int(rng.integers(2, 9))
+        ppr = int(rng.integers(1, 4)) if trial < 25 else int(rng.integers(1, 7))
+        N = int(rng.choice([d for d in range(1, RK + 1) if RK % d == 0]))
+        P = RK * ppr
+        E = int(rng.integers(1, P + 1))
+        B = 3
+        old = np.stack([rng.permutation(np.concatenate([np.arange(E), rng.integers(0, E, P - E)]))
+                        for _ in range(B)])
+        new = np.stack([rng.permutation(np.concatenate([np.arange(E), rng.integers(0, E, P - E)]))
+                        for _ in range(B)])
+        X = max(int(np.bincount(new[b], minlength=E).max()) for b in range(B))
+        q = o.rearrange_plan(old, new, _valid_l2p(new, E, X), RK, N)
+        assert (q["status"] == 0).all()
+        _check_plan(o, old, new, RK, N, q)
+
+
+def pin_rearrange_bad_maps(o):
+    """Entries outside their ranges, or a new expert with no old replica:
+    status 18 and every output of that problem -1; other problems unaffected."""
+    old = np.array([[0, 1, 2, 3]] * 5)
+    new = np.array([[1, 0, 3, 2]] * 5)
+    l2p = _valid_l2p(new, 4, 1)
+    old[1, 2] = 4
+    new[2, 0] = -1
+    l2p[3, 0, 0] = 4
+    new[4, 0] = 1
+    old[4, 1] = 0                                      # expert 1 no longer in the old placement
+    q = o.rearrange_plan(old, new, l2p, 2, 1)
+    assert q["status"].tolist() == [0, 18, 18, 18, 18]
+    for k in ("phy2log", "log2phy", "src", "moves"):
+        assert (q[k][1:] == -1).all()
+    assert q["phy2log"][0].tolist() == [0, 1, 2, 3] and (q["src"][0] == -1).all()
+
+
 ALL_PINS = [pin_golden_phy2log, pin_golden_layer0, pin_golden_gpu_loads, pin_dsv3_shape,
             pin_replication_bruteforce, pin_replication_dhondt, pin_packing_closed_forms,
             pin_identity_cases, pin_degenerate_loads, pin_exact_arithmetic, pin_invariants_random,
             pin_status_rules,
-            pin_hist_bruteforce, pin_window, pin_redirect, pin_ema, pin_placement_load]
+            pin_hist_bruteforce, pin_window, pin_redirect, pin_ema, pin_placement_load,
+            pin_rearrange_hand, pin_rearrange_identity_and_permutation, pin_rearrange_properties,
+            pin_rearrange_bad_maps]

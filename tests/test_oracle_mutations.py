@@ -42,6 +42,14 @@ MUTANTS = {
     "redirect_by_k": ("t = np.arange(T, dtype=np.int64)[:, None]", "t = np.arange(K, dtype=np.int64)[None, :]"),
     "ema_rounds_up": ("out = [e - (e >> shift) + c for e, c in zip(ema, cnt)]",
                       "out = [e - (-(-e >> shift)) + c for e, c in zip(ema, cnt)]"),
+    "rearrange_freed_descending": ("freed = [s for s in slots if s not in used_old]",
+                                   "freed = [s for s in reversed(slots) if s not in used_old]"),
+    "rearrange_keeps_one_less": ("for q, p in zip(old_e, new_e):", "for q, p in zip(old_e[1:], new_e[1:]):"),
+    "rearrange_node_before_rank": ("if same_rank:\n                src[s], cls = same_rank[0], 0",
+                                   "if same_rank and not same_node:\n                src[s], cls = same_rank[0], 0"),
+    "rearrange_highest_source": ("src[s], cls = holders[0], 2", "src[s], cls = holders[-1], 2"),
+    "rearrange_node_of_rank": ("same_node = [q for q in holders if q // per_node == s // per_node]",
+                               "same_node = [q for q in holders if q // ppr // N == s // ppr // N]"),
     "rank_load_ignores_count": ("r = [sum((Fraction(w[phy[g * ppr + s]], c[phy[g * ppr + s]])",
                                 "r = [sum((Fraction(w[phy[g * ppr + s]], 1)"),
 }
