@@ -6,7 +6,8 @@
  * loads into a replica placement (phy2log / log2phy / logcnt), and the
  * redirect of routed logical ids to physical replicas.  Around them: the
  * histogram and redirect fused in one pass, a moving-average load estimate,
- * and the per-rank load of a placement (its max / mean).
+ * the per-rank load of a placement (its max / mean), and the plan of weight
+ * copies that turns one placement into the next.
  *
  * What each call computes is defined by the EPLB README and its annotated
  * source on the translation page «DualPipe и EPLB: конвейер в обе стороны и
@@ -51,6 +52,8 @@ extern "C" {
 #define EPLB_S_BAD_LOAD   16  /* some load < 0 or > 2^40; outputs set to -1        */
 #define EPLB_S_OVERFLOW   17  /* lcm(replica counts of a node) * (node load sum)
                                  >= 2^127; outputs set to -1                       */
+#define EPLB_S_BAD_MAP    18  /* eplb_rearrange: an entry outside its range, or a
+                                 new expert with no old replica; outputs -1        */
 
 /*
  * eplb_load_hist -- expert load of one step, and the load over a window.
@@ -209,6 +212,53 @@ int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
 int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
                             int64_t B, int32_t E, int32_t P, int32_t RK,
                             double* rank_load, double* imbalance, void* stream);
+
+/*
+ * eplb_rearrange -- which expert weights to copy where when a new placement
+ * replaces the one in force, keeping every replica that can stay.
+ *
+ * Follows: the pages stop at the placement (the rebalance assigns replicas
+ * to GPUs: opening section and "Алгоритм" of Part 2) and say nothing of
+ * moving weights; this is the plain completion.  The new placement stays
+ * rank for rank and is permuted only within each rank (positions inside a
+ * GPU are interchangeable):
+ *   - rank r holds slots [r*ppr, (r+1)*ppr), ppr = P / RK;
+ *   - for each expert e, the first m old slots of the rank holding e are
+ *     kept, m = min(copies of e on the rank before, after), matched in order
+ *     to the first m new slots holding e;
+ *   - the other new slots of the rank, ascending, take the rank's other old
+ *     slots, ascending;
+ *   - a slot that changes copies its expert from an old slot holding it: on
+ *     the same rank if there is one (always a kept slot), else on the same
+ *     node (slot s is on node s / (P/N)), else anywhere; the lowest slot of
+ *     that class.  Sources refer to the OLD placement: a copy out of a slot
+ *     that also changes must read it before it is overwritten.
+ * The number of copies, per rank ppr minus the overlap of the two multisets,
+ * is the least any within-rank permutation of the new placement needs.
+ *
+ *   old_phy2log  [B][P] int32    the placement in force
+ *   new_phy2log  [B][P] int32    the new placement (from eplb_rebalance)
+ *   new_log2phy  [B][E][X] int32 its log2phy (-1 padded); entries are mapped
+ *                                through the same permutation, replica
+ *                                order kept (not checked against phy2log)
+ *   B, E, P, RK, N, X            problems, logical experts, physical experts,
+ *                                ranks, nodes (RK % N == 0), log2phy width
+ *   phy2log      [B][P] int32    out: the new placement, permuted in ranks
+ *   log2phy      [B][E][X] int32 out: its log2phy
+ *   src          [B][P] int32    out: old slot to copy slot p from; -1 kept
+ *   moves        [B][3] int32    out: copies from the same rank, the same
+ *                                node, another node
+ *   status       [B] int32       out: EPLB_S_OK or EPLB_S_BAD_MAP
+ * Outputs must not overlap the inputs.
+ *
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output equal to an
+ * input), EPLB_E_DIV (P % RK, RK % N), EPLB_E_LIMIT (E > 4096, P > 8192,
+ * X > 65535), EPLB_E_HIP.
+ */
+int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, const int32_t* new_log2phy,
+                       int64_t B, int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X,
+                       int32_t* phy2log, int32_t* log2phy, int32_t* src, int32_t* moves, int32_t* status,
+                       void* stream);
 
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);

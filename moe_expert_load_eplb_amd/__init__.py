@@ -29,9 +29,11 @@ EPLB_E_HIP = 7
 EPLB_S_OK = 0
 EPLB_S_BAD_LOAD = 16
 EPLB_S_OVERFLOW = 17
+EPLB_S_BAD_MAP = 18
 
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
-           "eplb_load_ema", "eplb_placement_load", "eplb_status_string", "eplb_rebalance_lds_bytes")
+           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_status_string",
+           "eplb_rebalance_lds_bytes")
 
 
 def _load() -> ctypes.CDLL:
@@ -56,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_load_ema.restype = i32
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
     lib.eplb_placement_load.restype = i32
+    lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
+    lib.eplb_rearrange.restype = i32
     lib.eplb_status_string.argtypes = [i32]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -266,3 +270,39 @@ def placement_load(load: torch.Tensor, phy2log: torch.Tensor, logcnt: torch.Tens
                                  _dev(imbalance, torch.float64, "imbalance"), _stream(dev))
     _check(rc, "eplb_placement_load")
     return rank_load, imbalance
+
+
+def rearrange(old_phy2log: torch.Tensor, new_phy2log: torch.Tensor, new_log2phy: torch.Tensor, RK: int, N: int,
+              out: tuple | None = None):
+    """Plan of weight copies from the placement in force to a new one.
+
+    old_phy2log, new_phy2log [B, P] int32; new_log2phy [B, E, X] int32.
+    Returns (phy2log [B, P], log2phy [B, E, X], src [B, P], moves [B, 3],
+    status [B]), all int32: the new placement permuted within ranks so that
+    every replica that can stay does, and for each changed slot the old slot
+    to copy from (-1 where nothing moves).
+    """
+    if old_phy2log.dim() != 2 or new_phy2log.dim() != 2 or new_log2phy.dim() != 3:
+        raise ValueError("old_phy2log [B, P], new_phy2log [B, P], new_log2phy [B, E, X] expected")
+    B, P = new_phy2log.shape
+    _, E, X = new_log2phy.shape
+    if tuple(old_phy2log.shape) != (B, P) or new_log2phy.shape[0] != B:
+        raise ValueError("the three maps must describe the same B problems and P slots")
+    dev = new_phy2log.device
+    if out is None:
+        out = (torch.empty((B, P), dtype=torch.int32, device=dev),
+               torch.empty((B, E, X), dtype=torch.int32, device=dev),
+               torch.empty((B, P), dtype=torch.int32, device=dev),
+               torch.empty((B, 3), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    phy2log, log2phy, src, moves, status = out
+    if (tuple(phy2log.shape) != (B, P) or tuple(log2phy.shape) != (B, E, X) or tuple(src.shape) != (B, P)
+            or tuple(moves.shape) != (B, 3) or tuple(status.shape) != (B,)):
+        raise ValueError("output shapes must be [B, P], [B, E, X], [B, P], [B, 3], [B]")
+    rc = lib.eplb_rearrange(_dev(old_phy2log, torch.int32, "old_phy2log"), _dev(new_phy2log, torch.int32, "new_phy2log"),
+                            _dev(new_log2phy, torch.int32, "new_log2phy"), B, E, P, int(RK), int(N), X,
+                            _dev(phy2log, torch.int32, "phy2log"), _dev(log2phy, torch.int32, "log2phy"),
+                            _dev(src, torch.int32, "src"), _dev(moves, torch.int32, "moves"),
+                            _dev(status, torch.int32, "status"), _stream(dev))
+    _check(rc, "eplb_rearrange")
+    return phy2log, log2phy, src, moves, status

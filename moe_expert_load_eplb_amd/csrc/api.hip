@@ -100,6 +100,29 @@ int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const i
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, const int32_t* new_log2phy,
+                       int64_t B, int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X,
+                       int32_t* phy2log, int32_t* log2phy, int32_t* src, int32_t* moves, int32_t* status,
+                       void* stream) {
+  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || P < 1 || RK < 1 || N < 1 || X < 1) return EPLB_E_ARG;
+  if (P % RK != 0 || RK % N != 0) return EPLB_E_DIV;
+  if (E > kMaxE || P > kMaxP || X > kMaxX) return EPLB_E_LIMIT;
+  if (B > 0) {
+    const void* in[3] = {old_phy2log, new_phy2log, new_log2phy};
+    const void* out[5] = {phy2log, log2phy, src, moves, status};
+    for (const void* a : in)
+      if (a == nullptr) return EPLB_E_ARG;
+    for (const void* a : out) {
+      if (a == nullptr) return EPLB_E_ARG;
+      for (const void* c : in)
+        if (a == c) return EPLB_E_ARG;
+    }
+  }
+  hipError_t err = launch_rearrange(old_phy2log, new_phy2log, new_log2phy, B, E, P, RK, N, X, phy2log, log2phy,
+                                    src, moves, status, (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);
@@ -119,6 +142,7 @@ const char* eplb_status_string(int32_t code) {
     case EPLB_E_HIP: return "HIP launch failed";
     case EPLB_S_BAD_LOAD: return "problem status: a load is negative or above 2^40";
     case EPLB_S_OVERFLOW: return "problem status: exact pack sums need 127 bits or more";
+    case EPLB_S_BAD_MAP: return "problem status: a map entry is out of range or an expert has no old replica";
     default: return "unknown code";
   }
 }

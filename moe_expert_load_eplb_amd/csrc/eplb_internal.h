@@ -15,6 +15,8 @@ constexpr int kMaxLdsBytes = 64 * 1024;          // per-workgroup LDS budget
 constexpr int kMaxE = 4096;                      // per-expert LDS tables
 constexpr int kMaxX = 65535;                     // log2phy width
 constexpr int kMaxCount = 16128;                 // replica count bound (< 131^2)
+constexpr int kMaxP = 8192;                      // physical experts per problem
+constexpr int32_t kStatusBadMap = 18;            // rearrangement: an entry out of range
 
 // ---------------------------------------------------------------- helpers
 // Magic numbers for floor(n / d) with 0 <= n < 2^31 and 1 <= d < 2^31
@@ -142,6 +144,11 @@ hipError_t launch_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
 hipError_t launch_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
                                  int64_t B, int32_t E, int32_t P, int32_t RK, double* rank_load,
                                  double* imbalance, hipStream_t stream);
+hipError_t launch_rearrange(const int32_t* old_p2l, const int32_t* new_p2l, const int32_t* new_l2p, int64_t B,
+                            int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X, int32_t* plan,
+                            int32_t* l2p_out, int32_t* src, int32_t* moves, int32_t* status,
+                            hipStream_t stream);
+int64_t rearrange_lds_bytes(int32_t E, int32_t P);
 hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
 hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
 hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,

@@ -40,6 +40,7 @@ def lib():
     lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
     lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
+    lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
@@ -50,7 +51,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
-                          "eplb_placement_load"}
+                          "eplb_placement_load", "eplb_rearrange"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -59,6 +60,7 @@ def test_codes_match_binding_and_oracle():
     c = header_constants()
     assert c["EPLB_OK"] == 0 and len({v for k, v in c.items() if k.startswith("EPLB_E_")}) == 7
     assert c["EPLB_S_BAD_LOAD"] == ora.STATUS_BAD_LOAD and c["EPLB_S_OVERFLOW"] == ora.STATUS_OVERFLOW
+    assert c["EPLB_S_BAD_MAP"] == ora.STATUS_BAD_MAP
     src = open(os.path.join(ROOT, "moe_expert_load_eplb_amd", "__init__.py")).read()
     for k, v in c.items():
         if k.startswith("EPLB_"):
@@ -178,3 +180,18 @@ def test_fastdiv_magic_numbers():
         ns += [int(x) for x in rng.integers(0, top, 4)]
         for n in ns:
             assert ((n * m) >> 32) >> (l - 1) == n // d, (d, n)
+
+
+def test_rearrange_validation(lib):
+    F = [FAKE + 64 * i for i in range(8)]
+    good = [F[0], F[1], F[2], 58, 256, 288, 32, 4, 9, F[3], F[4], F[5], F[6], F[7], None]
+    for pos, bad, code in [(3, -1, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (7, 0, 1), (8, 0, 1),
+                           (6, 5, 2), (7, 5, 2), (4, 4097, 5), (5, 8192 * 2, 5), (8, 70000, 5),
+                           (0, None, 1), (1, None, 1), (2, None, 1), (9, None, 1), (13, None, 1),
+                           (9, F[1], 1), (10, F[2], 1), (12, F[0], 1)]:
+        args = list(good)
+        args[pos] = bad
+        if pos == 5 and bad == 8192 * 2:
+            args[6] = 32                                # keep P % RK == 0
+        assert lib.eplb_rearrange(*args) == code, (pos, bad)
+    assert lib.eplb_rearrange(None, None, None, 0, 256, 288, 32, 4, 9, None, None, None, None, None, None) == 0
