@@ -8,7 +8,8 @@ One step = one pass of the whole path over one step of routing ids:
 Also reported: the serving-loop step (eplb_hist_redirect, which reads the ids
 once, then the rebalance for the next step), the moving-average estimator
 (eplb_load_ema), the per-rank load and max/mean of the placement
-(eplb_placement_load), and the rebalance latency of the global-policy decode
+(eplb_placement_load), the plan of weight copies between two placements
+(eplb_rearrange), and the rebalance latency of the global-policy decode
 shape and of the 1024-problem skewed batch.
 on the streaming workload: 58 MoE layers x 2^20 tokens x top-8 int32 ids per
 step (1.95 GB), Zipf(1.1) expert popularity, a 10-step window.  Ten distinct
@@ -170,8 +171,21 @@ def main() -> int:
         e[0].record(stream)
         eplb.placement_load(load, phy2log, logcnt, pl.RK, out=(rank_load, imbalance))
         e[1].record(stream)
+    # the plan of weight copies from the placement in force to the next one:
+    # the placement of the window before the timed steps vs the current one
+    prev = [t.clone() for t in placement]
+    eplb.rebalance(ema, pl.P, pl.G, pl.N, pl.RK, X, out=prev)
+    plan = eplb.rearrange(prev[0], phy2log, log2phy, pl.RK, pl.N)
+    revs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(50)]
+    for e in revs:
+        e[0].record(stream)
+        eplb.rearrange(prev[0], phy2log, log2phy, pl.RK, pl.N, out=plan)
+        e[1].record(stream)
     torch.cuda.synchronize()
     ema_ms = [e[0].elapsed_time(e[1]) for e in eevs]
+    rearrange_us = [e[0].elapsed_time(e[1]) * 1e3 for e in revs]
+    moves = plan[3].sum(dim=0).cpu().tolist()
+    assert int(plan[4].abs().sum()) == 0
     quality_us = [e[0].elapsed_time(e[1]) * 1e3 for e in qevs]
     imb = imbalance.cpu()
 
@@ -268,6 +282,12 @@ def main() -> int:
             "device_us_median": round(statistics.median(quality_us), 2),
             "imbalance_mean": round(float(imb.mean()), 4),
             "imbalance_max": round(float(imb.max()), 4),
+        },
+        "rearrange": {
+            "what": "eplb_rearrange: copy plan from the placement of the moving-average loads to the window's, 58 problems",
+            "device_us_median": round(statistics.median(rearrange_us), 2),
+            "copies_same_rank_node_other": moves,
+            "slots": L * pl.P,
         },
         "rebalance_other_device_us_median": other,
         "rebalance_58_layers": {

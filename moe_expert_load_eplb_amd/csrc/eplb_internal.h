@@ -148,7 +148,7 @@ hipError_t launch_rearrange(const int32_t* old_p2l, const int32_t* new_p2l, cons
                             int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X, int32_t* plan,
                             int32_t* l2p_out, int32_t* src, int32_t* moves, int32_t* status,
                             hipStream_t stream);
-int64_t rearrange_lds_bytes(int32_t E, int32_t P);
+int64_t rearrange_lds_bytes(int32_t E, int32_t P, int32_t N);
 hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
 hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
 hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
