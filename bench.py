@@ -307,11 +307,124 @@ def main() -> int:
         },
     }
 
+    result["other_workloads"] = small_workloads(eplb, wl, dev, stream)
+    result["serving_graph"] = graph_serving(eplb, wl, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, work, steps[(nwarm + args.steps - 1) % W], load,
                                               placement, hist_bytes + redir_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def small_workloads(eplb, wl, dev, stream):
+    """Device time per call of the histogram, redirect and fused pass on the
+    two smaller routing workloads (inputs of 30 MB and 3.8 MB sit in the
+    on-chip caches, so these calls are launch- and latency-bound: context,
+    not the HBM figure)."""
+    import torch
+    out = {}
+    for work in (wl.DSV3_PREFILL, wl.GLOBAL_DECODE):
+        pl = work.placement
+        E, W = pl.E, work.window
+        idx = torch.from_numpy(wl.routing_step(work, 0)).to(dev)
+        ring = torch.zeros((W, work.layers, E), dtype=torch.int32, device=dev)
+        load, bad = eplb.load_hist(idx, E, ring, 0)
+        placement = eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK)
+        red = eplb.redirect(idx, placement[1], placement[2])
+        calls = {
+            "hist": lambda: eplb.load_hist(idx, E, ring, 0, load, bad),
+            "redirect": lambda: eplb.redirect(idx, placement[1], placement[2], out=red),
+            "hist_redirect": lambda: eplb.hist_redirect(idx, E, ring, 0, placement[1], placement[2], load, bad, red),
+            "rebalance": lambda: eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, out=placement),
+        }
+        rec = {"ids": int(idx.numel())}
+        for name, fn in calls.items():
+            ts = []
+            for _ in range(30):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            rec[f"{name}_us"] = round(statistics.median(ts[5:]), 2)
+        out[work.name] = rec
+    return out
+
+
+def graph_serving(eplb, wl, dev, steps=64):
+    """Serving steps on the two smaller routing workloads, launched eagerly
+    and as replays of HIP graphs captured once per ring slot: the fused
+    statistics + redirect pass alone, and followed by the rebalance that
+    overwrites the placement in force.  Host clock over `steps` steps."""
+    import torch
+    out = {}
+    for work in (wl.DSV3_PREFILL, wl.GLOBAL_DECODE):
+        pl = work.placement
+        L, E, W = work.layers, pl.E, work.window
+        idx = torch.from_numpy(wl.routing_step(work, 0)).to(dev)
+        ring = torch.zeros((W, L, E), dtype=torch.int32, device=dev)
+        load = torch.zeros((L, E), dtype=torch.int64, device=dev)
+        bad = torch.zeros((L,), dtype=torch.int64, device=dev)
+        red = torch.empty_like(idx)
+        placement = eplb.rebalance(torch.ones((L, E), dtype=torch.int64, device=dev), pl.P, pl.G, pl.N, pl.RK)
+
+        def stats(s):
+            eplb.hist_redirect(idx, E, ring, s, placement[1], placement[2], load, bad, red)
+
+        def full(s):
+            stats(s)
+            eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, out=placement)
+
+        rec = {"ids_per_step": int(idx.numel())}
+        for name, fn in (("stats_redirect", stats), ("stats_redirect_rebalance", full)):
+            for s_ in range(W):
+                fn(s_)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s_ in range(steps):
+                fn(s_)
+            torch.cuda.synchronize()
+            eager = (time.perf_counter() - t0) / steps
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            graphs = []
+            for slot in range(W):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    fn(slot)
+                graphs.append(g)
+            for s_ in range(W):
+                graphs[s_ % W].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s_ in range(steps):
+                graphs[s_ % W].replay()
+            torch.cuda.synchronize()
+            graph = (time.perf_counter() - t0) / steps
+            rec[name] = {"eager_us": round(eager * 1e6, 1), "graph_us": round(graph * 1e6, 1)}
+            del graphs
+        out[work.name] = rec
+    return out
+
+
+_MP = {}
+
+
+def _mp_layer(l):
+    from oracle import eplb_oracle as ora
+    idx, E, l2p, cnt = _MP["idx"], _MP["E"], _MP["log2phy"], _MP["logcnt"]
+    ora.load_hist(idx[l:l + 1], E)
+    ora.redirect(idx[l:l + 1], l2p[l:l + 1], cnt[l:l + 1])
+    return l
+
+
+def _mp_rebalance(rows):
+    from oracle import eplb_oracle as ora
+    pl, X = _MP["pl"], _MP["X"]
+    ora.rebalance(_MP["load"][rows], pl.P, pl.G, pl.N, pl.RK, X)
+    return len(rows)
 
 
 def cpu_baseline(args, work, idx_dev, load_dev, placement, step_bytes):
@@ -337,6 +450,21 @@ def cpu_baseline(args, work, idx_dev, load_dev, placement, step_bytes):
     t3 = time.perf_counter()
     per_layer = ((t1 - t0) + (t3 - t2)) / nl
     step_s = per_layer * work.layers + (t2 - t1)
+
+    # the same oracle functions over a pool of forked workers, one layer (or
+    # one slice of rebalance problems) per task; the workers touch no GPU
+    import multiprocessing
+    nw = max(1, min(16, len(os.sched_getaffinity(0)), nl))
+    _MP.update(idx=idx_h, E=pl.E, log2phy=ref["log2phy"], logcnt=ref["logcnt"], load=load_h, pl=pl, X=X)
+    with multiprocessing.get_context("fork").Pool(nw) as pool:
+        pool.map(_mp_layer, range(min(nw, nl)))                       # warm the workers
+        m0 = time.perf_counter()
+        pool.map(_mp_layer, range(nl), chunksize=1)
+        m1 = time.perf_counter()
+        pool.map(_mp_rebalance, [list(range(i, work.layers, nw)) for i in range(nw)], chunksize=1)
+        m2 = time.perf_counter()
+    _MP.clear()
+    step_mc = (m1 - m0) * work.layers / nl + (m2 - m1)
     return {
         "value": round(step_bytes / step_s / 1e9, 3),
         "unit": "GB/s",
@@ -347,6 +475,13 @@ def cpu_baseline(args, work, idx_dev, load_dev, placement, step_bytes):
                    f"exact-rational rebalance; {step_s:.2f} s per step"),
         "rebalance_58_layers_s": round(t2 - t1, 3),
         "cpu": _cpu_model(),
+        "multicore": {
+            "value": round(step_bytes / step_mc / 1e9, 3),
+            "unit": "GB/s",
+            "cores": nw,
+            "sample": (f"the same oracle calls on a pool of {nw} forked workers: the {nl} layers one per task "
+                       f"(scaled to {work.layers}), the rebalance split over the workers; {step_mc:.2f} s per step"),
+        },
     }
 
 

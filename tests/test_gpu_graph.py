@@ -1,0 +1,96 @@
+"""The serving step captured in HIP graphs and replayed (needs an MI355X).
+
+The library allocates nothing and never synchronises, so its calls can be
+recorded in a graph.  One graph per ring slot holds a serving step: count
+step s into slot s % W and redirect it with the placement in force
+(eplb_hist_redirect), then the rebalance that overwrites that placement for
+the next step.  Every replay, with fresh ids copied into the captured input
+buffer by ordinary eager work in between, must give outputs identical to the
+same calls made eagerly on separate buffers, and to the oracle.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import eplb_oracle as ora
+
+pytestmark = pytest.mark.gpu
+
+eplb = pytest.importorskip("moe_expert_load_eplb_amd")
+DEV = torch.device("cuda:0")
+
+
+def note(msg: str) -> None:
+    print(f"[graph] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+class Loop:
+    """Buffers of one serving loop (the placement is updated in place)."""
+
+    def __init__(self, work, tokens, W):
+        pl = work.placement
+        L, K, E = work.layers, work.topk, pl.E
+        self.E, self.pl, self.W = E, pl, W
+        self.idx = torch.zeros((L, tokens, K), dtype=torch.int32, device=DEV)
+        self.ring = torch.zeros((W, L, E), dtype=torch.int32, device=DEV)
+        self.load = torch.zeros((L, E), dtype=torch.int64, device=DEV)
+        self.bad = torch.zeros((L,), dtype=torch.int64, device=DEV)
+        self.out = torch.zeros_like(self.idx)
+        X = pl.max_count
+        # the placement in force before the first step: every expert once, in order, on a uniform load
+        self.placement = eplb.rebalance(torch.ones((L, E), dtype=torch.int64, device=DEV), pl.P, pl.G, pl.N, pl.RK, X)
+
+    def step(self, s):
+        pl = self.pl
+        eplb.hist_redirect(self.idx, self.E, self.ring, s, self.placement[1], self.placement[2],
+                           self.load, self.bad, self.out)
+        eplb.rebalance(self.load, pl.P, pl.G, pl.N, pl.RK, out=self.placement)
+
+    def state(self):
+        return [t.cpu().numpy().copy() for t in (self.out, self.load, self.bad, *self.placement)]
+
+
+@pytest.mark.parametrize("work,tokens,W", [(wl.TINY_HIER, 4096, 3), (wl.DSV3_PREFILL, 2000, 4)],
+                         ids=["tiny", "dsv3"])
+def test_graph_replay_matches_eager(work, tokens, W):
+    graph_loop = Loop(work, tokens, W)
+    eager_loop = Loop(work, tokens, W)
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    graphs = []
+    for slot in range(W):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            graph_loop.step(slot)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # capture records the calls without running them: both loops start alike
+
+    hists = []
+    prev = [t.cpu().numpy().copy() for t in eager_loop.placement]
+    for s in range(2 * W + 3):
+        note(f"{work.name} step {s} (slot {s % W})")
+        idx_h = wl.routing_step(work, s, tokens=tokens)
+        graph_loop.idx.copy_(torch.from_numpy(idx_h))
+        eager_loop.idx.copy_(torch.from_numpy(idx_h))
+        graphs[s % W].replay()
+        eager_loop.step(s)
+        torch.cuda.synchronize()
+        g, e = graph_loop.state(), eager_loop.state()
+        for name, a, b in zip(("out", "load", "n_invalid", "phy2log", "log2phy", "logcnt", "status"), g, e):
+            assert np.array_equal(a, b), f"step {s}: {name} differs between graph replay and eager"
+        # and both against the oracle: redirect with the placement in force, window, new placement
+        cnt, inv = ora.load_hist(idx_h, work.placement.E)
+        hists.append(cnt)
+        assert np.array_equal(g[0], ora.redirect(idx_h, prev[1], prev[2]))
+        assert np.array_equal(g[1], ora.window_load(hists, W))
+        ref = ora.rebalance(g[1], work.placement.P, work.placement.G, work.placement.N, work.placement.RK,
+                            work.placement.max_count)
+        assert np.array_equal(g[3], ref["phy2log"]) and np.array_equal(g[5], ref["logcnt"])
+        prev = g[3:]
