@@ -437,3 +437,36 @@ def test_fused_full_size():
     for l in (0, 31, 57):
         assert_same(f"redirect layer {l}", out_h[l:l + 1],
                     ora.redirect(idx_h[l:l + 1], ref["log2phy"][l:l + 1], ref["logcnt"][l:l + 1]))
+
+
+@pytest.mark.parametrize("T,K", [(2048, 8), (70000, 5)], ids=["one-workgroup-per-layer", "several-per-layer"])
+def test_slot_and_invalid_overwritten(T, K):
+    """The slot of this step, n_invalid and the count buffer of the moving
+    average are written whatever they held before the call."""
+    rng = np.random.default_rng(T)
+    L, E, W = 3, 40, 4
+    idx_h = rng.integers(-2, E + 2, size=(L, T, K)).astype(np.int32)
+    for fused in (False, True):
+        note(f"slot overwrite T={T} K={K} fused={fused}")
+        ring = torch.full((W, L, E), 7, dtype=torch.int32, device=DEV)
+        load = torch.full((L, E), -5, dtype=torch.int64, device=DEV)
+        bad = torch.full((L,), 123, dtype=torch.int64, device=DEV)
+        if fused:
+            l2p = torch.zeros((L, E, 1), dtype=torch.int32, device=DEV)
+            cnt1 = torch.ones((L, E), dtype=torch.int32, device=DEV)
+            eplb.hist_redirect(gpu(idx_h), E, ring, 6, l2p, cnt1, load, bad)
+        else:
+            eplb.load_hist(gpu(idx_h), E, ring, 6, load, bad)
+        torch.cuda.synchronize()
+        cnt, invl = ora.load_hist(idx_h, E)
+        assert_same("slot", host(ring[2]).astype(np.int64), cnt)
+        assert_same("invalid", host(bad), invl)
+        assert_same("window", host(load), cnt + 7 * (W - 1))
+    ema = torch.full((L, E), 1000, dtype=torch.int64, device=DEV)
+    count = torch.full((L, E), 9, dtype=torch.int32, device=DEV)
+    bad = torch.full((L,), 123, dtype=torch.int64, device=DEV)
+    eplb.load_ema(gpu(idx_h), E, ema, 2, count, bad)
+    torch.cuda.synchronize()
+    assert_same("ema count", host(count).astype(np.int64), cnt)
+    assert_same("ema invalid", host(bad), invl)
+    assert_same("ema", host(ema), ora.ema_update(np.full((L, E), 1000), cnt, 2).reshape(L, E))
