@@ -22,6 +22,15 @@ section name:
   the pages' order: groups -> nodes, replicas within a node, replicas -> GPUs.
 * ``redirect`` -- each routed (token, k) goes to one physical replica of its
   logical expert; replica ``t mod logcnt`` of token row t.
+* ``ema_update`` -- an integer exponential moving average of the per-step
+  counts, the other reading of the opening section's "moving average".
+* ``placement_load`` -- per-GPU load of a placement and its max / mean
+  ([EPLB-ru], the translator's hands-on exercise 2 and the worked example).
+* ``rearrange_plan`` -- the weight copies that turn one placement into the
+  next; the pages are silent, so this follows a stated plain rule.
+* ``lp_solve`` / ``lp_redirect`` -- LPLB-style per-batch redistribution of
+  tokens over replica edges, and the redirect by its flows (the two LPLB
+  pages; exact integer reading stated in ``lp_solve``).
 
 Arithmetic: every value is an exact Python integer or ``fractions.Fraction``.
 The pages compute replica loads and pack sums in float32; this oracle uses
@@ -501,4 +510,210 @@ def rearrange_plan(old_phy2log, new_phy2log, new_log2phy, RK: int, N: int) -> di
         out["log2phy"][b] = [[perm[s] if s >= 0 else -1 for s in row] for row in l2p]
         out["src"][b] = src
         out["moves"][b] = moves
+    return out
+
+
+# --------------------------------------------------------------------------
+# Per-batch redistribution over a fixed replica topology (LPLB-style)
+# --------------------------------------------------------------------------
+
+STATUS_BAD_TOPOLOGY = 19
+
+
+def _lp_graph(cnt, home, rep, RK):
+    """Rank loads before any move, and the capacity between ranks: a replica
+    on rank g of expert x (home rank o) is an edge o -> g that can carry up
+    to cnt[x] of x's tokens."""
+    base = [0] * RK
+    for e, c in enumerate(cnt):
+        base[home[e]] += c
+    cap = [[0] * RK for _ in range(RK)]
+    for g in range(RK):
+        for x in rep[g]:
+            if x >= 0 and home[x] != g:
+                cap[home[x]][g] += cnt[x]
+    return base, cap
+
+
+def _lp_network(base, cap, lam):
+    """Residual capacities of the feasibility network for a bound lam:
+    source -> r carries what r must shed (base - lam), r -> sink what r may
+    still take (lam - base), and the rank edges their capacities."""
+    RK = len(base)
+    V = RK + 2
+    s, t = RK, RK + 1
+    r = [[0] * V for _ in range(V)]
+    for v in range(RK):
+        r[s][v] = max(0, base[v] - lam)
+        r[v][t] = max(0, lam - base[v])
+        for g in range(RK):
+            if g != v:
+                r[v][g] = cap[v][g]
+    return r, s, t
+
+
+def _max_flow(r, s, t):
+    """Shortest augmenting paths (Edmonds and Karp, J. ACM 1972) on the
+    residual matrix r, in place.  The search goes level by level from the
+    source; a node's predecessor is the lowest-numbered node of the previous
+    level with residual capacity to it, so the paths, and the flow, are one
+    definite choice among the optimal ones.  Returns the flow value."""
+    V = len(r)
+    total = 0
+    while True:
+        parent = [-1] * V
+        seen = [False] * V
+        seen[s] = True
+        frontier = [s]
+        while frontier and not seen[t]:
+            nxt = []
+            for v in range(V):
+                if seen[v]:
+                    continue
+                for u in frontier:                          # ascending
+                    if r[u][v] > 0:
+                        parent[v] = u
+                        nxt.append(v)
+                        break
+            for v in nxt:
+                seen[v] = True
+            frontier = nxt
+        if not seen[t]:
+            return total
+        b = None
+        v = t
+        while v != s:
+            u = parent[v]
+            b = r[u][v] if b is None else min(b, r[u][v])
+            v = u
+        v = t
+        while v != s:
+            u = parent[v]
+            r[u][v] -= b
+            r[v][u] += b
+            v = u
+        total += b
+
+
+def lp_solve(cnt, home, rep, RK: int) -> dict:
+    """Per-batch token redistribution over replica edges, exact.
+
+    Two pages describe LPLB: «DeepSeek开源LPLB：基于线性规划的MoE负载均衡器…»
+    (2048ai.net; items 4, 5 and 7: the replica topology r2o, the LP model and
+    the typical topologies) and the Machine Heart report on LPLB
+    (wwwcj777.com; section «LPLB 的工作原理»).  Each redundant expert links
+    the GPU of its original to its own GPU; that edge can carry at most the
+    tokens routed to the expert in the current batch; a linear program moves
+    tokens along the edges to make the loads of the expert-parallel group as
+    even as possible.  The pages do not write the program out; this reading
+    minimises the largest rank load with whole tokens:
+
+        minimise  lam  over integer flows 0 <= f[g][j] <= cnt[rep[g][j]]
+        subject to  base[r] - (flows out of r) + (flows into r) <= lam
+
+    where base[r] sums the batch counts of the experts whose original lives
+    on rank r (home), and slot j of rank g holds a replica of rep[g][j]
+    (-1: empty).  lam is the least integer for which a feasible flow exists
+    (binary search, each bound tested by a maximum flow); the flows are those
+    of the shortest-augmenting-path maximum flow at that lam, split over the
+    replica slots of each rank pair in ascending slot order.
+
+    cnt [B][E] int64 (0 .. 2^40), home [B][E] int32 in [0, RK), rep [B][RK][R]
+    int32 (-1 or an expert id; an expert has at most one replica).
+    Returns lam [B] int64, flow [B][RK][R] int64, rank_load [B][RK] int64,
+    status [B] (STATUS_OK, or STATUS_BAD_TOPOLOGY for an id or count out of
+    range or an expert replicated twice; outputs -1).
+    """
+    cnt = np.asarray(cnt)
+    home = np.asarray(home)
+    rep = np.asarray(rep)
+    B, E = cnt.shape
+    R = rep.shape[2]
+    out = {"lam": np.full(B, -1, dtype=np.int64), "flow": np.full((B, RK, R), -1, dtype=np.int64),
+           "rank_load": np.full((B, RK), -1, dtype=np.int64), "status": np.zeros(B, dtype=np.int32)}
+    for b in range(B):
+        c = [int(x) for x in cnt[b].tolist()]
+        h = [int(x) for x in home[b].tolist()]
+        rp = [[int(x) for x in row] for row in rep[b].tolist()]
+        reps = [x for row in rp for x in row if x != -1]
+        if (any(x < 0 or x > LOAD_MAX for x in c) or any(not (0 <= x < RK) for x in h)
+                or any(not (0 <= x < E) for x in reps) or len(set(reps)) != len(reps)):
+            out["status"][b] = STATUS_BAD_TOPOLOGY
+            continue
+        base, cap = _lp_graph(c, h, rp, RK)
+
+        def feasible(lam):
+            r, s, t = _lp_network(base, cap, lam)
+            need = sum(r[s])
+            return _max_flow(r, s, t) == need
+
+        lo, hi = 0, max(base)                   # hi: no move needed
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if feasible(mid):
+                hi = mid
+            else:
+                lo = mid + 1
+        lam = lo
+        r, s, t = _lp_network(base, cap, lam)
+        _max_flow(r, s, t)
+        # net flow on each rank pair, split over that pair's replica slots
+        flow = [[0] * R for _ in range(RK)]
+        load = list(base)
+        for o in range(RK):
+            for g in range(RK):
+                if o == g:
+                    continue
+                net = max(0, cap[o][g] - r[o][g])
+                for j in range(R):
+                    x = rp[g][j]
+                    if x >= 0 and h[x] == o and net > 0:
+                        f = min(net, c[x])
+                        flow[g][j] = f
+                        net -= f
+                        load[o] -= f
+                        load[g] += f
+        out["lam"][b] = lam
+        out["flow"][b] = flow
+        out["rank_load"][b] = load
+    return out
+
+
+def lp_redirect(idx, rep, flow, E: int) -> np.ndarray:
+    """Physical expert of every routed (token, k) under the batch's flows.
+
+    Physical ids: expert e's original is e; slot j of rank g is E + g*R + j
+    (the LPLB planner of the usage example on «DeepSeek开源LPLB…» counts
+    the logical experts plus the redundant ones per rank times the ranks).  The occurrences of expert x in a layer,
+    counted in (token, k) order, are numbered 0, 1, ...; the first f of them
+    go to x's replica, f being that replica's flow, the rest stay with the
+    original.  Ids outside [0, E) give -1.
+    """
+    idx = np.asarray(idx)
+    rep = np.asarray(rep)
+    flow = np.asarray(flow)
+    L = idx.shape[0]
+    RK, R = rep.shape[1], rep.shape[2]
+    out = np.empty(idx.shape, dtype=np.int32)
+    for l in range(L):
+        slot = np.full(E, -1, dtype=np.int64)
+        fx = np.zeros(E, dtype=np.int64)
+        for g in range(RK):
+            for j in range(R):
+                x = int(rep[l, g, j])
+                if x >= 0:
+                    slot[x] = E + g * R + j
+                    fx[x] = int(flow[l, g, j])
+        flat = idx[l].ravel().astype(np.int64)
+        valid = (flat >= 0) & (flat < E)
+        key = np.where(valid, flat, E)
+        order = np.argsort(key, kind="stable")           # positions grouped by expert, in order
+        sk = key[order]
+        first = np.searchsorted(sk, sk, side="left")
+        occ = np.empty_like(flat)
+        occ[order] = np.arange(flat.size) - first
+        e = np.where(valid, flat, 0)
+        to_rep = valid & (slot[e] >= 0) & (occ < fx[e])
+        res = np.where(to_rep, slot[e], flat)
+        out[l] = np.where(valid, res, -1).reshape(idx.shape[1:])
     return out

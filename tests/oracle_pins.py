@@ -570,10 +570,203 @@ def pin_rearrange_bad_maps(o):
     assert q["phy2log"][0].tolist() == [0, 1, 2, 3] and (q["src"][0] == -1).all()
 
 
+def _lp_random(rng, RK, R, E, B=1, top=50, fill=0.7):
+    """A random topology: home ranks, and replica slots filled with distinct
+    experts (not on their own home rank, mostly)."""
+    cnt = rng.integers(0, top, size=(B, E)).astype(np.int64)
+    home = rng.integers(0, RK, size=(B, E)).astype(np.int64)
+    rep = np.full((B, RK, R), -1, dtype=np.int64)
+    for b in range(B):
+        pool = list(rng.permutation(E))
+        for g in range(RK):
+            for j in range(R):
+                if pool and rng.random() < fill:
+                    rep[b, g, j] = pool.pop()
+    return cnt, home, rep
+
+
+def _lp_loads(cnt, home, rep, flow, RK):
+    load = np.zeros(RK, dtype=np.int64)
+    for e, c in enumerate(cnt):
+        load[home[e]] += c
+    for g in range(RK):
+        for j in range(rep.shape[1]):
+            x = rep[g, j]
+            if x >= 0:
+                load[home[x]] -= flow[g, j]
+                load[g] += flow[g, j]
+    return load
+
+
+def pin_lp_closed_forms(o):
+    """No replica: the largest home load.  Zero counts: 0.  Two ranks joined
+    by one replica of rank 0's expert: ceil((a + b) / 2) when a >= b, else b.
+    A capacity too small to balance: base minus the capacity.  Already even
+    loads: no flow."""
+    cnt = np.array([[5, 9, 1, 7]])
+    home = np.array([[0, 1, 1, 2]])
+    r = o.lp_solve(cnt, home, np.full((1, 3, 2), -1), 3)
+    assert r["lam"].tolist() == [10] and (r["flow"] == 0).all() and r["rank_load"].tolist() == [[5, 10, 7]]
+    r = o.lp_solve(np.zeros((1, 4), dtype=np.int64), home, np.array([[[1, -1], [0, -1], [2, -1]]]), 3)
+    assert r["lam"].tolist() == [0] and (r["flow"] == 0).all()
+    for a, b in ((10, 2), (11, 2), (3, 3), (2, 10), (0, 0), (1, 0), (7, 6)):
+        r = o.lp_solve(np.array([[a, b]]), np.array([[0, 1]]), np.array([[[-1], [0]]]), 2)
+        want = -(-(a + b) // 2) if a >= b else b
+        assert r["lam"].tolist() == [want], (a, b, r["lam"])
+        assert r["rank_load"].max() == want
+    r = o.lp_solve(np.array([[10, 90, 0]]), np.array([[0, 0, 1]]), np.array([[[-1], [0]]]), 2)
+    assert r["lam"].tolist() == [90] and r["flow"][0, 1, 0] == 10
+    cnt = np.full((1, 8), 4)
+    home = np.array([[0, 0, 1, 1, 2, 2, 3, 3]])
+    rep = np.array([[[2, 5], [4, 7], [6, 1], [0, 3]]])
+    r = o.lp_solve(cnt, home, rep, 4)
+    assert r["lam"].tolist() == [8] and (r["flow"] == 0).all()
+
+
+def pin_lp_subset_bound(o):
+    """The optimum equals the supply-demand bound (Gale, 1957): the largest,
+    over nonempty sets S of ranks, of ceil((load of S - capacity leaving S)
+    / |S|) -- computed here by enumerating every S."""
+    import itertools
+    rng = np.random.default_rng(31)
+    for trial in range(60):
+        RK = int(rng.integers(1, 7))
+        R = int(rng.integers(1, 4))
+        E = int(rng.integers(RK, 4 * RK + 2))
+        cnt, home, rep = _lp_random(rng, RK, R, E, top=int(rng.choice([3, 50, 10**6])))
+        r = o.lp_solve(cnt, home, rep, RK)
+        base = np.zeros(RK, dtype=np.int64)
+        np.add.at(base, home[0], cnt[0])
+        best = 0
+        for k in range(1, RK + 1):
+            for S in itertools.combinations(range(RK), k):
+                S = set(S)
+                out_cap = sum(int(cnt[0, x]) for g in range(RK) if g not in S for x in rep[0, g]
+                              if x >= 0 and home[0, x] in S)
+                v = sum(int(base[i]) for i in S) - out_cap
+                best = max(best, -(-v // k))
+        assert r["lam"][0] == best, (trial, r["lam"][0], best)
+
+
+def pin_lp_linprog(o):
+    """The same linear program in real numbers (scipy's HiGHS): its optimum
+    lies within one token below the integer optimum."""
+    from scipy.optimize import linprog
+    rng = np.random.default_rng(32)
+    for trial in range(30):
+        RK = int(rng.integers(2, 9))
+        R = int(rng.integers(1, 3))
+        E = 4 * RK
+        cnt, home, rep = _lp_random(rng, RK, R, E, top=1000)
+        r = o.lp_solve(cnt, home, rep, RK)
+        edges = [(int(home[0, x]), g, int(cnt[0, x])) for g in range(RK) for x in rep[0, g] if x >= 0]
+        base = np.zeros(RK)
+        np.add.at(base, home[0], cnt[0])
+        n = len(edges)
+        c = np.zeros(n + 1)
+        c[-1] = 1.0
+        A = np.zeros((RK, n + 1))
+        for i, (src, dst, _) in enumerate(edges):
+            A[src, i] -= 1.0
+            A[dst, i] += 1.0
+        A[:, -1] = -1.0
+        bounds = [(0, cap) for _, _, cap in edges] + [(0, None)]
+        res = linprog(c, A_ub=A, b_ub=-base, bounds=bounds, method="highs")
+        assert res.status == 0
+        lam_f = res.fun
+        assert lam_f - 1e-6 <= r["lam"][0] < lam_f + 1 + 1e-6, (trial, lam_f, r["lam"][0])
+
+
+def pin_lp_bruteforce(o):
+    """Tiny cases: every integer flow tried; the least largest load matches,
+    and the returned flows reach it within their capacities."""
+    import itertools
+    rng = np.random.default_rng(33)
+    for trial in range(40):
+        RK = int(rng.integers(2, 4))
+        cnt, home, rep = _lp_random(rng, RK, 1, RK + 2, top=6, fill=0.8)
+        r = o.lp_solve(cnt, home, rep, RK)
+        slots = [(g, j) for g in range(RK) for j in range(1) if rep[0, g, j] >= 0]
+        best = None
+        for fl in itertools.product(*[range(int(cnt[0, rep[0, g, j]]) + 1) for g, j in slots]):
+            flow = np.zeros((RK, 1), dtype=np.int64)
+            for (g, j), f in zip(slots, fl):
+                flow[g, j] = f
+            m = int(_lp_loads(cnt[0], home[0], rep[0], flow, RK).max())
+            best = m if best is None else min(best, m)
+        assert r["lam"][0] == best
+
+
+def pin_lp_flows_valid(o):
+    """Flows between 0 and the replicated expert's count (0 on empty slots),
+    loads recomputed from them equal the returned ones, and the largest is
+    the optimum; several replicas per rank pair share the pair's flow."""
+    rng = np.random.default_rng(34)
+    for trial in range(40):
+        RK = int(rng.integers(2, 9))
+        R = int(rng.integers(1, 5))
+        cnt, home, rep = _lp_random(rng, RK, R, 6 * RK, B=2, top=int(rng.choice([5, 1000])), fill=0.9)
+        r = o.lp_solve(cnt, home, rep, RK)
+        for b in range(2):
+            f = r["flow"][b]
+            assert (f >= 0).all() and (f[rep[b] < 0] == 0).all()
+            assert all(f[g, j] <= cnt[b, rep[b, g, j]] for g in range(RK) for j in range(R) if rep[b, g, j] >= 0)
+            load = _lp_loads(cnt[b], home[b], rep[b], f, RK)
+            assert load.tolist() == r["rank_load"][b].tolist()
+            assert load.max() == r["lam"][b] and load.sum() == cnt[b].sum()
+
+
+def pin_lp_redirect(o):
+    """Against a plain loop: occurrences of an expert counted in (token, k)
+    order, the first f to the replica; exactly min(f, count) ids move."""
+    rng = np.random.default_rng(35)
+    E, RK, R = 12, 3, 2
+    rep = np.array([[[4, -1], [0, 7], [-1, 11]], [[-1, -1], [3, -1], [5, 2]]])
+    flow = np.array([[[3, 0], [5, 0], [0, 100]], [[0, 0], [1, 0], [0, 2]]])
+    idx = rng.integers(-1, E + 1, size=(2, 50, 3)).astype(np.int32)
+    got = o.lp_redirect(idx, rep, flow, E)
+    for l in range(2):
+        seen = {}
+        slot = {int(rep[l, g, j]): (g, j) for g in range(RK) for j in range(R) if rep[l, g, j] >= 0}
+        for t in range(50):
+            for k in range(3):
+                e = int(idx[l, t, k])
+                if not (0 <= e < E):
+                    assert got[l, t, k] == -1
+                    continue
+                i = seen.get(e, 0)
+                seen[e] = i + 1
+                if e in slot and i < flow[l][slot[e]]:
+                    assert got[l, t, k] == E + slot[e][0] * R + slot[e][1]
+                else:
+                    assert got[l, t, k] == e
+        for x, (g, j) in slot.items():
+            moved = int((got[l] == E + g * R + j).sum())
+            assert moved == min(int(flow[l, g, j]), int((idx[l] == x).sum()))
+
+
+def pin_lp_status(o):
+    """An id, home or count out of range, or an expert with two replicas:
+    status 19 and every output -1; other problems unaffected."""
+    cnt = np.array([[5, 1, 2, 0]] * 6)
+    home = np.array([[0, 1, 1, 0]] * 6)
+    rep = np.array([[[1, -1], [0, -1]]] * 6)
+    cnt[1, 2] = -1
+    cnt[2, 2] = (1 << 40) + 1
+    home[3, 0] = 2
+    rep[4, 0, 1] = 4
+    rep[5, 0, 1] = 0                                    # expert 0 twice
+    r = o.lp_solve(cnt, home, rep, 2)
+    assert r["status"].tolist() == [0, 19, 19, 19, 19, 19]
+    assert (r["lam"][1:] == -1).all() and (r["flow"][1:] == -1).all() and (r["rank_load"][1:] == -1).all()
+    assert r["lam"][0] == 4
+
+
 ALL_PINS = [pin_golden_phy2log, pin_golden_layer0, pin_golden_gpu_loads, pin_dsv3_shape,
             pin_replication_bruteforce, pin_replication_dhondt, pin_packing_closed_forms,
             pin_identity_cases, pin_degenerate_loads, pin_exact_arithmetic, pin_invariants_random,
             pin_status_rules,
             pin_hist_bruteforce, pin_window, pin_redirect, pin_ema, pin_placement_load,
             pin_rearrange_hand, pin_rearrange_identity_and_permutation, pin_rearrange_properties,
-            pin_rearrange_bad_maps]
+            pin_rearrange_bad_maps, pin_lp_closed_forms, pin_lp_subset_bound, pin_lp_linprog, pin_lp_bruteforce,
+            pin_lp_flows_valid, pin_lp_redirect, pin_lp_status]

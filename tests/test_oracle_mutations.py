@@ -50,6 +50,13 @@ MUTANTS = {
     "rearrange_highest_source": ("src[s], cls = holders[0], 2", "src[s], cls = holders[-1], 2"),
     "rearrange_node_of_rank": ("same_node = [q for q in holders if q // per_node == s // per_node]",
                                "same_node = [q for q in holders if q // ppr // N == s // ppr // N]"),
+    "lp_capacity_is_one": ("cap[home[x]][g] += cnt[x]", "cap[home[x]][g] += 1"),
+    "lp_edge_reversed": ("cap[home[x]][g] += cnt[x]", "cap[g][home[x]] += cnt[x]"),
+    "lp_search_upper_off": ("lo, hi = 0, max(base)", "lo, hi = 0, max(base) - 1"),
+    "lp_split_ignores_count": ("f = min(net, c[x])", "f = net"),
+    "lp_sink_room_too_big": ("r[v][t] = max(0, lam - base[v])", "r[v][t] = max(0, lam - base[v] + 1)"),
+    "lp_redirect_keeps_first": ("to_rep = valid & (slot[e] >= 0) & (occ < fx[e])",
+                                "to_rep = valid & (slot[e] >= 0) & (occ >= fx[e])"),
     "rank_load_ignores_count": ("r = [sum((Fraction(w[phy[g * ppr + s]], c[phy[g * ppr + s]])",
                                 "r = [sum((Fraction(w[phy[g * ppr + s]], 1)"),
 }
