@@ -6,8 +6,9 @@
  * loads into a replica placement (phy2log / log2phy / logcnt), and the
  * redirect of routed logical ids to physical replicas.  Around them: the
  * histogram and redirect fused in one pass, a moving-average load estimate,
- * the per-rank load of a placement (its max / mean), and the plan of weight
- * copies that turns one placement into the next.
+ * the per-rank load of a placement (its max / mean), the plan of weight
+ * copies that turns one placement into the next, and an LPLB-style
+ * per-batch redistribution of tokens over replica edges.
  *
  * What each call computes is defined by the EPLB README and its annotated
  * source on the translation page «DualPipe и EPLB: конвейер в обе стороны и
@@ -54,6 +55,8 @@ extern "C" {
                                  >= 2^127; outputs set to -1                       */
 #define EPLB_S_BAD_MAP    18  /* eplb_rearrange: an entry outside its range, or a
                                  new expert with no old replica; outputs -1        */
+#define EPLB_S_BAD_TOPOLOGY 19 /* eplb_lp_solve: an id, home rank or count out of
+                                 range, or an expert replicated twice; outputs -1  */
 
 /*
  * eplb_load_hist -- expert load of one step, and the load over a window.
@@ -259,6 +262,45 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
                        int64_t B, int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X,
                        int32_t* phy2log, int32_t* log2phy, int32_t* src, int32_t* moves, int32_t* status,
                        void* stream);
+
+/*
+ * eplb_lp_solve -- per-batch redistribution of tokens over a fixed replica
+ * topology (LPLB-style), exact in integers.
+ *
+ * Follows: the two LPLB pages, «DeepSeek开源LPLB：基于线性规划的MoE负载均衡器…»
+ * (2048ai.net; items 4, 5 and 7: replica topology, LP model, topologies) and
+ * the Machine Heart report on LPLB (wwwcj777.com, «LPLB 的工作原理»): each
+ * redundant expert is an edge from its original's rank to its own rank that
+ * can carry up to the expert's tokens of the batch; tokens move along the
+ * edges to even out the ranks.  The pages leave the program unwritten; here:
+ *     minimise lam over integer flows 0 <= flow[g][j] <= cnt[rep[g][j]]
+ *     subject to, for every rank r,
+ *       base[r] - (flows of r's experts to other ranks) + (flows into r) <= lam
+ * with base[r] = sum of cnt[e] over the experts e with home[e] == r.
+ * lam is unique; the flows are the ones a shortest-augmenting-path maximum
+ * flow (lowest-numbered predecessor at each level) finds at lam, with each
+ * rank pair's net flow split over the pair's slots in ascending slot order.
+ *
+ *   cnt        [B][E] int64      tokens routed to each logical expert in the
+ *                                batch, 0 .. 2^40
+ *   home       [B][E] int32      rank holding each expert's original
+ *   rep        [B][RK][R] int32  expert replicated in slot j of rank g, or -1;
+ *                                an expert has at most one replica (a replica
+ *                                on its own home rank carries nothing)
+ *   B, E, RK, R                  problems, experts, ranks (1 .. 16), slots
+ *                                per rank (1 .. 64)
+ *   lam        [B] int64         out: the least reachable largest rank load
+ *   flow       [B][RK][R] int64  out: tokens slot (g, j) takes from the
+ *                                original of rep[g][j] (0 for empty slots)
+ *   rank_load  [B][RK] int64     out: rank loads after the moves (max = lam)
+ *   status     [B] int32         out: EPLB_S_OK or EPLB_S_BAD_TOPOLOGY
+ *
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array), EPLB_E_LIMIT
+ * (E > 4096, RK > 16, R > 64), EPLB_E_HIP.
+ */
+int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
+                      int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,
+                      void* stream);
 
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);

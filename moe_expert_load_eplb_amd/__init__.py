@@ -30,9 +30,10 @@ EPLB_S_OK = 0
 EPLB_S_BAD_LOAD = 16
 EPLB_S_OVERFLOW = 17
 EPLB_S_BAD_MAP = 18
+EPLB_S_BAD_TOPOLOGY = 19
 
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
-           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_status_string",
+           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_status_string",
            "eplb_rebalance_lds_bytes")
 
 
@@ -60,6 +61,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_placement_load.restype = i32
     lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
     lib.eplb_rearrange.restype = i32
+    lib.eplb_lp_solve.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p]
+    lib.eplb_lp_solve.restype = i32
     lib.eplb_status_string.argtypes = [i32]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -306,3 +309,35 @@ def rearrange(old_phy2log: torch.Tensor, new_phy2log: torch.Tensor, new_log2phy:
                             _dev(status, torch.int32, "status"), _stream(dev))
     _check(rc, "eplb_rearrange")
     return phy2log, log2phy, src, moves, status
+
+
+def lp_solve(cnt: torch.Tensor, home: torch.Tensor, rep: torch.Tensor, out: tuple | None = None):
+    """Per-batch redistribution of tokens over replica edges.
+
+    cnt [B, E] int64 (tokens per expert in the batch), home [B, E] int32
+    (rank of each expert's original), rep [B, RK, R] int32 (expert in each
+    replica slot, or -1).  Returns (lam [B] int64, flow [B, RK, R] int64,
+    rank_load [B, RK] int64, status [B] int32).
+    """
+    if cnt.dim() != 2 or home.dim() != 2 or rep.dim() != 3:
+        raise ValueError("cnt [B, E], home [B, E], rep [B, RK, R] expected")
+    B, E = cnt.shape
+    _, RK, R = rep.shape
+    if tuple(home.shape) != (B, E) or rep.shape[0] != B:
+        raise ValueError("cnt, home and rep must describe the same B problems")
+    dev = cnt.device
+    if out is None:
+        out = (torch.empty((B,), dtype=torch.int64, device=dev),
+               torch.empty((B, RK, R), dtype=torch.int64, device=dev),
+               torch.empty((B, RK), dtype=torch.int64, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    lam, flow, rank_load, status = out
+    if (tuple(lam.shape) != (B,) or tuple(flow.shape) != (B, RK, R) or tuple(rank_load.shape) != (B, RK)
+            or tuple(status.shape) != (B,)):
+        raise ValueError("output shapes must be [B], [B, RK, R], [B, RK], [B]")
+    rc = lib.eplb_lp_solve(_dev(cnt, torch.int64, "cnt"), _dev(home, torch.int32, "home"),
+                           _dev(rep, torch.int32, "rep"), B, E, RK, R, _dev(lam, torch.int64, "lam"),
+                           _dev(flow, torch.int64, "flow"), _dev(rank_load, torch.int64, "rank_load"),
+                           _dev(status, torch.int32, "status"), _stream(dev))
+    _check(rc, "eplb_lp_solve")
+    return lam, flow, rank_load, status

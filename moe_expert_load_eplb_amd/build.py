@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libeplb.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip", "fused.hip", "quality.hip", "rearrange.hip"]
+SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip", "fused.hip", "quality.hip", "rearrange.hip", "lp.hip"]
 
 
 def hipcc() -> str:

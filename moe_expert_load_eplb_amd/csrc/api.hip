@@ -123,6 +123,18 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
+                      int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,
+                      void* stream) {
+  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || RK < 1 || R < 1) return EPLB_E_ARG;
+  if (E > kMaxE || RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
+  if (B > 0 && (cnt == nullptr || home == nullptr || rep == nullptr || lam == nullptr || flow == nullptr ||
+                rank_load == nullptr || status == nullptr))
+    return EPLB_E_ARG;
+  hipError_t err = launch_lp_solve(cnt, home, rep, B, E, RK, R, lam, flow, rank_load, status, (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);
@@ -143,6 +155,7 @@ const char* eplb_status_string(int32_t code) {
     case EPLB_S_BAD_LOAD: return "problem status: a load is negative or above 2^40";
     case EPLB_S_OVERFLOW: return "problem status: exact pack sums need 127 bits or more";
     case EPLB_S_BAD_MAP: return "problem status: a map entry is out of range or an expert has no old replica";
+    case EPLB_S_BAD_TOPOLOGY: return "problem status: an id, home rank or count out of range, or an expert replicated twice";
     default: return "unknown code";
   }
 }

@@ -17,6 +17,9 @@ constexpr int kMaxX = 65535;                     // log2phy width
 constexpr int kMaxCount = 16128;                 // replica count bound (< 131^2)
 constexpr int kMaxP = 8192;                      // physical experts per problem
 constexpr int32_t kStatusBadMap = 18;            // rearrangement: an entry out of range
+constexpr int32_t kStatusBadTopology = 19;       // redistribution: an id, home or count out of range
+constexpr int kLpMaxRanks = 16;                  // ranks of one redistribution problem (2^RK rank sets)
+constexpr int kLpMaxSlots = 64;                  // replica slots per rank
 
 // ---------------------------------------------------------------- helpers
 // Magic numbers for floor(n / d) with 0 <= n < 2^31 and 1 <= d < 2^31
@@ -149,6 +152,9 @@ hipError_t launch_rearrange(const int32_t* old_p2l, const int32_t* new_p2l, cons
                             int32_t* l2p_out, int32_t* src, int32_t* moves, int32_t* status,
                             hipStream_t stream);
 int64_t rearrange_lds_bytes(int32_t E, int32_t P, int32_t N);
+hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
+                           int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
+                           int32_t* status, hipStream_t stream);
 hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
 hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
 hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,

@@ -1,0 +1,260 @@
+// Per-batch redistribution of tokens over a fixed replica topology
+// (LPLB-style), solved exactly in integers.
+//
+// Two pages describe LPLB: «DeepSeek开源LPLB：基于线性规划的MoE负载均衡器…»
+// (2048ai.net; items 4, 5 and 7: the replica topology, the LP model, the
+// typical topologies) and the Machine Heart report on LPLB (wwwcj777.com,
+// section «LPLB 的工作原理»).  A redundant expert links the GPU of its
+// original to its own GPU; that edge carries at most the tokens routed to
+// the expert in the batch; tokens move along the edges so that the loads of
+// the expert-parallel group are as even as possible.  Here: the least
+// largest rank load reachable with whole tokens, and one flow reaching it.
+//
+// One workgroup per problem (layer):
+//   1. home loads base[r] and the capacity cap[o][g] of every rank pair,
+//      with LDS atomics; a bitmap catches an expert replicated twice;
+//   2. the optimum, from the supply-demand theorem (Gale, 1957): a bound lam
+//      is reachable iff for every set S of ranks, load(S) - cap(S -> rest)
+//      <= lam * |S|, so lam* = max over S of ceil((load(S) - cap(S -> rest))
+//      / |S|); the 2^RK - 1 sets are enumerated in Gray-code order (one rank
+//      in or out per step, O(RK) to update the cut), spread over the threads;
+//   3. one wave computes a maximum flow of the feasibility network at lam*
+//      (source -> rank: what it must shed; rank -> sink: what it may take)
+//      by shortest augmenting paths (Edmonds and Karp, J. ACM 1972), the
+//      search level by level with one lane per node; a node's predecessor is
+//      the lowest-numbered node of the previous level with residual capacity,
+//      which fixes one definite flow among the optimal ones;
+//   4. the net flow of each rank pair is split over the pair's replica slots
+//      in ascending slot order.
+// Integer work throughout; RK <= 16 (the 8-GPU cube and 16-GPU hypercube
+// topologies of the pages), so every structure fits in LDS.
+#include "eplb_internal.h"
+
+namespace eplb {
+
+namespace {
+
+constexpr int kLpThreads = 256;
+constexpr int kLpMaxV = kLpMaxRanks + 2;
+constexpr int kLpMaxAugment = 1 << 16;     // far above the Edmonds-Karp bound V * E for V <= 18
+
+__device__ __forceinline__ void lp_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
+    const int64_t* __restrict__ cnt, const int32_t* __restrict__ home, const int32_t* __restrict__ rep,
+    int32_t E, int32_t RK, int32_t R, int64_t* __restrict__ lam_out, int64_t* __restrict__ flow_out,
+    int64_t* __restrict__ load_out, int32_t* __restrict__ status) {
+  __shared__ unsigned long long base[kLpMaxRanks];
+  __shared__ unsigned long long cap[kLpMaxRanks * kLpMaxRanks];      // cap[o * RK + g]
+  __shared__ long long res[kLpMaxV * kLpMaxV];                        // residual, res[u * V + v]
+  __shared__ uint32_t seen_bits[kMaxE / 32];
+  __shared__ long long s_best[kLpThreads / 64];
+
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t* c = cnt + b * E;
+  const int32_t* h = home + b * E;
+  const int32_t* rp = rep + b * (int64_t)RK * R;
+  const int V = RK + 2, src = RK, snk = RK + 1;
+
+  for (int i = tid; i < RK; i += kLpThreads) base[i] = 0;
+  for (int i = tid; i < RK * RK; i += kLpThreads) cap[i] = 0;
+  for (int i = tid; i < (E + 31) / 32; i += kLpThreads) seen_bits[i] = 0;
+  __syncthreads();
+
+  // ---- 1. home loads, rank-pair capacities
+  int bad = 0;
+  for (int e = tid; e < E; e += kLpThreads) {
+    const int64_t x = c[e];
+    const int32_t r = h[e];
+    const bool ok = x >= 0 && x <= kLoadMax && (uint32_t)r < (uint32_t)RK;
+    bad |= !ok;
+    if (ok) atomicAdd(&base[r], (unsigned long long)x);
+  }
+  for (int i = tid; i < RK * R; i += kLpThreads) {
+    const int32_t x = rp[i];
+    if (x == -1) continue;
+    if ((uint32_t)x >= (uint32_t)E) { bad = 1; continue; }
+    const uint32_t bit = 1u << (x & 31);
+    if (atomicOr(&seen_bits[x >> 5], bit) & bit) { bad = 1; continue; }   // replicated twice
+    const int32_t o = h[x], g = i / R;
+    const int64_t v = c[x];
+    if ((uint32_t)o < (uint32_t)RK && o != g && v >= 0 && v <= kLoadMax)
+      atomicAdd(&cap[o * RK + g], (unsigned long long)v);
+  }
+  bad = __syncthreads_or(bad);
+  int64_t* flow_b = flow_out + b * (int64_t)RK * R;
+  int64_t* load_b = load_out + b * RK;
+  if (bad) {
+    for (int i = tid; i < RK * R; i += kLpThreads) flow_b[i] = -1;
+    for (int i = tid; i < RK; i += kLpThreads) load_b[i] = -1;
+    if (tid == 0) {
+      lam_out[b] = -1;
+      status[b] = kStatusBadTopology;
+    }
+    return;
+  }
+
+  // ---- 2. lam* = max over rank sets S of ceil((load(S) - cap(S -> rest)) / |S|)
+  const uint32_t nsets = 1u << RK;                     // Gray index i in [1, nsets) gives S = i ^ (i >> 1)
+  const uint32_t per = (nsets - 1 + kLpThreads - 1) / kLpThreads;
+  const uint32_t i0 = 1 + (uint32_t)tid * per;
+  const uint32_t i1 = min(nsets, i0 + per);
+  long long best = 0;
+  if (i0 < i1) {
+    uint32_t S = i0 ^ (i0 >> 1);
+    long long ld = 0, out = 0;
+    for (int r = 0; r < RK; ++r) {
+      if (!((S >> r) & 1u)) continue;
+      ld += (long long)base[r];
+      for (int g = 0; g < RK; ++g)
+        if (!((S >> g) & 1u)) out += (long long)cap[r * RK + g];
+    }
+    for (uint32_t i = i0;; ) {
+      const int k = __popc(S);
+      const long long num = ld - out;
+      if (num > 0) {
+        const long long q = (num + k - 1) / k;
+        best = q > best ? q : best;
+      }
+      if (++i >= i1) break;
+      const int r = __builtin_ctz(i);                  // the rank that enters or leaves
+      const uint32_t T = S ^ (1u << r);
+      long long into_r = 0, from_r = 0;                // cap(S' -> r) and cap(r -> outside T)
+      for (int o = 0; o < RK; ++o) {
+        if (o == r) continue;
+        if ((T >> o) & 1u) into_r += (long long)cap[o * RK + r];
+        else from_r += (long long)cap[r * RK + o];
+      }
+      if ((T >> r) & 1u) {                             // r joins: its edges from the set become internal
+        ld += (long long)base[r];
+        out += from_r - into_r;
+      } else {                                         // r leaves
+        ld -= (long long)base[r];
+        out -= from_r - into_r;
+      }
+      S = T;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const long long o = __shfl_xor(best, off);
+    best = o > best ? o : best;
+  }
+  if (lane == 0) s_best[wave] = best;
+  // residual network at lam* (filled after the reduction)
+  __syncthreads();
+  long long lam = 0;
+  for (int w = 0; w < kLpThreads / 64; ++w) lam = s_best[w] > lam ? s_best[w] : lam;
+  for (int i = tid; i < V * V; i += kLpThreads) {
+    const int u = i / V, v = i - u * V;
+    long long x = 0;
+    if (u == src && v < RK) x = (long long)base[v] - lam > 0 ? (long long)base[v] - lam : 0;
+    else if (v == snk && u < RK) x = lam - (long long)base[u] > 0 ? lam - (long long)base[u] : 0;
+    else if (u < RK && v < RK && u != v) x = (long long)cap[u * RK + v];
+    res[i] = x;
+  }
+  __syncthreads();
+
+  // ---- 3. maximum flow at lam* (wave 0; one lane per node)
+  int exhausted = 0;
+  if (wave == 0) {
+    for (int it = 0; it < kLpMaxAugment; ++it) {
+      uint64_t seen = 1ull << src, frontier = 1ull << src;
+      int parent = -1;
+      while (frontier && !((seen >> snk) & 1ull)) {
+        int p = -1;
+        if (lane < V && !((seen >> lane) & 1ull)) {
+          for (int u = 0; u < V; ++u) {
+            if (((frontier >> u) & 1ull) && res[u * V + lane] > 0) { p = u; break; }
+          }
+        }
+        const uint64_t found = __builtin_amdgcn_ballot_w64(p >= 0);
+        if (p >= 0) parent = p;
+        seen |= found;
+        frontier = found;
+      }
+      if (!((seen >> snk) & 1ull)) break;
+      long long bn = -1;
+      for (int v = snk; v != src; ) {                  // uniform walk back to the source
+        const int u = __builtin_amdgcn_readlane(parent, v);
+        const long long x = res[u * V + v];
+        bn = (bn < 0 || x < bn) ? x : bn;
+        v = u;
+      }
+      lp_wave_sync();
+      if (lane == 0) {
+        for (int v = snk; v != src; ) {
+          const int u = __builtin_amdgcn_readlane(parent, v);
+          res[u * V + v] -= bn;
+          res[v * V + u] += bn;
+          v = u;
+        }
+      }
+      lp_wave_sync();
+      if (it == kLpMaxAugment - 1) exhausted = 1;
+    }
+  }
+  exhausted = __syncthreads_or(exhausted);
+  if (exhausted) {                                     // not reachable for V <= 18; reported, never silent
+    for (int i = tid; i < RK * R; i += kLpThreads) flow_b[i] = -1;
+    for (int i = tid; i < RK; i += kLpThreads) load_b[i] = -1;
+    if (tid == 0) {
+      lam_out[b] = -1;
+      status[b] = kStatusBadTopology;
+    }
+    return;
+  }
+
+  // ---- 4. net flow per rank pair, split over the pair's slots in slot order:
+  // thread (o, g) fills the slots of rank g that replicate an expert of rank
+  // o; thread (g, g) writes 0 to the slots of g that move nothing
+  for (int i = tid; i < RK * RK; i += kLpThreads) {
+    const int o = i / RK, g = i - o * RK;
+    const long long n = o == g ? 0 : (long long)cap[o * RK + g] - res[o * V + g];
+    long long left = n > 0 ? n : 0;
+    for (int j = 0; j < R; ++j) {
+      const int32_t x = rp[g * R + j];
+      const int ox = x >= 0 ? h[x] : g;
+      if (o == g) {
+        if (ox == g) flow_b[g * R + j] = 0;
+      } else if (ox == o) {
+        const long long cx = c[x];
+        const long long f = left < cx ? left : cx;
+        left -= f;
+        flow_b[g * R + j] = f;
+      }
+    }
+  }
+  for (int r = tid; r < RK; r += kLpThreads) {
+    long long l = (long long)base[r];
+    for (int g = 0; g < RK; ++g) {
+      if (g == r) continue;
+      const long long out_n = (long long)cap[r * RK + g] - res[r * V + g];
+      const long long in_n = (long long)cap[g * RK + r] - res[g * V + r];
+      l -= out_n > 0 ? out_n : 0;
+      l += in_n > 0 ? in_n : 0;
+    }
+    load_b[r] = l;
+  }
+  if (tid == 0) {
+    lam_out[b] = lam;
+    status[b] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
+                           int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
+                           int32_t* status, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  lp_solve_kernel<<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, lam, flow, rank_load, status);
+  return hipGetLastError();
+}
+
+}  // namespace eplb

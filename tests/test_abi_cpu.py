@@ -41,6 +41,7 @@ def lib():
     lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
     lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
+    lib.eplb_lp_solve.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
@@ -51,7 +52,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
-                          "eplb_placement_load", "eplb_rearrange"}
+                          "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -60,7 +61,7 @@ def test_codes_match_binding_and_oracle():
     c = header_constants()
     assert c["EPLB_OK"] == 0 and len({v for k, v in c.items() if k.startswith("EPLB_E_")}) == 7
     assert c["EPLB_S_BAD_LOAD"] == ora.STATUS_BAD_LOAD and c["EPLB_S_OVERFLOW"] == ora.STATUS_OVERFLOW
-    assert c["EPLB_S_BAD_MAP"] == ora.STATUS_BAD_MAP
+    assert c["EPLB_S_BAD_MAP"] == ora.STATUS_BAD_MAP and c["EPLB_S_BAD_TOPOLOGY"] == ora.STATUS_BAD_TOPOLOGY
     src = open(os.path.join(ROOT, "moe_expert_load_eplb_amd", "__init__.py")).read()
     for k, v in c.items():
         if k.startswith("EPLB_"):
@@ -195,3 +196,15 @@ def test_rearrange_validation(lib):
             args[6] = 32                                # keep P % RK == 0
         assert lib.eplb_rearrange(*args) == code, (pos, bad)
     assert lib.eplb_rearrange(None, None, None, 0, 256, 288, 32, 4, 9, None, None, None, None, None, None) == 0
+
+
+def test_lp_solve_validation(lib):
+    F = [FAKE + 64 * i for i in range(8)]
+    good = [F[0], F[1], F[2], 58, 256, 8, 2, F[3], F[4], F[5], F[6], None]
+    for pos, bad, code in [(3, -1, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (4, 4097, 5), (5, 17, 5), (6, 65, 5),
+                           (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1), (9, None, 1),
+                           (10, None, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_lp_solve(*args) == code, (pos, bad)
+    assert lib.eplb_lp_solve(None, None, None, 0, 256, 8, 2, None, None, None, None, None) == 0

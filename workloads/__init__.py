@@ -221,6 +221,71 @@ def skewed_loads(wl: Workload = SKEWED_1024, problems: range | None = None) -> n
     return out
 
 
+# ---------------------------------------------------------------- LPLB-style redistribution
+# The 8-GPU cube of the LPLB usage example (its r2o table): slot j of rank g
+# holds a replica of an expert whose original lives on rank CUBE_R2O[g][j].
+CUBE_R2O = ((3, 6), (0, 7), (1, 4), (2, 5), (7, 0), (4, 1), (5, 2), (6, 3))
+
+
+def hypercube_r2o(RK: int) -> tuple:
+    """Rank g's slot d replicates an expert of rank g xor 2^d (no diagonals)."""
+    dims = RK.bit_length() - 1
+    assert 1 << dims == RK
+    return tuple(tuple(g ^ (1 << d) for d in range(dims)) for g in range(RK))
+
+
+@dataclass
+class LpWorkload:
+    """Per-batch redistribution inputs: ids of one batch per layer, experts
+    in contiguous blocks per rank, replica slots named by an r2o table."""
+    name: str
+    wid: int
+    layers: int
+    E: int
+    RK: int
+    r2o: tuple
+    tokens: int
+    topk: int
+    param: float                   # Zipf exponent of the per-layer popularity
+
+
+LPLB_CUBE = LpWorkload(name="lplb_cube_58L_e256_8x2", wid=5, layers=58, E=256, RK=8, r2o=CUBE_R2O,
+                       tokens=16384, topk=8, param=1.1)
+LPLB_HYPERCUBE = LpWorkload(name="lplb_hypercube_58L_e256_16x4", wid=6, layers=58, E=256, RK=16,
+                            r2o=hypercube_r2o(16), tokens=16384, topk=8, param=1.1)
+
+
+def lp_inputs(w: LpWorkload, layers: range | None = None, tokens: int | None = None):
+    """(idx [L][T][K] int32, home [L][E] int32, rep [L][RK][R] int32).
+
+    Per layer: a Zipf popularity over a random permutation of the experts,
+    T tokens x K distinct ids drawn from it; expert e's original on rank
+    e // (E / RK); the slots that name rank o in r2o (in (g, j) order) take
+    o's experts in order of decreasing popularity (ties: lower id), so the
+    most popular experts of each rank have the replicas.
+    """
+    layers = range(w.layers) if layers is None else layers
+    T = w.tokens if tokens is None else tokens
+    per = w.E // w.RK
+    R = len(w.r2o[0])
+    idx = np.empty((len(layers), T, w.topk), dtype=np.int32)
+    home = np.empty((len(layers), w.E), dtype=np.int32)
+    rep = np.full((len(layers), w.RK, R), -1, dtype=np.int32)
+    for i, l in enumerate(layers):
+        rng = rng_for(w.wid, l)
+        p = zipf_probs(w.E, w.param, rng.permutation(w.E))
+        idx[i] = draw_ids(rng_for(w.wid, l, 1), p, T, w.topk, distinct=True)
+        home[i] = np.arange(w.E) // per
+        nxt = {o: 0 for o in range(w.RK)}
+        for g in range(w.RK):
+            for j in range(R):
+                o = w.r2o[g][j]
+                mine = sorted(range(o * per, (o + 1) * per), key=lambda e: (-p[e], e))
+                rep[i, g, j] = mine[nxt[o]]
+                nxt[o] += 1
+    return idx, home, rep
+
+
 def zipf_loads(B: int, E: int, s: float, tokens: int, wid: int = 9) -> np.ndarray:
     """Generic loads [B, E] int64: multinomial token counts, Zipf(s) popularity."""
     out = np.zeros((B, E), dtype=np.int64)
