@@ -684,10 +684,13 @@ def lp_redirect(idx, rep, flow, E: int) -> np.ndarray:
 
     Physical ids: expert e's original is e; slot j of rank g is E + g*R + j
     (the LPLB planner of the usage example on «DeepSeek开源LPLB…» counts
-    the logical experts plus the redundant ones per rank times the ranks).  The occurrences of expert x in a layer,
-    counted in (token, k) order, are numbered 0, 1, ...; the first f of them
-    go to x's replica, f being that replica's flow, the rest stay with the
-    original.  Ids outside [0, E) give -1.
+    the logical experts plus the redundant ones per rank times the ranks).
+    The occurrences of expert x in a layer, counted in (token, k) order, are
+    numbered 0, 1, ...; the first f of them go to x's replica, f being that
+    replica's flow, the rest stay with the original.  Ids outside [0, E)
+    give -1, and so does every id of a layer whose rep names an id outside
+    [0, E) or an expert twice (the topologies eplb_lp_solve rejects; the
+    pages' planner never builds one).
     """
     idx = np.asarray(idx)
     rep = np.asarray(rep)
@@ -696,6 +699,10 @@ def lp_redirect(idx, rep, flow, E: int) -> np.ndarray:
     RK, R = rep.shape[1], rep.shape[2]
     out = np.empty(idx.shape, dtype=np.int32)
     for l in range(L):
+        named = [int(x) for x in rep[l].ravel().tolist() if x != -1]
+        if any(not (0 <= x < E) for x in named) or len(set(named)) != len(named):
+            out[l] = -1
+            continue
         slot = np.full(E, -1, dtype=np.int64)
         fx = np.zeros(E, dtype=np.int64)
         for g in range(RK):

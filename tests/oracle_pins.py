@@ -743,6 +743,11 @@ def pin_lp_redirect(o):
         for x, (g, j) in slot.items():
             moved = int((got[l] == E + g * R + j).sum())
             assert moved == min(int(flow[l, g, j]), int((idx[l] == x).sum()))
+    bad = rep.copy()
+    bad[0, 0, 1] = 0                                  # expert 0 twice in layer 0
+    bad[1, 0, 0] = E                                  # an id out of range in layer 1
+    got = o.lp_redirect(idx, bad, flow, E)
+    assert (got == -1).all()
 
 
 def pin_lp_status(o):
