@@ -19,7 +19,8 @@
  *   - All array arguments are DEVICE pointers to contiguous, row-major memory
  *     that the caller allocates, owns and keeps alive until the work enqueued
  *     on `stream` has finished.  The library allocates, frees and synchronises
- *     nothing and keeps no state between calls.
+ *     nothing and keeps no state between calls (the one call that needs
+ *     working memory, eplb_lp_redirect, takes it as an argument).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; the return code reports host-side validation and launch
  *     only.  Calls on different streams may run concurrently provided their
@@ -301,6 +302,42 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
 int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                       int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,
                       void* stream);
+
+/*
+ * eplb_lp_redirect -- route every (token, k) by the flows of eplb_lp_solve.
+ *
+ * Follows: the LPLB usage example on «DeepSeek开源LPLB…» (the planner maps
+ * the model's logical ids to physical ones; physical experts are the E
+ * logical ones followed by RK * R redundant slots) and the flows above.  In
+ * each layer the occurrences of expert x are numbered 0, 1, ... in (token, k)
+ * order; if x has a replica in slot (g, j), the first flow[g][j] of them go
+ * there, the rest to the original:
+ *     out = E + g*R + j   for occurrence i < flow[g][j],   else   out = x
+ * An id outside [0, E) gives -1; so does every id of a layer whose rep names
+ * an id outside [0, E) or an expert twice.
+ *
+ *   idx        [L][T][K] int32   logical ids of the batch
+ *   rep        [L][RK][R] int32  replica slots (as for eplb_lp_solve)
+ *   flow       [L][RK][R] int64  tokens each slot takes (eplb_lp_solve)
+ *   RK, R                        ranks (1 .. 16) and slots per rank (1 .. 64)
+ *   workspace                    caller-owned device memory of at least
+ *                                eplb_lp_redirect_workspace_bytes(L, T, K, E)
+ *                                bytes (per-segment counts; contents on entry
+ *                                do not matter and are overwritten)
+ *   workspace_bytes              its size
+ *   out        [L][T][K] int32   out: physical ids; must not overlap idx
+ *
+ * Errors: as for eplb_redirect; EPLB_E_ARG also for RK or R < 1, a NULL
+ * array or workspace, or a workspace below the size needed; EPLB_E_LIMIT for
+ * RK > 16, R > 64, or more than 2^30 segments of 2048 ids.
+ */
+int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
+                         const int64_t* flow, int32_t RK, int32_t R, void* workspace, int64_t workspace_bytes,
+                         int32_t* out, void* stream);
+
+/* Bytes of workspace eplb_lp_redirect needs: L * ceil(T*K / 2048) * E * 4,
+ * or a negative EPLB_E_* code.  Host only. */
+int64_t eplb_lp_redirect_workspace_bytes(int64_t L, int64_t T, int32_t K, int32_t E);
 
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);

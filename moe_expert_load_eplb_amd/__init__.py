@@ -33,7 +33,8 @@ EPLB_S_BAD_MAP = 18
 EPLB_S_BAD_TOPOLOGY = 19
 
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
-           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_status_string",
+           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
+           "eplb_lp_redirect_workspace_bytes", "eplb_status_string",
            "eplb_rebalance_lds_bytes")
 
 
@@ -63,6 +64,10 @@ def _load() -> ctypes.CDLL:
     lib.eplb_rearrange.restype = i32
     lib.eplb_lp_solve.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p]
     lib.eplb_lp_solve.restype = i32
+    lib.eplb_lp_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, i32, p, i64, p, p]
+    lib.eplb_lp_redirect.restype = i32
+    lib.eplb_lp_redirect_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.eplb_lp_redirect_workspace_bytes.restype = i64
     lib.eplb_status_string.argtypes = [i32]
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -341,3 +346,38 @@ def lp_solve(cnt: torch.Tensor, home: torch.Tensor, rep: torch.Tensor, out: tupl
                            _dev(status, torch.int32, "status"), _stream(dev))
     _check(rc, "eplb_lp_solve")
     return lam, flow, rank_load, status
+
+
+def lp_redirect_workspace_bytes(L: int, T: int, K: int, E: int) -> int:
+    n = lib.eplb_lp_redirect_workspace_bytes(L, T, K, E)
+    if n < 0:
+        raise EplbError(-n, "eplb_lp_redirect_workspace_bytes")
+    return n
+
+
+def lp_redirect(idx: torch.Tensor, E: int, rep: torch.Tensor, flow: torch.Tensor,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Physical expert of every (token, k) under the flows of lp_solve:
+    [L, T, K] int32.  ``workspace`` (any dtype, contiguous, on the GPU) must
+    hold lp_redirect_workspace_bytes(L, T, K, E) bytes; one is made if absent."""
+    if idx.dim() != 3 or rep.dim() != 3 or flow.dim() != 3:
+        raise ValueError("idx [L, T, K], rep [L, RK, R], flow [L, RK, R] expected")
+    L, T, K = idx.shape
+    _, RK, R = rep.shape
+    if rep.shape[0] != L or tuple(flow.shape) != tuple(rep.shape):
+        raise ValueError("rep and flow must be [L, RK, R] for idx's layers")
+    need = lp_redirect_workspace_bytes(L, T, K, E)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4),), dtype=torch.uint8, device=idx.device)
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty_like(idx)
+    if out.shape != idx.shape:
+        raise ValueError("out must have idx's shape")
+    rc = lib.eplb_lp_redirect(_dev(idx, torch.int32, "idx"), L, T, K, E, _dev(rep, torch.int32, "rep"),
+                              _dev(flow, torch.int64, "flow"), RK, R, workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _dev(out, torch.int32, "out"),
+                              _stream(idx.device))
+    _check(rc, "eplb_lp_redirect")
+    return out

@@ -135,6 +135,31 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int64_t eplb_lp_redirect_workspace_bytes(int64_t L, int64_t T, int32_t K, int32_t E) {
+  if (L < 0 || T < 0 || K < 1 || E < 1) return -(int64_t)EPLB_E_ARG;
+  if (T > kMaxIdsPerLayer / K) return -(int64_t)EPLB_E_RANGE;
+  return L * lp_segments(T * (int64_t)K) * E * (int64_t)sizeof(int32_t);
+}
+
+int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
+                         const int64_t* flow, int32_t RK, int32_t R, void* workspace, int64_t workspace_bytes,
+                         int32_t* out, void* stream) {
+  int32_t rc = check_stream_args(idx, L, T, K, E);
+  if (rc != EPLB_OK) return rc;
+  if (RK < 1 || R < 1) return EPLB_E_ARG;
+  if (RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
+  const int64_t n = T * (int64_t)K;
+  if (L * lp_segments(n) > (int64_t(1) << 30)) return EPLB_E_LIMIT;
+  if (L > 0 && n > 0) {
+    if (rep == nullptr || flow == nullptr || out == nullptr || workspace == nullptr) return EPLB_E_ARG;
+    if ((const void*)out == (const void*)idx) return EPLB_E_ARG;
+    if (workspace_bytes < eplb_lp_redirect_workspace_bytes(L, T, K, E)) return EPLB_E_ARG;
+  }
+  hipError_t err = launch_lp_redirect(idx, L, n, E, rep, flow, RK, R, static_cast<int32_t*>(workspace), out,
+                                      (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);

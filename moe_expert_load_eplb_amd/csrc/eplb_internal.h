@@ -20,6 +20,7 @@ constexpr int32_t kStatusBadMap = 18;            // rearrangement: an entry out 
 constexpr int32_t kStatusBadTopology = 19;       // redistribution: an id, home or count out of range
 constexpr int kLpMaxRanks = 16;                  // ranks of one redistribution problem (2^RK rank sets)
 constexpr int kLpMaxSlots = 64;                  // replica slots per rank
+constexpr int kLpSeg = 2048;                     // ids per wave in the redirect by flows
 
 // ---------------------------------------------------------------- helpers
 // Magic numbers for floor(n / d) with 0 <= n < 2^31 and 1 <= d < 2^31
@@ -152,6 +153,10 @@ hipError_t launch_rearrange(const int32_t* old_p2l, const int32_t* new_p2l, cons
                             int32_t* l2p_out, int32_t* src, int32_t* moves, int32_t* status,
                             hipStream_t stream);
 int64_t rearrange_lds_bytes(int32_t E, int32_t P, int32_t N);
+int64_t lp_segments(int64_t n);
+hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t E, const int32_t* rep,
+                              const int64_t* flow, int32_t RK, int32_t R, int32_t* seg, int32_t* out,
+                              hipStream_t stream);
 hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
                            int32_t* status, hipStream_t stream);

@@ -247,7 +247,153 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   }
 }
 
+// ---------------------------------------------------------------- redirect by the flows
+// Occurrence i (in (token, k) order within the layer) of a replicated expert
+// x goes to x's replica when i < flow, else to the original.  The order is a
+// per-expert running count over the whole layer, so the layer is cut into
+// segments of kLpSeg ids, one wave each: (A) count every segment's ids per
+// expert into the workspace, (B) turn the counts into exclusive prefixes
+// over the segments, (C) each wave starts its experts' counters at those
+// prefixes and walks its segment 64 ids at a time, ranking equal ids among
+// the lanes with one ballot per bit of the expert id (peers share every
+// bit), so the numbering matches a sequential pass exactly.
+
+__host__ __device__ inline int lp_waves_per_block(int words_per_wave) {
+  const int w = (kMaxLdsBytes / 4) / words_per_wave;
+  return w < 1 ? 1 : (w > 4 ? 4 : w);
+}
+
+__global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __restrict__ idx, int64_t n, int32_t E,
+                                                           int64_t S, int64_t LS, int32_t wpb,
+                                                           int32_t* __restrict__ seg) {
+  extern __shared__ int32_t lp_cnt[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = (int64_t)blockIdx.x * wpb + wave;
+  if (q >= LS) return;                                 // whole wave; no workgroup barrier below
+  const int64_t l = q / S, s = q - l * S;
+  int32_t* cnt = lp_cnt + wave * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  lp_wave_sync();
+  const int32_t* src = idx + l * n + s * kLpSeg;
+  const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
+  for (int i = lane; i < len; i += 64) {
+    const int32_t e = src[i];
+    if ((uint32_t)e < (uint32_t)E) atomicAdd(&cnt[e], 1);
+  }
+  lp_wave_sync();
+  int32_t* dst = seg + q * E;
+  for (int e = lane; e < E; e += 64) dst[e] = cnt[e];
+}
+
+__global__ __launch_bounds__(256) void lp_seg_scan_kernel(int32_t* __restrict__ seg, int64_t L, int64_t S,
+                                                          int32_t E) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= L * E) return;
+  const int64_t l = t / E, e = t - l * E;
+  int32_t* p = seg + l * S * E + e;
+  int32_t run = 0;
+  for (int64_t s = 0; s < S; ++s) {
+    const int32_t v = p[s * E];
+    p[s * E] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restrict__ idx, int64_t n, int32_t E,
+                                                          int32_t nbits, const int32_t* __restrict__ rep,
+                                                          const int64_t* __restrict__ flow, int32_t RKR, int64_t S,
+                                                          int64_t LS, int32_t wpb, const int32_t* __restrict__ seg,
+                                                          int32_t* __restrict__ out) {
+  extern __shared__ int32_t lp_tab[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = (int64_t)blockIdx.x * wpb + wave;
+  if (q >= LS) return;                                 // whole wave; no workgroup barrier below
+  const int64_t l = q / S, s = q - l * S;
+  int32_t* run = lp_tab + wave * 3 * E;                // running occurrence count per expert
+  int32_t* pid = run + E;                              // replica's physical id, or -1
+  int32_t* fx = pid + E;                               // replica's flow (clamped to int32)
+  const int32_t* base = seg + q * E;
+  for (int e = lane; e < E; e += 64) {
+    run[e] = base[e];
+    pid[e] = -1;
+    fx[e] = 0;
+  }
+  lp_wave_sync();
+  const int32_t* rl = rep + l * RKR;
+  const int64_t* fl = flow + l * RKR;
+  int bad = 0;
+  for (int i = lane; i < RKR; i += 64) {
+    const int32_t x = rl[i];
+    if (x == -1) continue;
+    if ((uint32_t)x >= (uint32_t)E) { bad = 1; continue; }
+    if (atomicExch(&pid[x], E + i) != -1) bad = 1;     // named twice
+    const int64_t f = fl[i];
+    fx[x] = f <= 0 ? 0 : (f >= 0x7fffffff ? 0x7fffffff : (int32_t)f);
+  }
+  bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  lp_wave_sync();
+  const int32_t* src = idx + l * n + s * kLpSeg;
+  int32_t* dst = out + l * n + s * kLpSeg;
+  const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
+  const uint64_t below = (1ull << lane) - 1;
+  for (int r0 = 0; r0 < len; r0 += 256) {
+    int32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = r0 + k * 64 + lane;
+      v[k] = i < len ? src[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = r0 + k * 64 + lane;
+      if (r0 + k * 64 >= len) break;                   // uniform
+      const int32_t e = v[k];
+      const bool valid = i < len && (uint32_t)e < (uint32_t)E && !bad;
+      uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool one = (e >> bit) & 1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(valid && one);
+        peers &= one ? m : ~m;
+      }
+      int32_t res = -1;
+      if (valid) {
+        const int rank = __popcll(peers & below);
+        const int32_t occ = run[e] + rank;
+        const int32_t p = pid[e];
+        res = (p >= 0 && occ < fx[e]) ? p : e;
+        if (rank == 0) run[e] = occ + __popcll(peers);
+      }
+      lp_wave_sync();
+      if (i < len) dst[i] = res;
+    }
+  }
+}
+
 }  // namespace
+
+int64_t lp_segments(int64_t n) { return (n + kLpSeg - 1) / kLpSeg; }
+
+hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t E, const int32_t* rep,
+                              const int64_t* flow, int32_t RK, int32_t R, int32_t* seg, int32_t* out,
+                              hipStream_t stream) {
+  const int64_t S = lp_segments(n);
+  const int64_t LS = L * S;
+  if (LS == 0) return hipSuccess;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int wpb_a = lp_waves_per_block(E);
+  lp_seg_count_kernel<<<(unsigned)((LS + wpb_a - 1) / wpb_a), 64 * wpb_a, (size_t)wpb_a * E * 4, stream>>>(
+      idx, n, E, S, LS, wpb_a, seg);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  lp_seg_scan_kernel<<<(unsigned)((L * E + 255) / 256), 256, 0, stream>>>(seg, L, S, E);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int wpb_c = lp_waves_per_block(3 * E);
+  lp_redirect_kernel<<<(unsigned)((LS + wpb_c - 1) / wpb_c), 64 * wpb_c, (size_t)wpb_c * 3 * E * 4, stream>>>(
+      idx, n, E, nbits, rep, flow, RK * R, S, LS, wpb_c, seg, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,

@@ -42,6 +42,9 @@ def lib():
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
     lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
     lib.eplb_lp_solve.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p]
+    lib.eplb_lp_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, i32, p, i64, p, p]
+    lib.eplb_lp_redirect_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.eplb_lp_redirect_workspace_bytes.restype = i64
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
@@ -52,7 +55,8 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
-                          "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve"}
+                          "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
+                          "eplb_lp_redirect_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -208,3 +212,19 @@ def test_lp_solve_validation(lib):
         args[pos] = bad
         assert lib.eplb_lp_solve(*args) == code, (pos, bad)
     assert lib.eplb_lp_solve(None, None, None, 0, 256, 8, 2, None, None, None, None, None) == 0
+
+
+def test_lp_redirect_validation(lib):
+    F = [FAKE + 64 * i for i in range(8)]
+    need = lib.eplb_lp_redirect_workspace_bytes(58, 16384, 8, 256)
+    assert need == 58 * 64 * 256 * 4
+    assert lib.eplb_lp_redirect_workspace_bytes(58, 1 << 28, 8, 256) == -6
+    assert lib.eplb_lp_redirect_workspace_bytes(-1, 10, 8, 256) == -1
+    good = [F[0], 58, 16384, 8, 256, F[1], F[2], 8, 2, F[3], need, F[4], None]
+    for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (7, 0, 1), (8, 0, 1),
+                           (7, 17, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
+                           (11, None, 1), (11, F[0], 1), (10, need - 1, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_lp_redirect(*args) == code, (pos, bad)
+    assert lib.eplb_lp_redirect(None, 0, 16384, 8, 256, None, None, 8, 2, None, 0, None, None) == 0

@@ -109,3 +109,71 @@ def test_lp_solve_degenerate_and_bad():
                       torch.zeros((0, 4), dtype=torch.int32, device=DEV),
                       torch.zeros((0, 3, 2), dtype=torch.int32, device=DEV))
     assert [tuple(t.shape) for t in z] == [(0,), (0, 3, 2), (0, 3), (0,)]
+
+
+# ---------------------------------------------------------------- redirect by the flows
+
+@pytest.mark.parametrize("L,T,K,E,RK,R", [(2, 5000, 8, 64, 8, 2), (3, 1, 3, 5, 2, 1), (1, 2048, 1, 256, 8, 2),
+                                          (2, 4097, 2, 1, 1, 1), (1, 33333, 3, 4096, 16, 4),
+                                          (4, 700, 7, 300, 11, 3)])
+def test_lp_redirect_random(L, T, K, E, RK, R):
+    """Segments of 2048 ids cut anywhere (ragged tails, one id, several
+    segments), out-of-range ids, flows of 0, above the count and negative,
+    a workspace holding garbage."""
+    rng = np.random.default_rng(L * T + E)
+    idx_h = rng.integers(-2, E + 2, size=(L, T, K)).astype(np.int32)
+    rep = np.full((L, RK, R), -1, dtype=np.int32)
+    for l in range(L):
+        pool = list(rng.permutation(E))
+        for g in range(RK):
+            for j in range(R):
+                if pool and rng.random() < 0.8:
+                    rep[l, g, j] = pool.pop()
+    flow = rng.integers(-3, max(4, T * K // max(E, 1) * 2), size=(L, RK, R)).astype(np.int64)
+    flow[0, 0, 0] = 1 << 40
+    need = eplb.lp_redirect_workspace_bytes(L, T, K, E)
+    ws = torch.randint(-1000, 1000, (max(need // 4, 1),), dtype=torch.int32, device=DEV)
+    note(f"lp_redirect L={L} T={T} K={K} E={E} RK={RK} R={R}")
+    got = eplb.lp_redirect(gpu(idx_h, torch.int32), E, gpu(rep, torch.int32), gpu(flow, torch.int64), ws)
+    torch.cuda.synchronize()
+    assert_same("lp_redirect", got.cpu().numpy(), ora.lp_redirect(idx_h, rep, flow, E))
+
+
+def test_lp_redirect_bad_layers():
+    rng = np.random.default_rng(2)
+    E, RK, R = 20, 4, 2
+    idx_h = rng.integers(0, E, size=(3, 3000, 2)).astype(np.int32)
+    rep = np.array([[[0, 1], [2, 3], [4, 5], [6, 7]]] * 3, dtype=np.int32)
+    rep[1, 3, 1] = 0                                   # expert 0 twice
+    rep[2, 0, 0] = E + 4                               # out of range
+    flow = np.full((3, RK, R), 100, dtype=np.int64)
+    got = eplb.lp_redirect(gpu(idx_h, torch.int32), E, gpu(rep, torch.int32), gpu(flow, torch.int64)).cpu().numpy()
+    assert_same("lp_redirect", got, ora.lp_redirect(idx_h, rep, flow, E))
+    assert (got[1:] == -1).all() and (got[0] >= 0).all()
+
+
+@pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE], ids=lambda w: w.name)
+def test_lp_batch_end_to_end(work):
+    """One batch through the whole LPLB-style path on the GPU: per-layer
+    counts (eplb_load_hist, W = 1), the solve, the redirect; the redirect
+    matches the oracle on sampled layers, and on every layer the ids each
+    rank ends up serving add up to the solve's rank loads."""
+    idx_h, home, rep = wl.lp_inputs(work)
+    L, E, RK = work.layers, work.E, work.RK
+    R = rep.shape[2]
+    idx = gpu(idx_h, torch.int32)
+    ring = torch.zeros((1, L, E), dtype=torch.int32, device=DEV)
+    cnt, bad = eplb.load_hist(idx, E, ring, 0)
+    lam, flow, rank_load, status = eplb.lp_solve(cnt, gpu(home, torch.int32), gpu(rep, torch.int32))
+    out = eplb.lp_redirect(idx, E, gpu(rep, torch.int32), flow)
+    torch.cuda.synchronize()
+    assert int(status.abs().sum()) == 0 and int(bad.sum()) == 0
+    out_h, flow_h, load_h = out.cpu().numpy(), flow.cpu().numpy(), rank_load.cpu().numpy()
+    for l in (0, 29, 57):
+        assert_same(f"layer {l}", out_h[l:l + 1], ora.lp_redirect(idx_h[l:l + 1], rep[l:l + 1], flow_h[l:l + 1], E))
+    rank_of = np.empty((L, E + RK * R), dtype=np.int64)
+    rank_of[:, :E] = home
+    rank_of[:, E:] = np.repeat(np.arange(RK), R)[None, :]
+    for l in range(L):
+        served = np.bincount(rank_of[l][out_h[l].ravel()], minlength=RK)
+        assert served.tolist() == load_h[l].tolist(), f"layer {l}"
