@@ -9,7 +9,8 @@ Also reported: the serving-loop step (eplb_hist_redirect, which reads the ids
 once, then the rebalance for the next step), the moving-average estimator
 (eplb_load_ema), the per-rank load and max/mean of the placement
 (eplb_placement_load), the plan of weight copies between two placements
-(eplb_rearrange), and the rebalance latency of the global-policy decode
+(eplb_rearrange), the LPLB-style per-batch redistribution (eplb_lp_solve,
+eplb_lp_redirect), and the rebalance latency of the global-policy decode
 shape and of the 1024-problem skewed batch.
 on the streaming workload: 58 MoE layers x 2^20 tokens x top-8 int32 ids per
 step (1.95 GB), Zipf(1.1) expert popularity, a 10-step window.  Ten distinct
@@ -307,6 +308,7 @@ def main() -> int:
         },
     }
 
+    result["lp_redistribution"] = lp_batches(eplb, wl, dev, stream)
     result["other_workloads"] = small_workloads(eplb, wl, dev, stream)
     result["serving_graph"] = graph_serving(eplb, wl, dev)
 
@@ -350,6 +352,54 @@ def small_workloads(eplb, wl, dev, stream):
                 ts.append(a.elapsed_time(b) * 1e3)
             rec[f"{name}_us"] = round(statistics.median(ts[5:]), 2)
         out[work.name] = rec
+    return out
+
+
+def lp_batches(eplb, wl, dev, stream):
+    """The LPLB-style per-batch path on its two topologies (8-GPU cube,
+    16-GPU hypercube; 58 layers x 16384 tokens x top-8): device time of the
+    exact solve for all layers and of the redirect by its flows, and how far
+    the largest rank load drops."""
+    import torch
+    out = {}
+    for work in (wl.LPLB_CUBE, wl.LPLB_HYPERCUBE):
+        idx_h, home_h, rep_h = wl.lp_inputs(work)
+        L, E = work.layers, work.E
+        idx = torch.from_numpy(idx_h).to(dev)
+        home = torch.from_numpy(home_h).to(dev)
+        rep = torch.from_numpy(rep_h).to(dev)
+        ring = torch.zeros((1, L, E), dtype=torch.int32, device=dev)
+        cnt, bad = eplb.load_hist(idx, E, ring, 0)
+        sol = eplb.lp_solve(cnt, home, rep)
+        ws = torch.empty((eplb.lp_redirect_workspace_bytes(L, work.tokens, work.topk, E),), dtype=torch.uint8,
+                         device=dev)
+        red = eplb.lp_redirect(idx, E, rep, sol[1], ws)
+        torch.cuda.synchronize()
+        assert int(sol[3].abs().sum()) == 0
+
+        def med(fn, n=30):
+            ts = []
+            for _ in range(n):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            return statistics.median(ts[5:])
+        solve_us = med(lambda: eplb.lp_solve(cnt, home, rep, out=sol))
+        red_us = med(lambda: eplb.lp_redirect(idx, E, rep, sol[1], ws, out=red))
+        base = torch.zeros((L, work.RK), dtype=torch.int64, device=dev).scatter_add_(1, home.long(), cnt)
+        before = base.max(dim=1).values.double()
+        after = sol[0].double()
+        mean = cnt.sum(dim=1).double() / work.RK
+        out[work.name] = {
+            "solve_58_layers_us": round(solve_us, 2),
+            "redirect_us": round(red_us, 2),
+            "redirect_GBps": round(8 * idx.numel() / (red_us * 1e-6) / 1e9, 1),
+            "max_over_mean_before": round(float((before / mean).mean()), 4),
+            "max_over_mean_after": round(float((after / mean).mean()), 4),
+        }
     return out
 
 

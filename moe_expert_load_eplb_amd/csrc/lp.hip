@@ -17,7 +17,8 @@
 //      is reachable iff for every set S of ranks, load(S) - cap(S -> rest)
 //      <= lam * |S|, so lam* = max over S of ceil((load(S) - cap(S -> rest))
 //      / |S|); the 2^RK - 1 sets are enumerated in Gray-code order (one rank
-//      in or out per step, O(RK) to update the cut), spread over the threads;
+//      in or out per step; the cut changes by that rank's edges to and from
+//      the set, visited through neighbour bitmasks), spread over the threads;
 //   3. one wave computes a maximum flow of the feasibility network at lam*
 //      (source -> rank: what it must shed; rank -> sink: what it may take)
 //      by shortest augmenting paths (Edmonds and Karp, J. ACM 1972), the
@@ -28,13 +29,15 @@
 //      in ascending slot order.
 // Integer work throughout; RK <= 16 (the 8-GPU cube and 16-GPU hypercube
 // topologies of the pages), so every structure fits in LDS.
+#include <climits>
+
 #include "eplb_internal.h"
 
 namespace eplb {
 
 namespace {
 
-constexpr int kLpThreads = 256;
+constexpr int kLpThreads = 1024;
 constexpr int kLpMaxV = kLpMaxRanks + 2;
 constexpr int kLpMaxAugment = 1 << 16;     // far above the Edmonds-Karp bound V * E for V <= 18
 
@@ -53,6 +56,7 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   __shared__ long long res[kLpMaxV * kLpMaxV];                        // residual, res[u * V + v]
   __shared__ uint32_t seen_bits[kMaxE / 32];
   __shared__ long long s_best[kLpThreads / 64];
+  __shared__ uint32_t nin[kLpMaxRanks], nout[kLpMaxRanks];
 
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -101,11 +105,25 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   }
 
   // ---- 2. lam* = max over rank sets S of ceil((load(S) - cap(S -> rest)) / |S|)
+  // neighbour sets: bit o of nin[r] if cap[o][r] > 0, bit g of nout[r] if cap[r][g] > 0
+  if (tid < RK) {
+    uint32_t mi = 0, mo = 0;
+    for (int o = 0; o < RK; ++o) {
+      mi |= (uint32_t)(cap[o * RK + tid] > 0) << o;
+      mo |= (uint32_t)(cap[tid * RK + o] > 0) << o;
+    }
+    nin[tid] = mi;
+    nout[tid] = mo;
+  }
+  __syncthreads();
   const uint32_t nsets = 1u << RK;                     // Gray index i in [1, nsets) gives S = i ^ (i >> 1)
   const uint32_t per = (nsets - 1 + kLpThreads - 1) / kLpThreads;
   const uint32_t i0 = 1 + (uint32_t)tid * per;
   const uint32_t i1 = min(nsets, i0 + per);
-  long long best = 0;
+  // the largest ratio num / k is kept as a fraction (cross-multiplied:
+  // num <= 2^56, k <= 16) and rounded up once at the end
+  long long bnum = 0;
+  int bk = 1;
   if (i0 < i1) {
     uint32_t S = i0 ^ (i0 >> 1);
     long long ld = 0, out = 0;
@@ -118,29 +136,24 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
     for (uint32_t i = i0;; ) {
       const int k = __popc(S);
       const long long num = ld - out;
-      if (num > 0) {
-        const long long q = (num + k - 1) / k;
-        best = q > best ? q : best;
+      if (num * bk > bnum * k) {
+        bnum = num;
+        bk = k;
       }
       if (++i >= i1) break;
       const int r = __builtin_ctz(i);                  // the rank that enters or leaves
       const uint32_t T = S ^ (1u << r);
-      long long into_r = 0, from_r = 0;                // cap(S' -> r) and cap(r -> outside T)
-      for (int o = 0; o < RK; ++o) {
-        if (o == r) continue;
-        if ((T >> o) & 1u) into_r += (long long)cap[o * RK + r];
-        else from_r += (long long)cap[r * RK + o];
-      }
-      if ((T >> r) & 1u) {                             // r joins: its edges from the set become internal
-        ld += (long long)base[r];
-        out += from_r - into_r;
-      } else {                                         // r leaves
-        ld -= (long long)base[r];
-        out -= from_r - into_r;
-      }
+      long long into_r = 0, from_r = 0;                // cap(T without r -> r), cap(r -> outside T); cap[r][r] = 0
+      for (uint32_t m = nin[r] & T; m; m &= m - 1) into_r += (long long)cap[__builtin_ctz(m) * RK + r];
+      for (uint32_t m = nout[r] & ~T; m; m &= m - 1) from_r += (long long)cap[r * RK + __builtin_ctz(m)];
+      const long long d = from_r - into_r;
+      const bool joins = (T >> r) & 1u;
+      ld += joins ? (long long)base[r] : -(long long)base[r];
+      out += joins ? d : -d;
       S = T;
     }
   }
+  long long best = bnum > 0 ? (bnum + bk - 1) / bk : 0;
   for (int off = 32; off > 0; off >>= 1) {
     const long long o = __shfl_xor(best, off);
     best = o > best ? o : best;
@@ -160,42 +173,46 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   }
   __syncthreads();
 
-  // ---- 3. maximum flow at lam* (wave 0; one lane per node)
+  // ---- 3. maximum flow at lam* (wave 0; one lane per node).  Lane v keeps
+  // `in` = the set of nodes u with residual capacity u -> v, so one level of
+  // the search is a bit scan; the path's bottleneck travels with the search.
   int exhausted = 0;
   if (wave == 0) {
+    const bool node = lane < V;
+    uint64_t in = 0;
+    if (node)
+      for (int u = 0; u < V; ++u) in |= (uint64_t)(res[u * V + lane] > 0) << u;
     for (int it = 0; it < kLpMaxAugment; ++it) {
       uint64_t seen = 1ull << src, frontier = 1ull << src;
       int parent = -1;
+      long long neck = lane == src ? LLONG_MAX : 0;    // least residual on the path to this node
       while (frontier && !((seen >> snk) & 1ull)) {
-        int p = -1;
-        if (lane < V && !((seen >> lane) & 1ull)) {
-          for (int u = 0; u < V; ++u) {
-            if (((frontier >> u) & 1ull) && res[u * V + lane] > 0) { p = u; break; }
-          }
+        const uint64_t cand = node && !((seen >> lane) & 1ull) ? (in & frontier) : 0;
+        const int p = cand ? __builtin_ctzll(cand) : 0;
+        const long long pn = __shfl(neck, p);
+        if (cand) {
+          parent = p;
+          const long long x = res[p * V + lane];
+          neck = pn < x ? pn : x;
         }
-        const uint64_t found = __builtin_amdgcn_ballot_w64(p >= 0);
-        if (p >= 0) parent = p;
+        const uint64_t found = __builtin_amdgcn_ballot_w64(cand != 0);
         seen |= found;
         frontier = found;
       }
       if (!((seen >> snk) & 1ull)) break;
-      long long bn = -1;
-      for (int v = snk; v != src; ) {                  // uniform walk back to the source
-        const int u = __builtin_amdgcn_readlane(parent, v);
-        const long long x = res[u * V + v];
-        bn = (bn < 0 || x < bn) ? x : bn;
-        v = u;
+      const long long bn = __shfl(neck, snk);
+      uint64_t path = 0;                               // nodes on the path, source excluded
+      for (int v = snk; v != src; v = __builtin_amdgcn_readlane(parent, v)) path |= 1ull << v;
+      lp_wave_sync();
+      if (node && ((path >> lane) & 1ull)) {           // edge parent -> lane carries bn more
+        res[parent * V + lane] -= bn;
+        res[lane * V + parent] += bn;
       }
       lp_wave_sync();
-      if (lane == 0) {
-        for (int v = snk; v != src; ) {
-          const int u = __builtin_amdgcn_readlane(parent, v);
-          res[u * V + v] -= bn;
-          res[v * V + u] += bn;
-          v = u;
-        }
+      if (node) {
+        in = 0;
+        for (int u = 0; u < V; ++u) in |= (uint64_t)(res[u * V + lane] > 0) << u;
       }
-      lp_wave_sync();
       if (it == kLpMaxAugment - 1) exhausted = 1;
     }
   }
@@ -276,10 +293,15 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
   lp_wave_sync();
   const int32_t* src = idx + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
-  for (int i = lane; i < len; i += 64) {
-    const int32_t e = src[i];
-    if ((uint32_t)e < (uint32_t)E) atomicAdd(&cnt[e], 1);
+  int32_t v[kLpSeg / 64];                              // the whole segment in flight at once
+#pragma unroll
+  for (int k = 0; k < kLpSeg / 64; ++k) {
+    const int i = k * 64 + lane;
+    v[k] = i < len ? src[i] : -1;
   }
+#pragma unroll
+  for (int k = 0; k < kLpSeg / 64; ++k)
+    if ((uint32_t)v[k] < (uint32_t)E) atomicAdd(&cnt[v[k]], 1);
   lp_wave_sync();
   int32_t* dst = seg + q * E;
   for (int e = lane; e < E; e += 64) dst[e] = cnt[e];
@@ -292,10 +314,15 @@ __global__ __launch_bounds__(256) void lp_seg_scan_kernel(int32_t* __restrict__ 
   const int64_t l = t / E, e = t - l * E;
   int32_t* p = seg + l * S * E + e;
   int32_t run = 0;
-  for (int64_t s = 0; s < S; ++s) {
-    const int32_t v = p[s * E];
-    p[s * E] = run;
-    run += v;
+  for (int64_t s0 = 0; s0 < S; s0 += 8) {             // eight loads in flight, then their prefix
+    int32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? p[(s0 + k) * E] : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < S) p[(s0 + k) * E] = run;
+      run += v[k];
+    }
   }
 }
 
@@ -313,10 +340,22 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
   int32_t* pid = run + E;                              // replica's physical id, or -1
   int32_t* fx = pid + E;                               // replica's flow (clamped to int32)
   const int32_t* base = seg + q * E;
-  for (int e = lane; e < E; e += 64) {
-    run[e] = base[e];
-    pid[e] = -1;
-    fx[e] = 0;
+  for (int e0 = 0; e0 < E; e0 += 256) {                // four loads in flight per lane
+    int32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k * 64 + lane;
+      v[k] = e < E ? base[e] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e0 + k * 64 + lane;
+      if (e < E) {
+        run[e] = v[k];
+        pid[e] = -1;
+        fx[e] = 0;
+      }
+    }
   }
   lp_wave_sync();
   const int32_t* rl = rep + l * RKR;
@@ -336,17 +375,17 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
   int32_t* dst = out + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
   const uint64_t below = (1ull << lane) - 1;
-  for (int r0 = 0; r0 < len; r0 += 256) {
-    int32_t v[4];
+  int32_t v[kLpSeg / 64];                              // the whole segment in flight at once
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = r0 + k * 64 + lane;
-      v[k] = i < len ? src[i] : -1;
-    }
+  for (int k = 0; k < kLpSeg / 64; ++k) {
+    const int i = k * 64 + lane;
+    v[k] = i < len ? src[i] : -1;
+  }
+  {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = r0 + k * 64 + lane;
-      if (r0 + k * 64 >= len) break;                   // uniform
+    for (int k = 0; k < kLpSeg / 64; ++k) {
+      const int i = k * 64 + lane;
+      if (k * 64 >= len) break;                        // uniform
       const int32_t e = v[k];
       const bool valid = i < len && (uint32_t)e < (uint32_t)E && !bad;
       uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
