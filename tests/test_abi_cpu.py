@@ -228,3 +228,29 @@ def test_lp_redirect_validation(lib):
         args[pos] = bad
         assert lib.eplb_lp_redirect(*args) == code, (pos, bad)
     assert lib.eplb_lp_redirect(None, 0, 16384, 8, 256, None, None, 8, 2, None, 0, None, None) == 0
+
+
+def _cc(src, out, extra=(), libs=()):
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib_dir = os.path.dirname(LIB)
+    cmd = [cc, *extra, "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+           "-L", lib_dir, "-leplb", f"-Wl,-rpath,{lib_dir}", *libs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out
+
+
+def test_header_is_c99_and_every_entry_point_links(tmp_path):
+    """The boundary from plain C: eplb.h compiles under ISO C99 -pedantic,
+    every declared function links against libeplb.so, and the host-only
+    calls answer (no GPU touched)."""
+    import subprocess
+    exe = _cc(os.path.join(ROOT, "tests", "c", "abi_host.c"), str(tmp_path / "abi_host"), ("-std=c99", "-pedantic"))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "abi_host ok: 12 entry points" in r.stdout
+    assert len(declared_functions()) == 12
