@@ -164,6 +164,11 @@ def main() -> int:
         eevs[i][0].record(stream)
         eplb.load_ema(steps[i % W], E, ema, 4, count, n_invalid)
         eevs[i][1].record(stream)
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        fevs[i][0].record(stream)
+        eplb.ema_redirect(steps[i % W], E, ema, 4, log2phy, logcnt, count, n_invalid, out)
+        fevs[i][1].record(stream)
     rank_load = torch.empty((L, pl.RK), dtype=torch.float64, device=dev)
     imbalance = torch.empty((L,), dtype=torch.float64, device=dev)
     eplb.placement_load(load, phy2log, logcnt, pl.RK, out=(rank_load, imbalance))
@@ -184,6 +189,7 @@ def main() -> int:
         e[1].record(stream)
     torch.cuda.synchronize()
     ema_ms = [e[0].elapsed_time(e[1]) for e in eevs]
+    ema_red_ms = [e[0].elapsed_time(e[1]) for e in fevs]
     rearrange_us = [e[0].elapsed_time(e[1]) * 1e3 for e in revs]
     moves = plan[3].sum(dim=0).cpu().tolist()
     assert int(plan[4].abs().sum()) == 0
@@ -277,6 +283,8 @@ def main() -> int:
             "ms": round(avg(ema_ms), 4),
             "GBps": round(hist_bytes / (avg(ema_ms) * 1e-3) / 1e9, 1),
             "frac_of_peak": round(hist_bytes / (avg(ema_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fused_with_redirect_ms": round(avg(ema_red_ms), 4),
+            "fused_with_redirect_GBps": round(redir_bytes / (avg(ema_red_ms) * 1e-3) / 1e9, 1),
         },
         "placement_quality": {
             "what": "eplb_placement_load: per-rank load and max/mean of the placement in force, 58 problems",

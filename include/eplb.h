@@ -184,6 +184,21 @@ int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
                       int32_t* count, int32_t shift, int64_t* ema, int64_t* n_invalid, void* stream);
 
 /*
+ * eplb_ema_redirect -- eplb_load_ema and eplb_redirect in one pass over idx.
+ *
+ * Follows the same passages as the two calls it combines.  Counts the step's
+ * ids into `count`, folds them into `ema` (ema <- ema - (ema >> shift) +
+ * count), and writes the physical id of every (token, k) under the placement
+ * (log2phy, logcnt) given.  Every output is identical to calling
+ * eplb_load_ema then eplb_redirect with the same arguments; each id is read
+ * once instead of twice.  Arguments, layouts, errors: as for those two calls
+ * (out must not overlap idx).
+ */
+int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* count,
+                          int32_t shift, int64_t* ema, int64_t* n_invalid, const int32_t* log2phy,
+                          const int32_t* logcnt, int32_t X, int32_t* out, void* stream);
+
+/*
  * eplb_placement_load -- load of every rank under a placement, and max / mean.
  *
  * Follows: the glossary of Part 2 (each copy of an expert takes an equal

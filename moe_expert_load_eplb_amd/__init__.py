@@ -33,7 +33,7 @@ EPLB_S_BAD_MAP = 18
 EPLB_S_BAD_TOPOLOGY = 19
 
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
-           "eplb_load_ema", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
+           "eplb_load_ema", "eplb_ema_redirect", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
            "eplb_lp_redirect_workspace_bytes", "eplb_status_string",
            "eplb_rebalance_lds_bytes")
 
@@ -58,6 +58,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_hist_redirect.restype = i32
     lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
     lib.eplb_load_ema.restype = i32
+    lib.eplb_ema_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p, p, i32, p, p]
+    lib.eplb_ema_redirect.restype = i32
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
     lib.eplb_placement_load.restype = i32
     lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
@@ -249,6 +251,36 @@ def load_ema(idx: torch.Tensor, E: int, ema: torch.Tensor, shift: int,
                            _stream(dev))
     _check(rc, "eplb_load_ema")
     return ema, count, n_invalid
+
+
+def ema_redirect(idx: torch.Tensor, E: int, ema: torch.Tensor, shift: int, log2phy: torch.Tensor,
+                 logcnt: torch.Tensor, count: torch.Tensor | None = None, n_invalid: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None):
+    """load_ema and redirect in one pass over idx (the placement given is the
+    one in force for this step).  Returns (ema, count, n_invalid, out)."""
+    if idx.dim() != 3 or log2phy.dim() != 3 or logcnt.dim() != 2:
+        raise ValueError("idx [L, T, K], log2phy [L, E, X], logcnt [L, E] expected")
+    L, T, K = idx.shape
+    if tuple(ema.shape) != (L, E):
+        raise ValueError(f"ema must be [{L}, {E}], got {tuple(ema.shape)}")
+    if tuple(log2phy.shape[:2]) != (L, E) or tuple(logcnt.shape) != (L, E):
+        raise ValueError("log2phy / logcnt do not match idx's layers and E")
+    X = log2phy.shape[2]
+    dev = idx.device
+    if count is None:
+        count = torch.empty((L, E), dtype=torch.int32, device=dev)
+    if n_invalid is None:
+        n_invalid = torch.empty((L,), dtype=torch.int64, device=dev)
+    if out is None:
+        out = torch.empty_like(idx)
+    if tuple(count.shape) != (L, E) or tuple(n_invalid.shape) != (L,) or out.shape != idx.shape:
+        raise ValueError("count [L, E], n_invalid [L], out like idx expected")
+    rc = lib.eplb_ema_redirect(_dev(idx, torch.int32, "idx"), L, T, K, E, _dev(count, torch.int32, "count"),
+                               int(shift), _dev(ema, torch.int64, "ema"), _dev(n_invalid, torch.int64, "n_invalid"),
+                               _dev(log2phy, torch.int32, "log2phy"), _dev(logcnt, torch.int32, "logcnt"), X,
+                               _dev(out, torch.int32, "out"), _stream(dev))
+    _check(rc, "eplb_ema_redirect")
+    return ema, count, n_invalid, out
 
 
 def placement_load(load: torch.Tensor, phy2log: torch.Tensor, logcnt: torch.Tensor, RK: int,

@@ -87,6 +87,21 @@ int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
 
+int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* count,
+                          int32_t shift, int64_t* ema, int64_t* n_invalid, const int32_t* log2phy,
+                          const int32_t* logcnt, int32_t X, int32_t* out, void* stream) {
+  int32_t rc = check_stream_args(idx, L, T, K, E);
+  if (rc != EPLB_OK) return rc;
+  if (shift < 0 || shift > 62 || X < 1) return EPLB_E_ARG;
+  if (X > kMaxX) return EPLB_E_LIMIT;
+  if (L > 0 && (count == nullptr || ema == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
+  if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
+  if (L > 0 && T > 0 && (const void*)out == (const void*)idx) return EPLB_E_ARG;
+  hipError_t err = launch_ema_redirect(idx, L, T, K, E, count, shift, ema, n_invalid, log2phy, logcnt, X, out,
+                                       (hipStream_t)stream);
+  return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
 int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
                             int64_t B, int32_t E, int32_t P, int32_t RK,
                             double* rank_load, double* imbalance, void* stream) {

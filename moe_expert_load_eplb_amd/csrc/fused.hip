@@ -3,7 +3,7 @@
 // placement in force, so each id is read from HBM once: 4 bytes read and 4
 // written per id instead of 4 + 4 + 4 for the two passes.
 //
-// It is the histogram of eplb_load_hist and the redirect of eplb_redirect
+// It is the histogram of eplb_load_hist (or eplb_load_ema) and the redirect of eplb_redirect
 // (glossary of Part 2 of the EPLB README translation, «DualPipe и EPLB»,
 // ai.flicky.cc: the load of an expert is the tokens routed to it; an expert
 // with two copies gives each about half), done in the order a serving loop
@@ -114,13 +114,13 @@ __global__ __launch_bounds__(kStreamThreads) void hist_redirect_kernel(
 
 }  // namespace
 
-hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
-                                int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
-                                const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
-                                hipStream_t stream) {
-  if (L == 0) return hipSuccess;
+namespace {
+
+// Clear `slot` and n_invalid, then count and redirect every id in one pass.
+hipError_t launch_count_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* slot,
+                                 int64_t* n_invalid, const int32_t* log2phy, const int32_t* logcnt, int32_t X,
+                                 int32_t* out, hipStream_t stream) {
   const int64_t LE = L * (int64_t)E;
-  int32_t* slot = ring + (step % W) * LE;
   hipError_t err = launch_hist_clear(slot, LE, n_invalid, L, stream);
   if (err != hipSuccess) return err;
   const int64_t per_layer = T * (int64_t)K;
@@ -143,9 +143,31 @@ hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_
       hist_redirect_kernel<false><<<(unsigned)blocks, kStreamThreads, lds, stream>>>(
           idx, sp, kdiv, E, X, copies, log2phy, logcnt, out, slot, n_invalid);
     err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
+  return err;
+}
+
+}  // namespace
+
+hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
+                                int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
+                                const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,
+                                hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  const int64_t LE = L * (int64_t)E;
+  hipError_t err = launch_count_redirect(idx, L, T, K, E, ring + (step % W) * LE, n_invalid, log2phy, logcnt, X,
+                                         out, stream);
+  if (err != hipSuccess) return err;
   return launch_window_sum(ring, LE, W, load, stream);
+}
+
+hipError_t launch_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* count,
+                               int32_t shift, int64_t* ema, int64_t* n_invalid, const int32_t* log2phy,
+                               const int32_t* logcnt, int32_t X, int32_t* out, hipStream_t stream) {
+  if (L == 0) return hipSuccess;
+  hipError_t err = launch_count_redirect(idx, L, T, K, E, count, n_invalid, log2phy, logcnt, X, out, stream);
+  if (err != hipSuccess) return err;
+  return launch_ema_update(count, L * (int64_t)E, shift, ema, stream);
 }
 
 }  // namespace eplb

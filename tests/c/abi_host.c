@@ -13,7 +13,7 @@ int main(void) {
   const any_fn fns[] = {
       (any_fn)&eplb_load_hist,     (any_fn)&eplb_rebalance,
       (any_fn)&eplb_redirect,      (any_fn)&eplb_hist_redirect,
-      (any_fn)&eplb_load_ema,      (any_fn)&eplb_placement_load,
+      (any_fn)&eplb_load_ema,      (any_fn)&eplb_ema_redirect,  (any_fn)&eplb_placement_load,
       (any_fn)&eplb_rearrange,     (any_fn)&eplb_lp_solve,
       (any_fn)&eplb_lp_redirect,   (any_fn)&eplb_lp_redirect_workspace_bytes,
       (any_fn)&eplb_status_string, (any_fn)&eplb_rebalance_lds_bytes,

@@ -40,6 +40,7 @@ def lib():
     lib.eplb_hist_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, i64, p, p, p, p, i32, p, p]
     lib.eplb_load_ema.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p]
     lib.eplb_placement_load.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p]
+    lib.eplb_ema_redirect.argtypes = [p, i64, i64, i32, i32, p, i32, p, p, p, p, i32, p, p]
     lib.eplb_rearrange.argtypes = [p, p, p, i64, i32, i32, i32, i32, i32, p, p, p, p, p, p]
     lib.eplb_lp_solve.argtypes = [p, p, p, i64, i32, i32, i32, p, p, p, p, p]
     lib.eplb_lp_redirect.argtypes = [p, i64, i64, i32, i32, p, p, i32, i32, p, i64, p, p]
@@ -55,7 +56,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
-                          "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
+                          "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect", "eplb_ema_redirect",
                           "eplb_lp_redirect_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
@@ -252,5 +253,16 @@ def test_header_is_c99_and_every_entry_point_links(tmp_path):
     exe = _cc(os.path.join(ROOT, "tests", "c", "abi_host.c"), str(tmp_path / "abi_host"), ("-std=c99", "-pedantic"))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
-    assert "abi_host ok: 12 entry points" in r.stdout
-    assert len(declared_functions()) == 12
+    assert "abi_host ok: 13 entry points" in r.stdout
+    assert len(declared_functions()) == 13
+
+
+def test_ema_redirect_validation(lib):
+    F = [FAKE + 64 * i for i in range(8)]
+    good = [F[0], 2, 10, 8, 256, F[1], 4, F[2], F[3], F[4], F[5], 9, F[6], None]
+    for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (6, -1, 1), (6, 63, 1),
+                           (11, 0, 1), (11, 70000, 5), (0, None, 1), (5, None, 1), (7, None, 1), (8, None, 1),
+                           (9, None, 1), (10, None, 1), (12, None, 1), (12, F[0], 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_ema_redirect(*args) == code, (pos, bad)

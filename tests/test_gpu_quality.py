@@ -241,3 +241,52 @@ def test_ema_full_size():
         assert_same(f"step {s} counts", host(cnt).astype(np.int64), c)
         assert int(host(bad).sum()) == 0 and int(invl.sum()) == 0
         assert_same(f"step {s} ema", host(ema), ema_ref)
+
+
+# ---------------------------------------------------------------- moving average + redirect in one pass
+
+@pytest.mark.parametrize("L,T,K,E,shift", [(3, 20001, 3, 16, 2), (2, 7, 1, 5, 0), (5, 4097, 8, 256, 4),
+                                           (2, 70000, 5, 1, 7), (1, 33333, 2, 4096, 9)])
+def test_ema_redirect_ragged(L, T, K, E, shift):
+    """Counts, moving average, invalid ids and redirected ids of the fused
+    pass against the oracle: ragged tails, several workgroups per layer,
+    out-of-range ids and counts."""
+    rng = np.random.default_rng(L * T + K + shift)
+    idx_h = rng.integers(-3, E + 3, size=(L, T, K)).astype(np.int32)
+    X = 4
+    logcnt = rng.integers(-1, X + 2, size=(L, E)).astype(np.int32)
+    log2phy = rng.integers(0, 1000, size=(L, E, X)).astype(np.int32)
+    ema0 = rng.integers(0, 1 << 30, size=(L, E)).astype(np.int64)
+    ema = gpu(ema0)
+    note(f"ema_redirect L={L} T={T} K={K} E={E} shift={shift}")
+    _, cnt, bad, out = eplb.ema_redirect(gpu(idx_h), E, ema, shift, gpu(log2phy), gpu(logcnt))
+    torch.cuda.synchronize()
+    c, invl = ora.load_hist(idx_h, E)
+    assert_same("count", host(cnt).astype(np.int64), c)
+    assert_same("invalid", host(bad), invl)
+    assert_same("ema", host(ema), ora.ema_update(ema0, c, shift).reshape(L, E))
+    assert_same("redirect", host(out), ora.redirect(idx_h, log2phy, logcnt))
+
+
+def test_ema_redirect_full_size():
+    """One step of the streaming workload (58 x 2^20 x 8 ids) with its
+    placement: identical to eplb_load_ema followed by eplb_redirect, and to
+    the oracle on sampled layers."""
+    work = wl.STREAM_1M
+    pl = work.placement
+    L, E = work.layers, pl.E
+    idx = wl.routing_step_device(work, 0, DEV)
+    ema_a = torch.zeros((L, E), dtype=torch.int64, device=DEV)
+    _, cnt_a, bad_a = eplb.load_ema(idx, E, ema_a, 4)
+    placement = eplb.rebalance(ema_a, pl.P, pl.G, pl.N, pl.RK)
+    out_a = eplb.redirect(idx, placement[1], placement[2])
+    ema_b = torch.zeros((L, E), dtype=torch.int64, device=DEV)
+    _, cnt_b, bad_b, out_b = eplb.ema_redirect(idx, E, ema_b, 4, placement[1], placement[2])
+    torch.cuda.synchronize()
+    for name, a, b in (("ema", ema_a, ema_b), ("count", cnt_a, cnt_b), ("invalid", bad_a, bad_b), ("out", out_a, out_b)):
+        assert bool(torch.equal(a, b)), f"{name}: fused differs from the two separate calls"
+    idx_h = host(idx[[0, 57]])
+    ref = ora.redirect(idx_h, host(placement[1][[0, 57]]), host(placement[2][[0, 57]]))
+    assert_same("sampled layers", host(out_b[[0, 57]]), ref)
+    c, _ = ora.load_hist(idx_h, E)
+    assert_same("sampled counts", host(cnt_b[[0, 57]]).astype(np.int64), c)
