@@ -281,7 +281,7 @@ __device__ void pack_sorted(KeyOf key_of, int n, int m, int cap, int32_t* res) {
 }
 
 // The same packing with each pack in ONE 64-bit word, sum << 16 | pack << 8 |
-// items, for sums below 2^48, at most 256 packs and at most 255 items per
+// items, for sums below 2^48 - 1, at most 256 packs and at most 255 items per
 // pack; a full pack is all ones.  Words of different packs differ in the pack
 // bits, so one unsigned compare orders packs by (sum, index), and one add of
 // a pre-shifted key (key_of(t) = key << 16 | 1) both adds an item and
@@ -289,8 +289,84 @@ __device__ void pack_sorted(KeyOf key_of, int n, int m, int cap, int32_t* res) {
 // wavefront issues about one instruction per four cycles, so the step's
 // instruction count is its latency; this form has about half the
 // instructions of the general one.  res[t] = pack * cap + arrival position.
+__device__ __forceinline__ u64 shfl64(u64 x, int src) {
+  const int lo = __shfl((int)(uint32_t)x, src);
+  const int hi = __shfl((int)(uint32_t)(x >> 32), src);
+  return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// pack_words for 16 to 64 packs (one register), with runs of items placed
+// at once.  The packs' words are sorted and all distinct (a full or absent
+// pack is a sentinel: all-ones sum and its pack bits, above every real word;
+// real sums stay below 2^48 - 1).  Item j+s goes to the s-th lightest pack
+// exactly while s is below q_t for every earlier t of the run, q_t being the
+// number of packs lighter than the t-th pack after it takes item j+t (the
+// packs are sorted, so "the s-th pack is lighter" is "s < q_t").  Every lane
+// s tries item j+s at once: q_s by a binary search over the sorted words,
+// the prefix minimum of q over the lanes before s, and the run ends at the
+// first lane that fails.  Its packs are then re-ranked: a run pack t lands at
+// (q_t - run) + (run packs now below it), any other pack i at (i - run) + (run
+// packs now below it).  The result is the sequential greedy's, item for item.
+template <class KeyOf>
+__device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+  constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
+  const int lane = lane_id();
+  u64 w = lane < m ? ((u64)lane << 8) : (kSent | ((u64)lane << 8) | 0xffull);
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int tn = n - t0 < 64 ? n - t0 : 64;
+    const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
+    int rec = 0;                                   // lane l: record of item t0 + l
+    for (int j = 0; j < tn; ) {
+      const int it = j + lane;                     // this lane's candidate item
+      const u64 k = shfl64(kk, it & 63);
+      const bool real = w < kSent;
+      u64 us = w + k;
+      if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
+      int lo = 0;                                  // packs below us
+#pragma unroll
+      for (int st = 32; st > 0; st >>= 1) lo += shfl64(w, lo + st - 1) < us ? st : 0;
+      const int q = rdl64(w, 63) < us ? 64 : lo;
+      int incl = q;                                // prefix minimum of q
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        incl = lane >= off && o < incl ? o : incl;
+      }
+      const int before = __shfl_up(incl, 1);      // every lane active: bpermute reads 0 from inactive ones
+      const int pm = lane == 0 ? 64 : before;
+      const u64 vm = __builtin_amdgcn_ballot_w64(it < tn && real && lane < pm);
+      const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);      // lane 0 is always valid
+      const int r = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
+      const int rr = __shfl(r, (lane - j) & 63);
+      rec = (lane >= j && lane < j + mb) ? rr : rec;
+      const u64 nv = lane < mb ? us : w;
+      int c = 0;                                   // run packs now below this lane's word
+      for (int t = 0; t < mb; t += 4) {            // four reads in flight per round
+        const u64 a0 = rdl64(us, t);
+        const u64 a1 = rdl64(us, t + 1 < 64 ? t + 1 : 63);
+        const u64 a2 = rdl64(us, t + 2 < 64 ? t + 2 : 63);
+        const u64 a3 = rdl64(us, t + 3 < 64 ? t + 3 : 63);
+        c += (a0 < nv ? 1 : 0) + (t + 1 < mb && a1 < nv ? 1 : 0) + (t + 2 < mb && a2 < nv ? 1 : 0) +
+             (t + 3 < mb && a3 < nv ? 1 : 0);
+      }
+      const int pos = ((lane < mb ? q - mb : lane - mb) + c) << 2;
+      const int nlo = __builtin_amdgcn_ds_permute(pos, (int)(uint32_t)nv);
+      const int nhi = __builtin_amdgcn_ds_permute(pos, (int)(uint32_t)(nv >> 32));
+      w = ((u64)(uint32_t)nhi << 32) | (uint32_t)nlo;
+      j += mb;
+    }
+    if (lane < tn) res[t0 + lane] = rec;
+  }
+}
+
 template <int K, class KeyOf>
 __device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+  if constexpr (K == 1) {
+    if (m >= 16) {
+      pack_words_wide(key_of, n, m, cap, res);
+      return;
+    }
+  }
   const int lane = lane_id();
   u64 w[K];
 #pragma unroll
@@ -520,7 +596,7 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   if (lane == 0) {
     if (ovf || (total >> 127) != 0) s.flags[0] = EPLB_S_OVERFLOW;
     // key width for step 3: one word per pack, 64-bit sums, or 128-bit sums
-    s.nflag[n] = (total >> 48) == 0 && p.RKn <= 256 && p.ppr <= 255 ? 2 : ((u64)(total >> 64) == 0 ? 1 : 0);
+    s.nflag[n] = total < (((u128)1 << 48) - 1) && p.RKn <= 256 && p.ppr <= 255 ? 2 : ((u64)(total >> 64) == 0 ? 1 : 0);
   }
 #pragma unroll
   for (int r = 0; r < K; ++r) {
@@ -710,7 +786,7 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
       u64 tot = 0;
       for (int g = lane; g < p.Gp; g += 64) tot += s.gsum[g];
       tot = wave_sum64(tot);
-      const bool words = (tot >> 48) == 0 && p.Np <= 256 && p.gpn <= 255;
+      const bool words = tot < (1ull << 48) - 1 && p.Np <= 256 && p.gpn <= 255;
       const u64* gsum = s.gsum;
       const int32_t* gord = s.gord;
       if (words) {

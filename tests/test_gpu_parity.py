@@ -234,6 +234,11 @@ def test_decode_144_global():
     (96, 12, 4, 16, 160),
     (200, 8, 2, 100, 400),    # 50 GPUs per node (>= 64 packs would need >1 pack per lane)
     (130, 2, 1, 130, 260),    # 130 packs: two packs per lane
+    (64, 1, 1, 16, 64),       # 16 packs: the run-at-once packing, smallest case
+    (51, 1, 1, 17, 68),       # 17 packs
+    (100, 3, 2, 64, 256),     # global, 64 packs: runs can span the whole wave
+    (300, 3, 1, 60, 600),     # global, 60 packs of 10
+    (64, 32, 16, 32, 96),     # 32 groups onto 16 nodes: step 1 packs with runs
 ])
 def test_shapes_random(shape):
     E, G, N, RK, P = shape
