@@ -20,9 +20,9 @@
 // scales every per-replica load by D = lcm(replica counts of the node): item
 // keys u * (D / c) and pack sums are exact integers, 64-bit when
 // D * (node load sum) < 2^64, else 128-bit; a node with D * sum >= 2^127
-// marks the problem EPLB_S_OVERFLOW.  D and D / c come from a table of prime
-// powers: D is the product of p over the prime powers p^k that divide some
-// count, and D / c the product over those that do not divide c.
+// marks the problem EPLB_S_OVERFLOW.  D comes from a table of prime powers
+// (the product of p over the prime powers p^k that divide some count), and
+// D / c from an exact long division by c.
 //
 // The two greedy procedures are sequential chains.  Each runs in one
 // wavefront with its state in registers, kept SORTED across the lanes (the
@@ -39,6 +39,8 @@
 // (per-replica load desc); the stable order of the node's physical experts
 // (equal loads in ascending physical index) follows from prefix sums over
 // that order, so no sort is needed.
+#include <climits>
+
 #include "eplb.h"
 #include "eplb_internal.h"
 
@@ -86,6 +88,33 @@ constexpr PrimePowers make_prime_powers() {
 }
 
 __device__ __constant__ PrimePowers kPrimePowers = make_prime_powers();
+
+// The prime powers q = p^k <= 64 with p and the mask of their multiples up
+// to 64 (bit c - 1 set for c = q, 2q, ...): for counts up to 64, "q divides
+// some count" is one AND with the mask of the counts present.
+struct SmallPrimePowers {
+  int n;
+  uint32_t q[32];
+  uint32_t p[32];
+  unsigned long long mult[32];
+};
+constexpr SmallPrimePowers make_small_prime_powers() {
+  SmallPrimePowers t{};
+  for (int q = 2; q <= 64; ++q) {
+    int p = 2;
+    while (q % p != 0) ++p;                  // smallest prime factor
+    int r = q;
+    while (r % p == 0) r /= p;
+    if (r != 1) continue;
+    unsigned long long m = 0;
+    for (int c = q; c <= 64; c += q) m |= 1ull << (c - 1);
+    t.q[t.n] = (uint32_t)q;
+    t.p[t.n] = (uint32_t)p;
+    t.mult[t.n] = m;
+    ++t.n;
+  }
+  return t;
+}
 
 // ---------------------------------------------------------------- lane helpers
 
@@ -160,29 +189,89 @@ __device__ __forceinline__ u128 mul_u128_u64(u128 a, u64 b, bool& ovf) {
   return r;
 }
 
-__device__ __forceinline__ u64 wave_sum64(u64 v) {
-  for (int off = 32; off > 0; off >>= 1) v += (u64)__shfl_xor((unsigned long long)v, off);
+// Wave-wide scans and reductions on DPP moves (no LDS round trips): within
+// each row of 16 lanes a Hillis-Steele scan with row_shr 1, 2, 4, 8, then
+// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the
+// first two rows' total into rows 2 and 3 (row_bcast:31).  Lanes without a
+// source take `id`, the operation's identity.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp(int id, int x) {
+  return __builtin_amdgcn_update_dpp(id, x, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ u64 dpp64(u64 id, u64 x) {
+  const int lo = dpp<kCtrl, kRowMask>((int)(uint32_t)id, (int)(uint32_t)x);
+  const int hi = dpp<kCtrl, kRowMask>((int)(uint32_t)(id >> 32), (int)(uint32_t)(x >> 32));
+  return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+template <class T, class Op>
+__device__ __forceinline__ T wave_scan_incl(T v, T id, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    v = op(v, dpp64<0x111>(id, v));
+    v = op(v, dpp64<0x112>(id, v));
+    v = op(v, dpp64<0x114>(id, v));
+    v = op(v, dpp64<0x118>(id, v));
+    v = op(v, dpp64<0x142, 0xA>(id, v));
+    v = op(v, dpp64<0x143, 0xC>(id, v));
+  } else {
+    v = op(v, dpp<0x111>(id, v));
+    v = op(v, dpp<0x112>(id, v));
+    v = op(v, dpp<0x114>(id, v));
+    v = op(v, dpp<0x118>(id, v));
+    v = op(v, dpp<0x142, 0xA>(id, v));
+    v = op(v, dpp<0x143, 0xC>(id, v));
+  }
   return v;
+}
+// lane i <- lane i - 1, lane 0 <- id
+__device__ __forceinline__ int shr1_or(int id, int x) { return dpp<0x138>(id, x); }
+__device__ __forceinline__ u64 shr1_or64(u64 id, u64 x) { return dpp64<0x138>(id, x); }
+
+// D / c for a count c in [1, 2^14], D of `digits` 32-bit digits: long
+// division digit by digit.  Each partial numerator r * 2^32 + digit is below
+// c * 2^32 <= 2^46, exact as a double; its product with the correctly rounded
+// 1 / c is within 2^-20 of the true quotient (below 2^32), so truncating it
+// gives the quotient or one less, and the remainder check fixes the latter.
+__device__ __forceinline__ u128 div_by_count(u128 D, int digits, uint32_t c) {
+  const double rc = 1.0 / (double)c;
+  u128 q = 0;
+  u64 r = 0;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    if (k >= digits) continue;
+    const u64 num = (r << 32) | (uint32_t)(D >> (32 * k));
+    u64 qk = (u64)((double)num * rc);
+    int64_t rem = (int64_t)(num - qk * c);
+    if (rem < 0) {
+      qk -= 1;
+      rem += c;
+    } else if (rem >= (int64_t)c) {
+      qk += 1;
+      rem -= c;
+    }
+    q = (q << 32) | qk;
+    r = (u64)rem;
+  }
+  return q;
+}
+
+__device__ __forceinline__ u64 wave_sum64(u64 v) {
+  return rdl64(wave_scan_incl<u64>(v, 0ull, [](u64 a, u64 b) { return a + b; }), 63);
+}
+__device__ __forceinline__ u64 wave_or64(u64 v) {
+  return rdl64(wave_scan_incl<u64>(v, 0ull, [](u64 a, u64 b) { return a | b; }), 63);
 }
 __device__ __forceinline__ int wave_max(int v) {
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+  return rdl(wave_scan_incl<int>(v, INT_MIN, [](int a, int b) { return a > b ? a : b; }), 63);
 }
 __device__ __forceinline__ int wave_incl_sum(int v) {
-  const int lane = lane_id();
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
+  return wave_scan_incl<int>(v, 0, [](int a, int b) { return a + b; });
 }
 __device__ __forceinline__ int wave_incl_max(int v) {
-  const int lane = lane_id();
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v = max(v, o);
-  }
-  return v;
+  return wave_scan_incl<int>(v, INT_MIN, [](int a, int b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int wave_incl_min(int v) {
+  return wave_scan_incl<int>(v, INT_MAX, [](int a, int b) { return a < b ? a : b; });
 }
 
 // ---------------------------------------------------------------- greedy packing
@@ -295,23 +384,32 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
   return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// pack_words for 16 to 64 packs (one register), with runs of items placed
+// pack_words for up to 64 packs (one register), with runs of items placed
 // at once.  The packs' words are sorted and all distinct (a full or absent
 // pack is a sentinel: all-ones sum and its pack bits, above every real word;
 // real sums stay below 2^48 - 1).  Item j+s goes to the s-th lightest pack
 // exactly while s is below q_t for every earlier t of the run, q_t being the
 // number of packs lighter than the t-th pack after it takes item j+t (the
 // packs are sorted, so "the s-th pack is lighter" is "s < q_t").  Every lane
-// s tries item j+s at once: q_s by a binary search over the sorted words,
-// the prefix minimum of q over the lanes before s, and the run ends at the
-// first lane that fails.  Its packs are then re-ranked: a run pack t lands at
-// (q_t - run) + (run packs now below it), any other pack i at (i - run) + (run
-// packs now below it).  The result is the sequential greedy's, item for item.
+// s tries item j+s at once: q_s by a two-level search of the sorted words in
+// LDS (every 8th word, then 8 words), the prefix minimum of q over the lanes
+// before s (DPP), and the run ends at the first lane that fails.  Its packs
+// are then re-ranked: a run pack t lands at (q_t - run) + (run packs now
+// below it), any other pack i at (i - run) + (run packs now below it), and
+// each lane writes its word to its new position in LDS.  The result is the
+// sequential greedy's, item for item.  scr: 128 words of this wave's LDS
+// (16-byte aligned): the sorted words, then the run's updated words.
+constexpr int kWideMinPacks = 17;      // from here on the words are searched in LDS
+
 template <class KeyOf>
-__device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+__device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* res, u64* scr) {
   constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
   const int lane = lane_id();
+  u64* sw = scr;                                   // [64] words by position
+  u64* su = scr + 64;                              // [64] updated word of each lane's pack
   u64 w = lane < m ? ((u64)lane << 8) : (kSent | ((u64)lane << 8) | 0xffull);
+  sw[lane] = w;
+  wave_lds_sync();
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
@@ -320,50 +418,136 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
       const int it = j + lane;                     // this lane's candidate item
       const u64 k = shfl64(kk, it & 63);
       const bool real = w < kSent;
-      u64 us = w + k;
-      if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
-      int lo = 0;                                  // packs below us
-#pragma unroll
-      for (int st = 32; st > 0; st >>= 1) lo += shfl64(w, lo + st - 1) < us ? st : 0;
-      const int q = rdl64(w, 63) < us ? 64 : lo;
-      int incl = q;                                // prefix minimum of q
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        incl = lane >= off && o < incl ? o : incl;
-      }
-      const int before = __shfl_up(incl, 1);      // every lane active: bpermute reads 0 from inactive ones
-      const int pm = lane == 0 ? 64 : before;
-      const u64 vm = __builtin_amdgcn_ballot_w64(it < tn && real && lane < pm);
-      const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);      // lane 0 is always valid
       const int r = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
       const int rr = __shfl(r, (lane - j) & 63);
+      u64 us = w + k;
+      if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
+      su[lane] = us;
+      int b = 0;                                   // groups of 8 words wholly below us
+#pragma unroll
+      for (int g = 0; g < 8; ++g) b += sw[8 * g + 7] < us ? 1 : 0;
+      const ulonglong2* f = (const ulonglong2*)(sw + 8 * (b < 8 ? b : 7));
+      const ulonglong2 f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
+      const int fine = (f0.x < us) + (f0.y < us) + (f1.x < us) + (f1.y < us) + (f2.x < us) + (f2.y < us) +
+                       (f3.x < us) + (f3.y < us);
+      const int q = b == 8 ? 64 : 8 * b + fine;    // words below us
+      const int pm = shr1_or(64, wave_incl_min(q));   // minimum of q over the lanes before
+      const u64 vm = __builtin_amdgcn_ballot_w64(it < tn && real && lane < pm);
+      const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);      // lane 0 is always valid
       rec = (lane >= j && lane < j + mb) ? rr : rec;
       const u64 nv = lane < mb ? us : w;
+      wave_lds_sync();
       int c = 0;                                   // run packs now below this lane's word
-      for (int t = 0; t < mb; t += 4) {            // four reads in flight per round
-        const u64 a0 = rdl64(us, t);
-        const u64 a1 = rdl64(us, t + 1 < 64 ? t + 1 : 63);
-        const u64 a2 = rdl64(us, t + 2 < 64 ? t + 2 : 63);
-        const u64 a3 = rdl64(us, t + 3 < 64 ? t + 3 : 63);
-        c += (a0 < nv ? 1 : 0) + (t + 1 < mb && a1 < nv ? 1 : 0) + (t + 2 < mb && a2 < nv ? 1 : 0) +
-             (t + 3 < mb && a3 < nv ? 1 : 0);
+      const ulonglong2* ru = (const ulonglong2*)su;
+      for (int t = 0; t < mb; t += 8) {            // eight words per round, four reads in flight
+        const ulonglong2 a0 = ru[t / 2], a1 = ru[t / 2 + 1], a2 = ru[t / 2 + 2], a3 = ru[t / 2 + 3];
+        c += (a0.x < nv) + (t + 1 < mb && a0.y < nv) + (t + 2 < mb && a1.x < nv) + (t + 3 < mb && a1.y < nv) +
+             (t + 4 < mb && a2.x < nv) + (t + 5 < mb && a2.y < nv) + (t + 6 < mb && a3.x < nv) +
+             (t + 7 < mb && a3.y < nv);
       }
-      const int pos = ((lane < mb ? q - mb : lane - mb) + c) << 2;
-      const int nlo = __builtin_amdgcn_ds_permute(pos, (int)(uint32_t)nv);
-      const int nhi = __builtin_amdgcn_ds_permute(pos, (int)(uint32_t)(nv >> 32));
-      w = ((u64)(uint32_t)nhi << 32) | (uint32_t)nlo;
+      const int pos = (lane < mb ? q - mb : lane - mb) + c;
+      wave_lds_sync();
+      sw[pos] = nv;
+      wave_lds_sync();
+      w = sw[lane];
       j += mb;
     }
     if (lane < tn) res[t0 + lane] = rec;
   }
 }
 
+// The same runs for at most M <= 16 packs, all in registers and DPP moves.
+// The m real packs sit sorted in lanes 0..m-1 (open packs first, then full
+// ones) and lanes m..63 hold absent-pack sentinels above them.  Lane s of a
+// run takes item j+s exactly while its own word is below the updated word of
+// every earlier lane (that is, s < q_t for every t < s), so the run is found
+// from the exclusive prefix minimum of the updated words; then the run's
+// updated words and the other packs' words are put back in order by a
+// bitonic sorting network over the first M lanes.  The next run's keys are
+// fetched (ds_bpermute) while the network runs.
+constexpr int kFewMinPacks = 4;        // fewer packs: runs are at most that long, the sequential form is faster
+
+// partner of each lane in a sorting-network stage: lane ^ kX within rows of 16
+template <int kX>
+__device__ __forceinline__ int xlane(int x) {
+  if constexpr (kX == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+  if constexpr (kX == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);        // quad_perm 2,3,0,1
+  if constexpr (kX == 3) return __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);        // quad_perm 3,2,1,0
+  if constexpr (kX == 7) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);       // row_half_mirror
+  if constexpr (kX == 15) return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);      // row_mirror
+  if constexpr (kX == 4) {     // banks 0, 2 take lane + 4 (row_shl:4), banks 1, 3 lane - 4 (row_shr:4)
+    const int t = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);
+    return __builtin_amdgcn_update_dpp(t, x, 0x114, 0xF, 0xA, false);
+  }
+  return x;
+}
+// one compare-exchange stage: the lane whose `kLow` bit is clear keeps the
+// smaller word of the pair (all words distinct)
+template <int kX, int kLow>
+__device__ __forceinline__ u64 cx_stage(u64 x) {
+  const int lo = xlane<kX>((int)(uint32_t)x);
+  const int hi = xlane<kX>((int)(uint32_t)(x >> 32));
+  const u64 px = ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
+  const bool lower = (lane_id() & kLow) == 0;
+  return (lower == (px < x)) ? px : x;
+}
+// ascending sort of the words in each block of M lanes (M = 8 or 16)
+template <int M>
+__device__ __forceinline__ u64 sort_lanes(u64 x) {
+  x = cx_stage<1, 1>(x);
+  x = cx_stage<3, 2>(x);
+  x = cx_stage<1, 1>(x);
+  x = cx_stage<7, 4>(x);
+  x = cx_stage<2, 2>(x);
+  x = cx_stage<1, 1>(x);
+  if constexpr (M == 16) {
+    x = cx_stage<15, 8>(x);
+    x = cx_stage<4, 4>(x);
+    x = cx_stage<2, 2>(x);
+    x = cx_stage<1, 1>(x);
+  }
+  return x;
+}
+
+template <int M, class KeyOf>
+__device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+  constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
+  const int lane = lane_id();
+  u64 w = lane < m ? ((u64)lane << 8) : (kSent | ((u64)lane << 8) | 0xffull);
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int tn = n - t0 < 64 ? n - t0 : 64;
+    const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
+    u64 k = kk;                                    // lane s: key of item j + s
+    for (int j = 0; j < tn; ) {
+      const bool real = w < kSent;
+      u64 us = w + k;
+      if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
+      u64 pmin = us;                               // prefix minimum of us within the first M lanes
+      pmin = min(pmin, dpp64<0x111>(~0ull, pmin));
+      pmin = min(pmin, dpp64<0x112>(~0ull, pmin));
+      pmin = min(pmin, dpp64<0x114>(~0ull, pmin));
+      if constexpr (M == 16) pmin = min(pmin, dpp64<0x118>(~0ull, pmin));
+      const u64 before = shr1_or64(~0ull, pmin);  // over the lanes before this one
+      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < tn && real && w < before);
+      const int mb = __builtin_ctzll(~vm);         // lane 0 is always valid, lane m never
+      if (lane < mb) res[t0 + j + lane] = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
+      j += mb;
+      k = shfl64(kk, (j + lane) & 63);
+      w = sort_lanes<M>(lane < mb ? us : w);
+    }
+  }
+}
+
 template <int K, class KeyOf>
-__device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+__device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res, u64* scr) {
   if constexpr (K == 1) {
-    if (m >= 16) {
-      pack_words_wide(key_of, n, m, cap, res);
+    if (m >= kWideMinPacks) {
+      pack_words_wide(key_of, n, m, cap, res, scr);
+      return;
+    }
+    if (m >= kFewMinPacks) {
+      if (m > 8) pack_words_few<16>(key_of, n, m, cap, res);
+      else pack_words_few<8>(key_of, n, m, cap, res);
       return;
     }
   }
@@ -484,6 +668,7 @@ struct Smem {
   int32_t* gord;   // [Gp]  groups, heaviest first
   int32_t* gres;   // [Gp]  packing result per visiting rank
   int32_t* rep;    // [Np][Rn]
+  u64* pk;         // [nscr][128]  per wave: lane-parallel packing scratch (when packs >= kWideMinPacks)
   int32_t* posaux; // [nscr][3 * En]  per wave: class start, item offset, position of expert
   int32_t* ordr;   // [nscr][Pn]  per wave: item (local expert | rank << 16) in visiting order
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
@@ -506,6 +691,7 @@ __device__ Smem carve(unsigned char* base, const RbPlan& p) {
   s.gord = (int32_t*)(base + p.o_gord);
   s.gres = (int32_t*)(base + p.o_gres);
   s.rep = (int32_t*)(base + p.o_rep);
+  s.pk = (u64*)(base + p.o_pk);
   s.posaux = (int32_t*)(base + p.o_posaux);
   s.ordr = (int32_t*)(base + p.o_ordr);
   s.ores = (int32_t*)(base + p.o_ores);
@@ -565,32 +751,44 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   sum = wave_sum64(sum);
   cmax = wave_max(cmax);
 
-  // D = product of p over the prime powers p^k <= cmax dividing some count;
-  // Q = D / c = product of p over those not dividing c.
+  // D = product of p over the prime powers p^k <= cmax dividing some count
+  // (= lcm of the counts); Q = D / c by exact division.
   u128 D = 1;
-  u128 Q[K];
   bool ovf = false;
-#pragma unroll
-  for (int r = 0; r < K; ++r) Q[r] = 1;
-  for (int t = 0; t < kPrimePowers.count && (int)kPrimePowers.q[t] <= cmax; ++t) {
-    const uint32_t q = kPrimePowers.q[t];
-    const u64 pr = kPrimePowers.p[t];
-    const FastDiv fd{kPrimePowers.mul[t], kPrimePowers.shift[t]};
-    bool div[K];
-    u64 any = 0;
+  if (cmax <= 64) {
+    u64 present = 0;                           // bit c - 1 for each count c on the node
 #pragma unroll
     for (int r = 0; r < K; ++r) {
       const int pos = r * 64 + lane;
-      const uint32_t c = (uint32_t)(ci[r] >> 16);
-      div[r] = pos < En && fastdiv_apply(c, fd) * q == c;
-      any |= ballot(div[r]);
+      if (pos < En) present |= 1ull << ((ci[r] >> 16) - 1);
     }
-    if (any != 0) {
-      D = mul_u128_u64(D, pr, ovf);
+    present = wave_or64(present);
+    constexpr SmallPrimePowers t = make_small_prime_powers();
 #pragma unroll
-      for (int r = 0; r < K; ++r)
-        if (!div[r]) Q[r] = mul_u128_u64(Q[r], pr, ovf);
+    for (int i = 0; i < t.n; ++i) {
+      if ((int)t.q[i] > cmax) break;
+      if ((present & t.mult[i]) != 0) D *= t.p[i];   // lcm(1..64) < 2^93: no overflow
     }
+  } else {
+    for (int t = 0; t < kPrimePowers.count && (int)kPrimePowers.q[t] <= cmax; ++t) {
+      const uint32_t q = kPrimePowers.q[t];
+      const FastDiv fd{kPrimePowers.mul[t], kPrimePowers.shift[t]};
+      u64 any = 0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int pos = r * 64 + lane;
+        const uint32_t c = (uint32_t)(ci[r] >> 16);
+        any |= ballot(pos < En && fastdiv_apply(c, fd) * q == c);
+      }
+      if (any != 0) D = mul_u128_u64(D, kPrimePowers.p[t], ovf);
+    }
+  }
+  const int digits = (uint32_t)(D >> 96) != 0 ? 4 : (uint32_t)(D >> 64) != 0 ? 3 : (uint32_t)(D >> 32) != 0 ? 2 : 1;
+  u128 Q[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const uint32_t c = (uint32_t)(ci[r] >> 16) > 0 ? (uint32_t)(ci[r] >> 16) : 1u;
+    Q[r] = div_by_count(D, digits, c);
   }
   const u128 total = mul_u128_u64(D, sum, ovf);
   if (lane == 0) {
@@ -700,7 +898,7 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
     const u128* kexp = s.kexp + n * En;
     if (width == 2) {
       auto key = [=](int t) { return ((u64)kexp[ordr[t] & 0xffff] << 16) | 1ull; };
-      pack_words<KP>(key, Pn, p.RKn, p.ppr, ores);
+      pack_words<KP>(key, Pn, p.RKn, p.ppr, ores, s.pk + ws * 128);
     } else if (width == 1) {
       auto key = [=](int t, int) { return (u64)kexp[ordr[t] & 0xffff]; };
       pack_sorted<KP, 1>(key, Pn, p.RKn, p.ppr, ores);
@@ -791,8 +989,8 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
       const int32_t* gord = s.gord;
       if (words) {
         auto key = [=](int t) { return (gsum[gord[t]] << 16) | 1ull; };
-        if (p.KN == 1) pack_words<1>(key, p.Gp, p.Np, p.gpn, s.gres);
-        else pack_words<8>(key, p.Gp, p.Np, p.gpn, s.gres);
+        if (p.KN == 1) pack_words<1>(key, p.Gp, p.Np, p.gpn, s.gres, s.pk);
+        else pack_words<8>(key, p.Gp, p.Np, p.gpn, s.gres, s.pk);
       } else {
         auto key = [=](int t, int) { return gsum[gord[t]]; };
         if (p.KN == 1) pack_sorted<1, 1>(key, p.Gp, p.Np, p.gpn, s.gres);
@@ -916,6 +1114,8 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.o_cnt = take(4ll * E, 4);
   p.o_srt = take(4ll * E, 4);
   p.o_rep = take(4ll * Np * rn1, 4);
+  const bool wide = (p.KP == 1 && p.RKn >= kWideMinPacks) || (p.KN == 1 && Np >= kWideMinPacks && p.gpn > 1);
+  p.o_pk = wide ? take(1024ll * nscr, 16) : 0;
   // Two overlaid regions: the loads and step-1 arrays die once the mlog
   // order is built; the per-wave step-3 scratch is used only after that.
   const int64_t base = (off + 15) / 16 * 16;

@@ -239,6 +239,9 @@ def test_decode_144_global():
     (100, 3, 2, 64, 256),     # global, 64 packs: runs can span the whole wave
     (300, 3, 1, 60, 600),     # global, 60 packs of 10
     (64, 32, 16, 32, 96),     # 32 groups onto 16 nodes: step 1 packs with runs
+    (100, 5, 1, 12, 144),     # 12 packs of 12: register runs, three item chunks
+    (45, 3, 1, 9, 90),        # 9 packs
+    (40, 8, 4, 20, 60),       # 5 packs per node, 8 groups onto 4 nodes
 ])
 def test_shapes_random(shape):
     E, G, N, RK, P = shape
