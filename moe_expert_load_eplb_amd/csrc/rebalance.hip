@@ -600,10 +600,20 @@ __device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res, u6
 // on ties) gets a replica and moves to its new place.  As in pack_sorted,
 // position 0 is also kept in scalar registers and the next one is chosen
 // from position 1 read before the update.
+// One compare orders two experts: u_a / c_a before u_b / c_b (index a < b on
+// ties) exactly when (u_a << 9) * c_b + (511 - a) > (u_b << 9) * c_a + (511 - b)
+// (loads <= 2^40, counts < 2^14, indices < 512: below 2^63), so the chain
+// keeps u << 9 and count << 16 | (511 - index) (0 for sentinels).
 // rep[r] = local index | rank << 16 of the r-th replica created.
 template <int K>
 __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep) {
   const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int i = ci[r] & 0xffff;
+    ci[r] = (ci[r] & ~0xffff) | (i < 512 ? 511 - i : 0);
+    u[r] <<= 9;
+  }
   u64 u0 = rdl64(u[0], 0);
   int ci0 = rdl(ci[0], 0);
   for (int r0 = 0; r0 < Rn; r0 += 64) {
@@ -613,26 +623,27 @@ __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep
       const u64 u1 = rdl64(u[0], 1);
       const int ci1 = rdl(ci[0], 1);
       const int c0 = ci0 >> 16;
-      const int i0 = ci0 & 0xffff;
-      rec = push_record(rec, i0 | (c0 << 16));
+      const int t0 = ci0 & 0xffff;
+      rec = push_record(rec, (511 - t0) | (c0 << 16));
       const int nc = c0 + 1;
-      const int nci = (nc << 16) | i0;
+      const int nci = (nc << 16) | t0;
       int q = 0;
 #pragma unroll
       for (int r = 0; r < K; ++r) {
         if (r > 0 && q < 64 * r - 1) break;       // sorted: nothing further comes first
-        const u64 lhs = u[r] * (u64)(uint32_t)nc;             // u_p / c_p  vs  u0 / nc
-        const u64 rhs = u0 * (u64)(uint32_t)(ci[r] >> 16);
-        const bool before = lhs > rhs || (lhs == rhs && (ci[r] & 0xffff) < i0);
-        u64 mask = __builtin_amdgcn_ballot_w64(before);
+        const u64 kp = u[r] * (u64)(uint32_t)nc + (u64)(uint32_t)(ci[r] & 0xffff);
+        const u64 kq = u0 * (u64)(uint32_t)(ci[r] >> 16) + (u64)(uint32_t)t0;
+        u64 mask = __builtin_amdgcn_ballot_w64(kp > kq);
         if (r == 0) mask &= ~1ull;
         q += __popcll(mask);
       }
       if (K == 1 || q < 64) {                     // only register 0 moves
         const u64 ud = shl1_64(u[0]);
         const int cid = shl1(ci[0]);
-        u[0] = lane < q ? ud : (lane == q ? u0 : u[0]);
-        ci[0] = lane < q ? cid : (lane == q ? nci : ci[0]);
+        const u64 uin = lane == q ? u0 : u[0];
+        const int cin = lane == q ? nci : ci[0];
+        u[0] = lane < q ? ud : uin;
+        ci[0] = lane < q ? cid : cin;
       } else {
         u64 ud[K];
         int cid[K];
@@ -650,6 +661,11 @@ __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep
       if (q > 0) { u0 = u1; ci0 = ci1; } else { ci0 = nci; }
     }
     if (lane < tn) rep[r0 + tn - 1 - lane] = rec;
+  }
+#pragma unroll
+  for (int r = 0; r < K; ++r) {              // back to count << 16 | index (sentinels: garbage index)
+    ci[r] = (ci[r] & ~0xffff) | (511 - (ci[r] & 0xffff));
+    u[r] >>= 9;
   }
 }
 
@@ -888,8 +904,16 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
     wave_lds_sync();
     for (int rr = lane; rr < Rn; rr += 64) {   // replicas
       const int cls = rcls[rr];
-      int before = 0;
-      for (int r2 = 0; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
+      int before = 0;                           // earlier replicas of the same class
+      int r2 = 0;
+      for (; r2 + 8 <= rr; r2 += 8) {
+        int a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = rcls[r2 + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) before += a[k] == cls ? 1 : 0;
+      }
+      for (; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
       int size = 1;
       while (cls + size < En && cstart[cls + size] == cls) ++size;
       ordr[coff[cls] + size + before] = rep[rr];   // local index | rank << 16
@@ -1016,17 +1040,31 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
     s.wl[m] = s.w[e];
   }
   __syncthreads();
-  // experts of each node by (load desc, local index asc)
+  // experts of each node by (load desc, local index asc), ranked by counting
+  // over the unique keys load << 9 | (511 - local index) (loads <= 2^40,
+  // local indices < 512); the keys take the place of the logical-order
+  // loads, which are dead once the mlog order is built
+  u64* key = s.w;
+  for (int m = tid; m < p.E; m += NT) {
+    const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
+    key[m] = (s.wl[m] << 9) | (u64)(511 - (m - n * p.En));
+  }
+  __syncthreads();
   for (int m = tid; m < p.E; m += NT) {
     const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
     const int i = m - n * p.En;
-    const u64* wn = s.wl + n * p.En;
-    const u64 wi = wn[i];
+    const u64* kn = key + n * p.En;
+    const u64 ki = kn[i];
     int rank = 0;
-    for (int h = 0; h < p.En; ++h) {
-      const u64 wh = wn[h];
-      rank += (wh > wi || (wh == wi && h < i)) ? 1 : 0;
+    int h = 0;
+    for (; h + 8 <= p.En; h += 8) {            // eight reads in flight
+      u64 a[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] = kn[h + k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rank += a[k] > ki ? 1 : 0;
     }
+    for (; h < p.En; ++h) rank += kn[h] > ki ? 1 : 0;
     s.srt[n * p.En + rank] = i;
   }
   __syncthreads();
