@@ -717,6 +717,17 @@ __device__ Smem carve(unsigned char* base, const RbPlan& p) {
   return s;
 }
 
+// dst[0, n) = -1 by the workgroup: 16-byte stores between a 4-byte head and tail
+__device__ void fill_minus_one(int32_t* dst, int64_t n, int tid, int nt) {
+  const int64_t head0 = (int64_t)(((16u - ((uint32_t)(uintptr_t)dst & 15u)) & 15u) >> 2);
+  const int64_t head = head0 < n ? head0 : n;
+  if (tid < head) dst[tid] = -1;
+  int4* v = (int4*)(dst + head);
+  const int64_t nv = (n - head) >> 2;
+  for (int64_t i = tid; i < nv; i += nt) v[i] = make_int4(-1, -1, -1, -1);
+  for (int64_t i = head + nv * 4 + tid; i < n; i += nt) dst[i] = -1;
+}
+
 __device__ void write_failed(const RbPlan& p, int64_t b, int32_t code, int32_t* phy2log,
                              int32_t* log2phy, int32_t* logcnt, int32_t* status) {
   for (int i = threadIdx.x; i < p.P; i += blockDim.x) phy2log[b * p.P + i] = -1;
@@ -940,13 +951,9 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
       o_l2p[(int64_t)e * p.X + rk] = pid;
     }
   }
-  // counts, and -1 beyond them in log2phy, for the node's experts
-  for (int i = lane; i < En; i += 64) {
-    const int e = m2l[i];
-    const int c = s.cnt[n * En + i];
-    o_cnt[e] = c;
-    for (int k = c; k < p.X; ++k) o_l2p[(int64_t)e * p.X + k] = -1;
-  }
+  // counts of the node's experts (their log2phy rows beyond the count hold
+  // the -1 the kernel wrote first)
+  for (int i = lane; i < En; i += 64) o_cnt[m2l[i]] = s.cnt[n * En + i];
 }
 
 // ---------------------------------------------------------------- kernel
@@ -966,6 +973,10 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
   const int wid = tid >> 6;
   const int NW = NT >> 6;
   const int lane = lane_id();
+
+  // log2phy starts as all -1, written coalesced; the placement overwrites
+  // each expert's first `count` entries after the barriers below
+  fill_minus_one(log2phy + b * (int64_t)p.E * p.X, (int64_t)p.E * p.X, tid, NT);
 
   // ---- loads, range check
   if (tid == 0) s.flags[0] = 0;
