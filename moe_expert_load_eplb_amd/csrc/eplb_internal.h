@@ -131,6 +131,7 @@ struct RbPlan {
   int32_t o_kexp, o_w, o_wl, o_gsum, o_m2l, o_cnt, o_srt;
   int32_t o_gnode, o_gslot, o_gord, o_gres, o_rep, o_pk, o_posaux, o_ordr, o_ores, o_rcls;
   int32_t o_nflag, o_flags;
+  int32_t pk_words;        // per-wave packing scratch, in 8-byte words
   int32_t lds_bytes;
   FastDiv fd_S, fd_En, fd_X;
 };

@@ -384,75 +384,107 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
   return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// pack_words for up to 64 packs (one register), with runs of items placed
-// at once.  The packs' words are sorted and all distinct (a full or absent
-// pack is a sentinel: all-ones sum and its pack bits, above every real word;
-// real sums stay below 2^48 - 1).  Item j+s goes to the s-th lightest pack
-// exactly while s is below q_t for every earlier t of the run, q_t being the
-// number of packs lighter than the t-th pack after it takes item j+t (the
-// packs are sorted, so "the s-th pack is lighter" is "s < q_t").  Every lane
-// s tries item j+s at once: q_s by a two-level search of the sorted words in
-// LDS (every 8th word, then 8 words), the prefix minimum of q over the lanes
-// before s (DPP), and the run ends at the first lane that fails.  Its packs
-// are then re-ranked: a run pack t lands at (q_t - run) + (run packs now
-// below it), any other pack i at (i - run) + (run packs now below it), and
-// each lane writes its word to its new position in LDS.  The result is the
-// sequential greedy's, item for item.  scr: 128 words of this wave's LDS
-// (16-byte aligned): the sorted words, then the run's updated words.
-constexpr int kWideMinPacks = 17;      // from here on the words are searched in LDS
+// pack_words for 17 to 64 * K packs (K <= 4 registers), with runs of items
+// placed at once.  The packs' words are sorted and all distinct (a full or
+// absent pack is a sentinel: all-ones sum and its pack bits, above every
+// real word; real sums stay below 2^48 - 1).  Item j+s goes to the s-th
+// lightest pack exactly while s is below q_t for every earlier t of the run,
+// q_t being the number of packs lighter than the t-th pack after it takes
+// item j+t (the packs are sorted, so "the s-th pack is lighter" is
+// "s < q_t").  Every lane s tries item j+s at once: q_s by a two-level
+// search of the sorted words in LDS (every GS-th word, then GS words), the
+// prefix minimum of q over the lanes before s (DPP), and the run ends at the
+// first lane that fails.  Its packs are then re-ranked: a run pack t lands
+// at (q_t - run) + (run packs now below it, by comparing words), any other
+// pack at position i at (i - run) + (run packs with q_t <= i, from a
+// histogram of the q_t and its prefix sums), and each word is written to its
+// new position in LDS.  The result is the sequential greedy's, item for
+// item.  scr: 64 * K + 64 words and 64 * K + 1 counters of this wave's LDS
+// (16-byte aligned): the sorted words, the run's updated words, the histogram.
+constexpr int kWideMinPacks = 17;      // one register per lane: from here on the words are searched in LDS
 
-template <class KeyOf>
+__device__ __forceinline__ int wave_excl_carry_scan(int v, int& carry) {   // inclusive scan + running carry
+  const int incl = wave_incl_sum(v) + carry;
+  carry = rdl(incl, 63);
+  return incl;
+}
+
+template <int K, class KeyOf>
 __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* res, u64* scr) {
   constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
+  constexpr int NP = 64 * K;                       // positions
+  constexpr int GS = K <= 2 ? 8 : 16;              // words per group of the two-level search
+  constexpr int NG = NP / GS;
   const int lane = lane_id();
-  u64* sw = scr;                                   // [64] words by position
-  u64* su = scr + 64;                              // [64] updated word of each lane's pack
-  u64 w = lane < m ? ((u64)lane << 8) : (kSent | ((u64)lane << 8) | 0xffull);
-  sw[lane] = w;
+  u64* sw = scr;                                   // [NP] words by position
+  u64* su = scr + NP;                              // [64] updated word of each run candidate
+  int* hist = (int*)(scr + NP + 64);               // [NP + 1] run packs by landing point
+  u64 w[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    w[r] = pos < m ? ((u64)pos << 8) : (kSent | ((u64)pos << 8) | 0xffull);
+    sw[pos] = w[r];
+  }
   wave_lds_sync();
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
-    int rec = 0;                                   // lane l: record of item t0 + l
     for (int j = 0; j < tn; ) {
       const int it = j + lane;                     // this lane's candidate item
       const u64 k = shfl64(kk, it & 63);
-      const bool real = w < kSent;
-      const int r = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
-      const int rr = __shfl(r, (lane - j) & 63);
-      u64 us = w + k;
+      const bool real = w[0] < kSent;
+      u64 us = w[0] + k;
       if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
       su[lane] = us;
-      int b = 0;                                   // groups of 8 words wholly below us
 #pragma unroll
-      for (int g = 0; g < 8; ++g) b += sw[8 * g + 7] < us ? 1 : 0;
-      const ulonglong2* f = (const ulonglong2*)(sw + 8 * (b < 8 ? b : 7));
-      const ulonglong2 f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
-      const int fine = (f0.x < us) + (f0.y < us) + (f1.x < us) + (f1.y < us) + (f2.x < us) + (f2.y < us) +
-                       (f3.x < us) + (f3.y < us);
-      const int q = b == 8 ? 64 : 8 * b + fine;    // words below us
-      const int pm = shr1_or(64, wave_incl_min(q));   // minimum of q over the lanes before
+      for (int r = 0; r <= K; ++r)
+        if (r < K || lane == 0) hist[r * 64 + lane] = 0;
+      int b = 0;                                   // groups of GS words wholly below us
+#pragma unroll
+      for (int g = 0; g < NG; ++g) b += sw[GS * g + GS - 1] < us ? 1 : 0;
+      const ulonglong2* f = (const ulonglong2*)(sw + GS * (b < NG ? b : NG - 1));
+      int fine = 0;
+#pragma unroll
+      for (int h = 0; h < GS / 2; ++h) {
+        const ulonglong2 fw = f[h];
+        fine += (fw.x < us ? 1 : 0) + (fw.y < us ? 1 : 0);
+      }
+      const int q = b == NG ? NP : GS * b + fine;  // words below us
+      const int pm = shr1_or(1 << 20, wave_incl_min(q));   // minimum of q over the lanes before
       const u64 vm = __builtin_amdgcn_ballot_w64(it < tn && real && lane < pm);
       const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);      // lane 0 is always valid
-      rec = (lane >= j && lane < j + mb) ? rr : rec;
-      const u64 nv = lane < mb ? us : w;
+      if (lane < mb) res[t0 + j + lane] = (int)((w[0] >> 8) & 0xff) * cap + (int)(w[0] & 0xff);
       wave_lds_sync();
-      int c = 0;                                   // run packs now below this lane's word
+      if (lane < mb) atomicAdd(&hist[q], 1);
+      int crun = 0;                                // run packs now below this lane's updated word
       const ulonglong2* ru = (const ulonglong2*)su;
       for (int t = 0; t < mb; t += 8) {            // eight words per round, four reads in flight
         const ulonglong2 a0 = ru[t / 2], a1 = ru[t / 2 + 1], a2 = ru[t / 2 + 2], a3 = ru[t / 2 + 3];
-        c += (a0.x < nv) + (t + 1 < mb && a0.y < nv) + (t + 2 < mb && a1.x < nv) + (t + 3 < mb && a1.y < nv) +
-             (t + 4 < mb && a2.x < nv) + (t + 5 < mb && a2.y < nv) + (t + 6 < mb && a3.x < nv) +
-             (t + 7 < mb && a3.y < nv);
+        crun += (a0.x < us) + (t + 1 < mb && a0.y < us) + (t + 2 < mb && a1.x < us) + (t + 3 < mb && a1.y < us) +
+                (t + 4 < mb && a2.x < us) + (t + 5 < mb && a2.y < us) + (t + 6 < mb && a3.x < us) +
+                (t + 7 < mb && a3.y < us);
       }
-      const int pos = (lane < mb ? q - mb : lane - mb) + c;
       wave_lds_sync();
-      sw[pos] = nv;
+      int carry = 0;
+      int pos[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int p = r * 64 + lane;
+        const int below = wave_excl_carry_scan(hist[p], carry);   // run packs with q_t <= p
+        pos[r] = (r == 0 && lane < mb) ? q - mb + crun : p - mb + below;
+      }
       wave_lds_sync();
-      w = sw[lane];
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int p = r * 64 + lane;
+        if (p < m) sw[pos[r]] = (r == 0 && lane < mb) ? us : w[r];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int r = 0; r < K; ++r) w[r] = sw[r * 64 + lane];
       j += mb;
     }
-    if (lane < tn) res[t0 + lane] = rec;
   }
 }
 
@@ -540,9 +572,13 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
 
 template <int K, class KeyOf>
 __device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res, u64* scr) {
+  if constexpr (K > 1 && K <= 4) {
+    pack_words_wide<K>(key_of, n, m, cap, res, scr);
+    return;
+  }
   if constexpr (K == 1) {
     if (m >= kWideMinPacks) {
-      pack_words_wide(key_of, n, m, cap, res, scr);
+      pack_words_wide<1>(key_of, n, m, cap, res, scr);
       return;
     }
     if (m >= kFewMinPacks) {
@@ -684,7 +720,7 @@ struct Smem {
   int32_t* gord;   // [Gp]  groups, heaviest first
   int32_t* gres;   // [Gp]  packing result per visiting rank
   int32_t* rep;    // [Np][Rn]
-  u64* pk;         // [nscr][128]  per wave: lane-parallel packing scratch (when packs >= kWideMinPacks)
+  u64* pk;         // [nscr][pk_words]  per wave: lane-parallel packing scratch
   int32_t* posaux; // [nscr][3 * En]  per wave: class start, item offset, position of expert
   int32_t* ordr;   // [nscr][Pn]  per wave: item (local expert | rank << 16) in visiting order
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
@@ -933,7 +969,7 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
     const u128* kexp = s.kexp + n * En;
     if (width == 2) {
       auto key = [=](int t) { return ((u64)kexp[ordr[t] & 0xffff] << 16) | 1ull; };
-      pack_words<KP>(key, Pn, p.RKn, p.ppr, ores, s.pk + ws * 128);
+      pack_words<KP>(key, Pn, p.RKn, p.ppr, ores, s.pk + ws * p.pk_words);
     } else if (width == 1) {
       auto key = [=](int t, int) { return (u64)kexp[ordr[t] & 0xffff]; };
       pack_sorted<KP, 1>(key, Pn, p.RKn, p.ppr, ores);
@@ -1163,8 +1199,14 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.o_cnt = take(4ll * E, 4);
   p.o_srt = take(4ll * E, 4);
   p.o_rep = take(4ll * Np * rn1, 4);
-  const bool wide = (p.KP == 1 && p.RKn >= kWideMinPacks) || (p.KN == 1 && Np >= kWideMinPacks && p.gpn > 1);
-  p.o_pk = wide ? take(1024ll * nscr, 16) : 0;
+  // lane-parallel packing scratch: step 3 in the one-word form with more than
+  // 16 GPUs per node (or more than 64), step 1 with 17 to 64 nodes
+  const bool wide3 = p.KP <= 4 && (p.KP > 1 || p.RKn >= kWideMinPacks);
+  const bool wide1 = p.KN == 1 && Np >= kWideMinPacks && p.gpn > 1;
+  const int kw = wide3 ? p.KP : 1;
+  const int64_t pk_bytes = (8ll * (64 * kw + 64) + 4ll * (64 * kw + 1) + 15) / 16 * 16;
+  p.pk_words = (int32_t)(pk_bytes / 8);
+  p.o_pk = (wide3 || wide1) ? take(pk_bytes * nscr, 16) : 0;
   // Two overlaid regions: the loads and step-1 arrays die once the mlog
   // order is built; the per-wave step-3 scratch is used only after that.
   const int64_t base = (off + 15) / 16 * 16;

@@ -242,6 +242,10 @@ def test_decode_144_global():
     (100, 5, 1, 12, 144),     # 12 packs of 12: register runs, three item chunks
     (45, 3, 1, 9, 90),        # 9 packs
     (40, 8, 4, 20, 60),       # 5 packs per node, 8 groups onto 4 nodes
+    (100, 4, 1, 100, 300),    # 100 packs: runs over two registers of positions
+    (90, 1, 1, 90, 180),
+    (256, 8, 1, 200, 800),    # 200 packs of 4 over four registers
+    (256, 1, 1, 256, 512),    # 256 packs: every pack index of the one-word form
 ])
 def test_shapes_random(shape):
     E, G, N, RK, P = shape
