@@ -106,6 +106,9 @@ def test_rebalance_limits_and_nulls(lib):
     assert lib.eplb_rebalance(FAKE, 1, 16, 24, 4, 2, 8, 5, FAKE, FAKE, FAKE, None, None) == 1
     assert lib.eplb_rebalance(FAKE, 1, 8192, 8192, 1, 1, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == 5
     assert lib.eplb_rebalance_lds_bytes(4096, 8192, 1, 1, 8, 4097) == -5        # LDS budget
+    assert lib.eplb_rebalance_lds_bytes(1024, 1024, 1, 1, 8, 1) == -5          # 1024 experts on one node
+    assert lib.eplb_rebalance_lds_bytes(512, 512, 1, 1, 8, 1) > 0               # 512 fit
+    assert lib.eplb_rebalance_lds_bytes(1024, 1024, 2, 2, 8, 1) > 0             # 512 per node
     # the documented workloads fit
     for args in [(16, 24, 4, 2, 8, 5), (256, 288, 8, 4, 32, 9), (256, 320, 8, 5, 40, 65),
                  (512, 640, 16, 8, 64, 17), (256, 288, 8, 18, 144, 33), (60, 1830, 1, 1, 10, 1771)]:
