@@ -266,21 +266,57 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
 
 // ---------------------------------------------------------------- redirect by the flows
 // Occurrence i (in (token, k) order within the layer) of a replicated expert
-// x goes to x's replica when i < flow, else to the original.  The order is a
-// per-expert running count over the whole layer, so the layer is cut into
-// segments of kLpSeg ids, one wave each: (A) count every segment's ids per
-// expert into the workspace, (B) turn the counts into exclusive prefixes
-// over the segments, (C) each wave starts its experts' counters at those
-// prefixes and walks its segment 64 ids at a time, ranking equal ids among
-// the lanes with one ballot per bit of the expert id (peers share every
-// bit), so the numbering matches a sequential pass exactly.
+// x goes to x's replica when i < flow, else to the original.  Only the
+// replicated experts need that order: each gets a compact number (its slot's
+// rank among the filled slots), and the order is a per-number running count
+// over the whole layer.  The layer is cut into segments of kLpSeg ids, one
+// wave each: (A) count every segment's ids per compact number into the
+// workspace, (B) turn the counts into exclusive prefixes over the segments,
+// (C) each wave starts its counters at those prefixes and walks its segment
+// 64 ids at a time; a group of 64 with no replicated id is copied through,
+// otherwise equal numbers are ranked among the lanes with one ballot per bit
+// of the number (peers share every bit), so the numbering matches a
+// sequential pass exactly.
 
 __host__ __device__ inline int lp_waves_per_block(int words_per_wave) {
   const int w = (kMaxLdsBytes / 4) / words_per_wave;
   return w < 1 ? 1 : (w > 4 ? 4 : w);
 }
 
+// cmap[e] = compact number (< C) of expert e (-1: not replicated); with
+// pid/fx, the slot's physical id and its flow clamped to int32.  Returns whether the
+// layer's table is bad (an id out of range, or an expert named twice).
+__device__ bool lp_build_map(const int32_t* rl, const int64_t* fl, int32_t RKR, int32_t E, int32_t C,
+                             int32_t* cmap, int32_t* pid, int32_t* fx) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < E; e += 64) cmap[e] = -1;
+  lp_wave_sync();
+  int bad = 0;
+  int base = 0;
+  for (int i0 = 0; i0 < RKR; i0 += 64) {
+    const int i = i0 + lane;
+    const int32_t x = i < RKR ? rl[i] : -1;
+    const bool inr = (uint32_t)x < (uint32_t)E;
+    if (x != -1 && !inr) bad = 1;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(inr);
+    const int c = base + __popcll(m & ((1ull << lane) - 1));
+    if (inr && c >= C) bad = 1;                        // more filled slots than experts: a repeat
+    if (inr && c < C) {
+      if (atomicExch(&cmap[x], c) != -1) bad = 1;   // named twice
+      if (pid != nullptr) {
+        pid[c] = E + i;
+        const int64_t f = fl[i];
+        fx[c] = f <= 0 ? 0 : (f >= 0x7fffffff ? 0x7fffffff : (int32_t)f);
+      }
+    }
+    base += __popcll(m);
+  }
+  lp_wave_sync();
+  return __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+}
+
 __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __restrict__ idx, int64_t n, int32_t E,
+                                                           const int32_t* __restrict__ rep, int32_t RKR, int32_t C,
                                                            int64_t S, int64_t LS, int32_t wpb,
                                                            int32_t* __restrict__ seg) {
   extern __shared__ int32_t lp_cnt[];
@@ -288,9 +324,9 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
   const int64_t q = (int64_t)blockIdx.x * wpb + wave;
   if (q >= LS) return;                                 // whole wave; no workgroup barrier below
   const int64_t l = q / S, s = q - l * S;
-  int32_t* cnt = lp_cnt + wave * E;
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  lp_wave_sync();
+  int32_t* cmap = lp_cnt + wave * (E + C);
+  int32_t* cnt = cmap + E;
+  for (int c = lane; c < C; c += 64) cnt[c] = 0;
   const int32_t* src = idx + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
   int32_t v[kLpSeg / 64];                              // the whole segment in flight at once
@@ -299,112 +335,94 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
     const int i = k * 64 + lane;
     v[k] = i < len ? src[i] : -1;
   }
+  lp_build_map(rep + l * RKR, nullptr, RKR, E, C, cmap, nullptr, nullptr);
 #pragma unroll
-  for (int k = 0; k < kLpSeg / 64; ++k)
-    if ((uint32_t)v[k] < (uint32_t)E) atomicAdd(&cnt[v[k]], 1);
+  for (int k = 0; k < kLpSeg / 64; ++k) {
+    const int c = (uint32_t)v[k] < (uint32_t)E ? cmap[v[k]] : -1;
+    if (c >= 0) atomicAdd(&cnt[c], 1);
+  }
   lp_wave_sync();
-  int32_t* dst = seg + q * E;
-  for (int e = lane; e < E; e += 64) dst[e] = cnt[e];
+  int32_t* dst = seg + q * C;
+  for (int c = lane; c < C; c += 64) dst[c] = cnt[c];
 }
 
+// One wave per (layer, compact number): the segments' counts, 64 segments
+// per pass, become exclusive prefixes by a wave scan.
 __global__ __launch_bounds__(256) void lp_seg_scan_kernel(int32_t* __restrict__ seg, int64_t L, int64_t S,
-                                                          int32_t E) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= L * E) return;
-  const int64_t l = t / E, e = t - l * E;
-  int32_t* p = seg + l * S * E + e;
-  int32_t run = 0;
-  for (int64_t s0 = 0; s0 < S; s0 += 8) {             // eight loads in flight, then their prefix
-    int32_t v[8];
+                                                          int32_t C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (t >= L * C) return;                              // whole wave
+  const int64_t l = t / C, c = t - l * C;
+  int32_t* p = seg + l * S * C + c;
+  int32_t carry = 0;
+  for (int64_t s0 = 0; s0 < S; s0 += 64) {
+    const int64_t sg = s0 + lane;
+    const int32_t v = sg < S ? p[sg * C] : 0;
+    int32_t incl = v;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? p[(s0 + k) * E] : 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k < S) p[(s0 + k) * E] = run;
-      run += v[k];
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t o = __shfl_up(incl, off);
+      incl += lane >= off ? o : 0;
     }
+    if (sg < S) p[sg * C] = carry + incl - v;
+    carry += __shfl(incl, 63);
   }
 }
 
 __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restrict__ idx, int64_t n, int32_t E,
                                                           int32_t nbits, const int32_t* __restrict__ rep,
-                                                          const int64_t* __restrict__ flow, int32_t RKR, int64_t S,
-                                                          int64_t LS, int32_t wpb, const int32_t* __restrict__ seg,
+                                                          const int64_t* __restrict__ flow, int32_t RKR, int32_t C,
+                                                          int64_t S, int64_t LS, int32_t wpb,
+                                                          const int32_t* __restrict__ seg,
                                                           int32_t* __restrict__ out) {
   extern __shared__ int32_t lp_tab[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t q = (int64_t)blockIdx.x * wpb + wave;
   if (q >= LS) return;                                 // whole wave; no workgroup barrier below
   const int64_t l = q / S, s = q - l * S;
-  int32_t* run = lp_tab + wave * 3 * E;                // running occurrence count per expert
-  int32_t* pid = run + E;                              // replica's physical id, or -1
-  int32_t* fx = pid + E;                               // replica's flow (clamped to int32)
-  const int32_t* base = seg + q * E;
-  for (int e0 = 0; e0 < E; e0 += 256) {                // four loads in flight per lane
-    int32_t v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = e0 + k * 64 + lane;
-      v[k] = e < E ? base[e] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = e0 + k * 64 + lane;
-      if (e < E) {
-        run[e] = v[k];
-        pid[e] = -1;
-        fx[e] = 0;
-      }
-    }
-  }
-  lp_wave_sync();
-  const int32_t* rl = rep + l * RKR;
-  const int64_t* fl = flow + l * RKR;
-  int bad = 0;
-  for (int i = lane; i < RKR; i += 64) {
-    const int32_t x = rl[i];
-    if (x == -1) continue;
-    if ((uint32_t)x >= (uint32_t)E) { bad = 1; continue; }
-    if (atomicExch(&pid[x], E + i) != -1) bad = 1;     // named twice
-    const int64_t f = fl[i];
-    fx[x] = f <= 0 ? 0 : (f >= 0x7fffffff ? 0x7fffffff : (int32_t)f);
-  }
-  bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
-  lp_wave_sync();
+  int32_t* cmap = lp_tab + wave * (E + 3 * C);
+  int32_t* run = cmap + E;                             // running occurrence count per compact number
+  int32_t* pid = run + C;                              // its replica's physical id
+  int32_t* fx = pid + C;                               // its replica's flow (clamped to int32)
   const int32_t* src = idx + l * n + s * kLpSeg;
   int32_t* dst = out + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
-  const uint64_t below = (1ull << lane) - 1;
   int32_t v[kLpSeg / 64];                              // the whole segment in flight at once
 #pragma unroll
   for (int k = 0; k < kLpSeg / 64; ++k) {
     const int i = k * 64 + lane;
     v[k] = i < len ? src[i] : -1;
   }
-  {
+  const int32_t* base = seg + q * C;
+  for (int c = lane; c < C; c += 64) run[c] = base[c];
+  const bool bad = lp_build_map(rep + l * RKR, flow + l * RKR, RKR, E, C, cmap, pid, fx);
+  const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
-    for (int k = 0; k < kLpSeg / 64; ++k) {
-      const int i = k * 64 + lane;
-      if (k * 64 >= len) break;                        // uniform
-      const int32_t e = v[k];
-      const bool valid = i < len && (uint32_t)e < (uint32_t)E && !bad;
-      uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
+  for (int k = 0; k < kLpSeg / 64; ++k) {
+    const int i = k * 64 + lane;
+    if (k * 64 >= len) break;                          // uniform
+    const int32_t e = v[k];
+    const bool inr = i < len && (uint32_t)e < (uint32_t)E && !bad;
+    const int c = inr ? cmap[e] : -1;
+    int32_t res = inr ? e : -1;
+    const uint64_t has = __builtin_amdgcn_ballot_w64(c >= 0);
+    if (has != 0) {                                    // uniform
+      uint64_t peers = has;
       for (int bit = 0; bit < nbits; ++bit) {
-        const bool one = (e >> bit) & 1;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(valid && one);
+        const bool one = (c >> bit) & 1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(c >= 0 && one);
         peers &= one ? m : ~m;
       }
-      int32_t res = -1;
-      if (valid) {
+      if (c >= 0) {
         const int rank = __popcll(peers & below);
-        const int32_t occ = run[e] + rank;
-        const int32_t p = pid[e];
-        res = (p >= 0 && occ < fx[e]) ? p : e;
-        if (rank == 0) run[e] = occ + __popcll(peers);
+        const int32_t occ = run[c] + rank;
+        if (occ < fx[c]) res = pid[c];
+        if (rank == 0) run[c] = occ + __popcll(peers);
       }
       lp_wave_sync();
-      if (i < len) dst[i] = res;
     }
+    if (i < len) dst[i] = res;
   }
 }
 
@@ -418,19 +436,21 @@ hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t 
   const int64_t S = lp_segments(n);
   const int64_t LS = L * S;
   if (LS == 0) return hipSuccess;
+  const int32_t RKR = RK * R;
+  const int32_t C = RKR < E ? RKR : E;                 // compact numbers: distinct replicated experts
   int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const int wpb_a = lp_waves_per_block(E);
-  lp_seg_count_kernel<<<(unsigned)((LS + wpb_a - 1) / wpb_a), 64 * wpb_a, (size_t)wpb_a * E * 4, stream>>>(
-      idx, n, E, S, LS, wpb_a, seg);
+  while ((1 << nbits) < C) ++nbits;
+  const int wpb_a = lp_waves_per_block(E + C);
+  lp_seg_count_kernel<<<(unsigned)((LS + wpb_a - 1) / wpb_a), 64 * wpb_a, (size_t)wpb_a * (E + C) * 4, stream>>>(
+      idx, n, E, rep, RKR, C, S, LS, wpb_a, seg);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  lp_seg_scan_kernel<<<(unsigned)((L * E + 255) / 256), 256, 0, stream>>>(seg, L, S, E);
+  lp_seg_scan_kernel<<<(unsigned)((L * C + 3) / 4), 256, 0, stream>>>(seg, L, S, C);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int wpb_c = lp_waves_per_block(3 * E);
-  lp_redirect_kernel<<<(unsigned)((LS + wpb_c - 1) / wpb_c), 64 * wpb_c, (size_t)wpb_c * 3 * E * 4, stream>>>(
-      idx, n, E, nbits, rep, flow, RK * R, S, LS, wpb_c, seg, out);
+  const int wpb_c = lp_waves_per_block(E + 3 * C);
+  lp_redirect_kernel<<<(unsigned)((LS + wpb_c - 1) / wpb_c), 64 * wpb_c, (size_t)wpb_c * (E + 3 * C) * 4, stream>>>(
+      idx, n, E, nbits, rep, flow, RKR, C, S, LS, wpb_c, seg, out);
   return hipGetLastError();
 }
 
