@@ -18,7 +18,8 @@
 //      <= lam * |S|, so lam* = max over S of ceil((load(S) - cap(S -> rest))
 //      / |S|); the 2^RK - 1 sets are enumerated in Gray-code order (one rank
 //      in or out per step; the cut changes by that rank's edges to and from
-//      the set, visited through neighbour bitmasks), spread over the threads;
+//      the set, summed from per-rank tables over 4-rank quarters of the
+//      set), spread over the threads;
 //   3. one wave computes a maximum flow of the feasibility network at lam*
 //      (source -> rank: what it must shed; rank -> sink: what it may take)
 //      by shortest augmenting paths (Edmonds and Karp, J. ACM 1972), the
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   __shared__ long long res[kLpMaxV * kLpMaxV];                        // residual, res[u * V + v]
   __shared__ uint32_t seen_bits[kMaxE / 32];
   __shared__ long long s_best[kLpThreads / 64];
-  __shared__ uint32_t nin[kLpMaxRanks], nout[kLpMaxRanks];
+  __shared__ long long psym[kLpMaxRanks * 4 * 16];                   // [r][quarter][4-bit subset]
+  __shared__ long long outtot[kLpMaxRanks];
 
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -105,17 +107,31 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   }
 
   // ---- 2. lam* = max over rank sets S of ceil((load(S) - cap(S -> rest)) / |S|)
-  // neighbour sets: bit o of nin[r] if cap[o][r] > 0, bit g of nout[r] if cap[r][g] > 0
+  // When rank r enters or leaves, giving the set T, the cut cap(T -> rest)
+  // changes by d_r(T) = cap(r -> outside T) - cap(T -> r)
+  //                  = outtot[r] - sum over g in T of (cap[r][g] + cap[g][r]),
+  // and that sum is read from psym[r][q][T's bits q*4 .. q*4+3] for the
+  // four quarters q of the ranks (one LDS round trip per step).
+  for (int i = tid; i < kLpMaxRanks * 4 * 16; i += kLpThreads) {
+    const int r = i >> 6, q = (i >> 4) & 3, m = i & 15;
+    long long v = 0;
+    if (r < RK)
+      for (int t = 0; t < 4; ++t) {
+        const int g = q * 4 + t;
+        if (((m >> t) & 1) && g < RK && g != r) v += (long long)(cap[r * RK + g] + cap[g * RK + r]);
+      }
+    psym[i] = v;
+  }
   if (tid < RK) {
-    uint32_t mi = 0, mo = 0;
-    for (int o = 0; o < RK; ++o) {
-      mi |= (uint32_t)(cap[o * RK + tid] > 0) << o;
-      mo |= (uint32_t)(cap[tid * RK + o] > 0) << o;
-    }
-    nin[tid] = mi;
-    nout[tid] = mo;
+    long long o = 0;
+    for (int g = 0; g < RK; ++g) o += (long long)cap[tid * RK + g];
+    outtot[tid] = o;
   }
   __syncthreads();
+  auto cut_change = [&](int r, uint32_t T) {
+    const long long* pr = psym + r * 64;
+    return outtot[r] - pr[T & 15] - pr[16 + ((T >> 4) & 15)] - pr[32 + ((T >> 8) & 15)] - pr[48 + ((T >> 12) & 15)];
+  };
   const uint32_t nsets = 1u << RK;                     // Gray index i in [1, nsets) gives S = i ^ (i >> 1)
   const uint32_t per = (nsets - 1 + kLpThreads - 1) / kLpThreads;
   const uint32_t i0 = 1 + (uint32_t)tid * per;
@@ -127,30 +143,55 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   if (i0 < i1) {
     uint32_t S = i0 ^ (i0 >> 1);
     long long ld = 0, out = 0;
-    for (int r = 0; r < RK; ++r) {
-      if (!((S >> r) & 1u)) continue;
+    uint32_t T = 0;
+    for (uint32_t m = S; m; m &= m - 1) {              // the first set, one rank at a time
+      const int r = __builtin_ctz(m);
+      T |= 1u << r;
       ld += (long long)base[r];
-      for (int g = 0; g < RK; ++g)
-        if (!((S >> g) & 1u)) out += (long long)cap[r * RK + g];
+      out += cut_change(r, T);
     }
-    for (uint32_t i = i0;; ) {
-      const int k = __popc(S);
+    auto consider = [&](uint32_t set) {
+      const int k = __popc(set);
       const long long num = ld - out;
       if (num * bk > bnum * k) {
         bnum = num;
         bk = k;
       }
-      if (++i >= i1) break;
-      const int r = __builtin_ctz(i);                  // the rank that enters or leaves
-      const uint32_t T = S ^ (1u << r);
-      long long into_r = 0, from_r = 0;                // cap(T without r -> r), cap(r -> outside T); cap[r][r] = 0
-      for (uint32_t m = nin[r] & T; m; m &= m - 1) into_r += (long long)cap[__builtin_ctz(m) * RK + r];
-      for (uint32_t m = nout[r] & ~T; m; m &= m - 1) from_r += (long long)cap[r * RK + __builtin_ctz(m)];
-      const long long d = from_r - into_r;
-      const bool joins = (T >> r) & 1u;
+    };
+    consider(S);
+    uint32_t i = i0 + 1;
+    for (; i + 4 <= i1; i += 4) {                      // four steps' table reads in flight
+      int r[4];
+      uint32_t T[4];
+      long long d[4], bs[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        r[k] = __builtin_ctz(i + k);                   // the rank that enters or leaves
+        T[k] = (k == 0 ? S : T[k - 1]) ^ (1u << r[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        d[k] = cut_change(r[k], T[k]);
+        bs[k] = (long long)base[r[k]];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool joins = (T[k] >> r[k]) & 1u;
+        ld += joins ? bs[k] : -bs[k];
+        out += joins ? d[k] : -d[k];
+        consider(T[k]);
+      }
+      S = T[3];
+    }
+    for (; i < i1; ++i) {
+      const int r = __builtin_ctz(i);
+      const uint32_t T2 = S ^ (1u << r);
+      const long long d = cut_change(r, T2);
+      const bool joins = (T2 >> r) & 1u;
       ld += joins ? (long long)base[r] : -(long long)base[r];
       out += joins ? d : -d;
-      S = T;
+      S = T2;
+      consider(S);
     }
   }
   long long best = bnum > 0 ? (bnum + bk - 1) / bk : 0;
@@ -175,44 +216,57 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
 
   // ---- 3. maximum flow at lam* (wave 0; one lane per node).  Lane v keeps
   // `in` = the set of nodes u with residual capacity u -> v, so one level of
-  // the search is a bit scan; the path's bottleneck travels with the search.
+  // the search is a bit scan and a ballot.  The path is then walked back
+  // from the sink (its bottleneck from the tree edges' residuals), and `in`
+  // changes only where the path did: a path edge that runs dry leaves its
+  // head's set, each reverse edge joins its tail's set.
   int exhausted = 0;
   if (wave == 0) {
     const bool node = lane < V;
     uint64_t in = 0;
-    if (node)
-      for (int u = 0; u < V; ++u) in |= (uint64_t)(res[u * V + lane] > 0) << u;
+    if (node) {
+#pragma unroll
+      for (int u = 0; u < kLpMaxV; ++u)
+        if (u < V) in |= (uint64_t)(res[u * V + lane] > 0) << u;
+    }
     for (int it = 0; it < kLpMaxAugment; ++it) {
       uint64_t seen = 1ull << src, frontier = 1ull << src;
       int parent = -1;
-      long long neck = lane == src ? LLONG_MAX : 0;    // least residual on the path to this node
       while (frontier && !((seen >> snk) & 1ull)) {
         const uint64_t cand = node && !((seen >> lane) & 1ull) ? (in & frontier) : 0;
-        const int p = cand ? __builtin_ctzll(cand) : 0;
-        const long long pn = __shfl(neck, p);
-        if (cand) {
-          parent = p;
-          const long long x = res[p * V + lane];
-          neck = pn < x ? pn : x;
-        }
+        if (cand) parent = __builtin_ctzll(cand);
         const uint64_t found = __builtin_amdgcn_ballot_w64(cand != 0);
         seen |= found;
         frontier = found;
       }
       if (!((seen >> snk) & 1ull)) break;
-      const long long bn = __shfl(neck, snk);
+      const bool reached = node && lane != src && ((seen >> lane) & 1ull);
+      long long fwd = 0, bwd = 0;                      // residuals of parent -> lane and lane -> parent
+      if (reached) {
+        fwd = res[parent * V + lane];
+        bwd = res[lane * V + parent];
+      }
       uint64_t path = 0;                               // nodes on the path, source excluded
-      for (int v = snk; v != src; v = __builtin_amdgcn_readlane(parent, v)) path |= 1ull << v;
-      lp_wave_sync();
-      if (node && ((path >> lane) & 1ull)) {           // edge parent -> lane carries bn more
-        res[parent * V + lane] -= bn;
-        res[lane * V + parent] += bn;
+      long long bn = LLONG_MAX;
+      int child = -1;                                  // this node's successor on the path
+      for (int v = snk; v != src; ) {
+        const int pv = __builtin_amdgcn_readlane(parent, v);
+        const long long fv = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(fwd >> 32), v) << 32) |
+                                         (uint32_t)__builtin_amdgcn_readlane((int)fwd, v));
+        bn = fv < bn ? fv : bn;
+        path |= 1ull << v;
+        child = lane == pv ? v : child;
+        v = pv;
       }
       lp_wave_sync();
-      if (node) {
-        in = 0;
-        for (int u = 0; u < V; ++u) in |= (uint64_t)(res[u * V + lane] > 0) << u;
+      if ((path >> lane) & 1ull) {                     // edge parent -> lane carries bn more
+        const long long nf = fwd - bn;
+        res[parent * V + lane] = nf;
+        res[lane * V + parent] = bwd + bn;
+        if (nf == 0) in &= ~(1ull << parent);
       }
+      if (child >= 0) in |= 1ull << child;
+      lp_wave_sync();
       if (it == kLpMaxAugment - 1) exhausted = 1;
     }
   }
