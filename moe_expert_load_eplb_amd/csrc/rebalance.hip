@@ -32,6 +32,10 @@
 //                updated pack is re-inserted at the position one ballot
 //                counts, and the positions before it move down one lane
 //                (DPP wave_shl).  No reduction tree, no LDS on the chain.
+//                With 4 or more packs in the one-word form, RUNS of items
+//                go at once: item j+s takes the pack at position s while
+//                that pack stays below every earlier item's updated pack,
+//                which each lane checks for its own item in parallel.
 //   replication  positions hold experts ordered by (load per replica desc,
 //                index asc).  The expert at position 0 gets the replica and
 //                is re-inserted the same way.
@@ -369,15 +373,6 @@ __device__ void pack_sorted(KeyOf key_of, int n, int m, int cap, int32_t* res) {
   }
 }
 
-// The same packing with each pack in ONE 64-bit word, sum << 16 | pack << 8 |
-// items, for sums below 2^48 - 1, at most 256 packs and at most 255 items per
-// pack; a full pack is all ones.  Words of different packs differ in the pack
-// bits, so one unsigned compare orders packs by (sum, index), and one add of
-// a pre-shifted key (key_of(t) = key << 16 | 1) both adds an item and
-// counts it.  A lone
-// wavefront issues about one instruction per four cycles, so the step's
-// instruction count is its latency; this form has about half the
-// instructions of the general one.  res[t] = pack * cap + arrival position.
 __device__ __forceinline__ u64 shfl64(u64 x, int src) {
   const int lo = __shfl((int)(uint32_t)x, src);
   const int hi = __shfl((int)(uint32_t)(x >> 32), src);
@@ -570,6 +565,17 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
   }
 }
 
+// The same packing with each pack in ONE 64-bit word, sum << 16 | pack << 8 |
+// items, for sums below 2^48 - 1, at most 256 packs and at most 255 items per
+// pack.  Words of different packs differ in the pack bits, so one unsigned
+// compare orders packs by (sum, index), and one add of a pre-shifted key
+// (key_of(t) = key << 16 | 1) both adds an item and counts it.  From 4 packs
+// on, runs of items are placed at once (pack_words_few, pack_words_wide);
+// below that, one item per step, a full pack being all ones.  A lone
+// wavefront's step costs about its dependent-instruction count in issue
+// slots; this form has about half the instructions of the general one.
+// res[t] = pack * cap + arrival position; scr: the wave's LDS scratch for
+// pack_words_wide.
 template <int K, class KeyOf>
 __device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res, u64* scr) {
   if constexpr (K > 1 && K <= 4) {
