@@ -257,6 +257,50 @@ def test_shapes_random(shape):
     rebalance_both(load, P, G, N, RK)
 
 
+def _fuzz_shapes(rng, count):
+    """Valid placement shapes of every kind: hierarchical and global, 1 to 64
+    GPUs per node (the sequential, register-run and LDS-run packing forms),
+    one to eight registers of experts per node."""
+    shapes = []
+    while len(shapes) < count:
+        N = int(rng.choice([1, 1, 2, 3, 4, 5, 8]))
+        hier = rng.random() < 0.6
+        G = N * int(rng.integers(1, 5)) if hier else int(rng.choice([g for g in range(2, 13) if g % N]) if N > 1 else 1)
+        if not hier and N == 1:
+            hier = True
+        Np = N if hier else 1
+        S = int(rng.integers(1, 9))
+        E = G * S if hier else int(rng.integers(2, 80))
+        RKn = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 33, 40, 64]))
+        RK = RKn * Np
+        ppr = int(rng.integers(1, 6))
+        P = RK * ppr
+        if P < E or E > 512 or E // Np > 512 or RK > 512:
+            continue
+        if hier and E % G:
+            continue
+        shapes.append((E, G, N, RK, P))
+    return shapes
+
+
+def test_random_shapes_fuzz():
+    """300 random valid shapes, 3 problems each (zero, tied, skewed and
+    large loads), element by element against the oracle."""
+    rng = np.random.default_rng(20251203)
+    for E, G, N, RK, P in _fuzz_shapes(rng, 300):
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            load = rng.integers(0, 5, size=(3, E))
+        elif kind == 1:
+            load = rng.integers(0, 1 << 20, size=(3, E))
+        elif kind == 2:
+            load = (rng.zipf(1.3, size=(3, E)) * 1000).clip(0, 1 << 40)
+        else:
+            load = rng.integers((1 << 40) - 100, (1 << 40) + 1, size=(3, E))
+        load[0, : E // 2] = 0
+        rebalance_both(load.astype(np.int64), P, G, N, RK)
+
+
 def test_large_loads_and_exactness():
     rng = np.random.default_rng(5)
     load = rng.integers((1 << 40) - 5000, (1 << 40) + 1, size=(16, 64))
