@@ -271,7 +271,7 @@ def _fuzz_shapes(rng, count):
         Np = N if hier else 1
         S = int(rng.integers(1, 9))
         E = G * S if hier else int(rng.integers(2, 80))
-        RKn = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 33, 40, 64]))
+        RKn = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 17, 24, 33, 40, 64, 80, 130, 200]))
         RK = RKn * Np
         ppr = int(rng.integers(1, 6))
         P = RK * ppr
@@ -284,7 +284,7 @@ def _fuzz_shapes(rng, count):
 
 
 def test_random_shapes_fuzz():
-    """300 random valid shapes, 3 problems each (zero, tied, skewed and
+    """300 random valid shapes (1 to 200 GPUs per node), 3 problems each (zero, tied, skewed and
     large loads), element by element against the oracle."""
     rng = np.random.default_rng(20251203)
     for E, G, N, RK, P in _fuzz_shapes(rng, 300):
