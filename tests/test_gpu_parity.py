@@ -258,9 +258,9 @@ def test_shapes_random(shape):
 
 
 def _fuzz_shapes(rng, count):
-    """Valid placement shapes of every kind: hierarchical and global, 1 to 64
-    GPUs per node (the sequential, register-run and LDS-run packing forms),
-    one to eight registers of experts per node."""
+    """Valid placement shapes of every kind: hierarchical and global, 1 to 200
+    GPUs per node (the sequential, register-run and LDS-run packing forms, one
+    to four registers of packs), one to eight registers of experts per node."""
     shapes = []
     while len(shapes) < count:
         N = int(rng.choice([1, 1, 2, 3, 4, 5, 8]))
@@ -284,8 +284,8 @@ def _fuzz_shapes(rng, count):
 
 
 def test_random_shapes_fuzz():
-    """300 random valid shapes (1 to 200 GPUs per node), 3 problems each (zero, tied, skewed and
-    large loads), element by element against the oracle."""
+    """300 random valid shapes, 3 problems each (zero, tied, skewed and large
+    loads), element by element against the oracle."""
     rng = np.random.default_rng(20251203)
     for E, G, N, RK, P in _fuzz_shapes(rng, 300):
         kind = rng.integers(0, 4)
