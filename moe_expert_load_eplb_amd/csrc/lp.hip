@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   __shared__ uint32_t seen_bits[kMaxE / 32];
   __shared__ long long s_best[kLpThreads / 64];
   __shared__ long long psym[kLpMaxRanks * 4 * 16];                   // [r][quarter][4-bit subset]
-  __shared__ long long outtot[kLpMaxRanks];
+  __shared__ long long wbase[kLpMaxRanks];                            // base[r] - cap(r -> every other rank)
 
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
 
   // ---- 2. lam* = max over rank sets S of ceil((load(S) - cap(S -> rest)) / |S|)
   // When rank r enters or leaves, giving the set T, the cut cap(T -> rest)
-  // changes by d_r(T) = cap(r -> outside T) - cap(T -> r)
-  //                  = outtot[r] - sum over g in T of (cap[r][g] + cap[g][r]),
+  // changes by cap(r -> outside T) - cap(T -> r)
+  //          = cap(r -> all) - sum over g in T of (cap[r][g] + cap[g][r]),
   // and that sum is read from psym[r][q][T's bits q*4 .. q*4+3] for the
   // four quarters q of the ranks (one LDS round trip per step).
   for (int i = tid; i < kLpMaxRanks * 4 * 16; i += kLpThreads) {
@@ -125,76 +125,65 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   if (tid < RK) {
     long long o = 0;
     for (int g = 0; g < RK; ++g) o += (long long)cap[tid * RK + g];
-    outtot[tid] = o;
+    wbase[tid] = (long long)base[tid] - o;
   }
   __syncthreads();
-  auto cut_change = [&](int r, uint32_t T) {
+  // f(S) = load(S) - cap(S -> rest) changes, when rank r joins or leaves and
+  // the set becomes T, by +-(base[r] - cap(r -> outside T) + cap(T -> r))
+  //   = +-(wbase[r] + sum over g in T of (cap[r][g] + cap[g][r]))
+  auto step_change = [&](int r, uint32_t T) {
     const long long* pr = psym + r * 64;
-    return outtot[r] - pr[T & 15] - pr[16 + ((T >> 4) & 15)] - pr[32 + ((T >> 8) & 15)] - pr[48 + ((T >> 12) & 15)];
+    return wbase[r] + pr[T & 15] + pr[16 + ((T >> 4) & 15)] + pr[32 + ((T >> 8) & 15)] + pr[48 + ((T >> 12) & 15)];
   };
   const uint32_t nsets = 1u << RK;                     // Gray index i in [1, nsets) gives S = i ^ (i >> 1)
   const uint32_t per = (nsets - 1 + kLpThreads - 1) / kLpThreads;
   const uint32_t i0 = 1 + (uint32_t)tid * per;
   const uint32_t i1 = min(nsets, i0 + per);
-  // the largest ratio num / k is kept as a fraction (cross-multiplied:
-  // num <= 2^56, k <= 16) and rounded up once at the end
-  long long bnum = 0;
-  int bk = 1;
+  // best = the largest ceil(f(S) / |S|) so far (at least 0): a set beats it
+  // exactly when f(S) > best * |S| (f <= 2^56, |S| <= 16), and only then is
+  // the division made
+  long long best = 0;
   if (i0 < i1) {
     uint32_t S = i0 ^ (i0 >> 1);
-    long long ld = 0, out = 0;
+    long long f = 0;
     uint32_t T = 0;
     for (uint32_t m = S; m; m &= m - 1) {              // the first set, one rank at a time
       const int r = __builtin_ctz(m);
       T |= 1u << r;
-      ld += (long long)base[r];
-      out += cut_change(r, T);
+      f += step_change(r, T);
     }
     auto consider = [&](uint32_t set) {
       const int k = __popc(set);
-      const long long num = ld - out;
-      if (num * bk > bnum * k) {
-        bnum = num;
-        bk = k;
-      }
+      if (f > best * k) best = (f + k - 1) / k;
     };
     consider(S);
     uint32_t i = i0 + 1;
     for (; i + 4 <= i1; i += 4) {                      // four steps' table reads in flight
       int r[4];
-      uint32_t T[4];
-      long long d[4], bs[4];
+      uint32_t T4[4];
+      long long d[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         r[k] = __builtin_ctz(i + k);                   // the rank that enters or leaves
-        T[k] = (k == 0 ? S : T[k - 1]) ^ (1u << r[k]);
+        T4[k] = (k == 0 ? S : T4[k - 1]) ^ (1u << r[k]);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        d[k] = cut_change(r[k], T[k]);
-        bs[k] = (long long)base[r[k]];
-      }
+      for (int k = 0; k < 4; ++k) d[k] = step_change(r[k], T4[k]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const bool joins = (T[k] >> r[k]) & 1u;
-        ld += joins ? bs[k] : -bs[k];
-        out += joins ? d[k] : -d[k];
-        consider(T[k]);
+        f += ((T4[k] >> r[k]) & 1u) ? d[k] : -d[k];
+        consider(T4[k]);
       }
-      S = T[3];
+      S = T4[3];
     }
     for (; i < i1; ++i) {
       const int r = __builtin_ctz(i);
-      const uint32_t T2 = S ^ (1u << r);
-      const long long d = cut_change(r, T2);
-      const bool joins = (T2 >> r) & 1u;
-      ld += joins ? (long long)base[r] : -(long long)base[r];
-      out += joins ? d : -d;
-      S = T2;
+      S ^= 1u << r;
+      const long long d = step_change(r, S);
+      f += ((S >> r) & 1u) ? d : -d;
       consider(S);
     }
   }
-  long long best = bnum > 0 ? (bnum + bk - 1) / bk : 0;
   for (int off = 32; off > 0; off >>= 1) {
     const long long o = __shfl_xor(best, off);
     best = o > best ? o : best;
