@@ -1016,10 +1016,6 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
   const int NW = NT >> 6;
   const int lane = lane_id();
 
-  // log2phy starts as all -1, written coalesced; the placement overwrites
-  // each expert's first `count` entries after the barriers below
-  fill_minus_one(log2phy + b * (int64_t)p.E * p.X, (int64_t)p.E * p.X, tid, NT);
-
   // ---- loads, range check
   if (tid == 0) s.flags[0] = 0;
   __syncthreads();
@@ -1034,6 +1030,10 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
     write_failed(p, b, s.flags[0], phy2log, log2phy, logcnt, status);
     return;
   }
+  // log2phy starts as all -1, written coalesced after the loads have arrived
+  // (stores issued before them would hold up their wait); the placement
+  // overwrites each expert's first `count` entries after the barriers below
+  fill_minus_one(log2phy + b * (int64_t)p.E * p.X, (int64_t)p.E * p.X, tid, NT);
 
   // ---- step 1: groups -> nodes
   if (p.gpn == 1) {
