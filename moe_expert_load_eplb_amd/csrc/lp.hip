@@ -41,6 +41,8 @@ namespace {
 constexpr int kLpThreads = 1024;
 constexpr int kLpMaxV = kLpMaxRanks + 2;
 constexpr int kLpMaxAugment = 1 << 16;     // far above the Edmonds-Karp bound V * E for V <= 18
+constexpr int kLpSplitRanks = 12;          // from 2^12 rank sets on, step 2 is spread over kLpParts workgroups
+constexpr int kLpParts = 4;                // (<= kLpSplitRanks: the bounds sit in a layer's rank_load row)
 
 __device__ __forceinline__ void lp_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -48,9 +50,15 @@ __device__ __forceinline__ void lp_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// kMode 0: the whole solve in one workgroup per layer.  With many ranks the
+// enumeration of step 2 is split: kMode 1 runs `parts` workgroups per layer,
+// each over its share of the rank sets, and leaves its bound in
+// load_out[b][part] (a scratch use of the output, rewritten at the end);
+// kMode 2 then takes the largest of those and does steps 3 and 4.
+template <int kMode>
 __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
     const int64_t* __restrict__ cnt, const int32_t* __restrict__ home, const int32_t* __restrict__ rep,
-    int32_t E, int32_t RK, int32_t R, int64_t* __restrict__ lam_out, int64_t* __restrict__ flow_out,
+    int32_t E, int32_t RK, int32_t R, int32_t parts, int64_t* __restrict__ lam_out, int64_t* __restrict__ flow_out,
     int64_t* __restrict__ load_out, int32_t* __restrict__ status) {
   __shared__ unsigned long long base[kLpMaxRanks];
   __shared__ unsigned long long cap[kLpMaxRanks * kLpMaxRanks];      // cap[o * RK + g]
@@ -60,7 +68,8 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   __shared__ long long psym[kLpMaxRanks * 4 * 16];                   // [r][quarter][4-bit subset]
   __shared__ long long wbase[kLpMaxRanks];                            // base[r] - cap(r -> every other rank)
 
-  const int64_t b = blockIdx.x;
+  const int64_t b = kMode == 1 ? blockIdx.x / parts : blockIdx.x;
+  const int part = kMode == 1 ? (int)(blockIdx.x - b * parts) : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t* c = cnt + b * E;
@@ -96,6 +105,7 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   bad = __syncthreads_or(bad);
   int64_t* flow_b = flow_out + b * (int64_t)RK * R;
   int64_t* load_b = load_out + b * RK;
+  if (kMode == 1 && bad) return;                       // the second pass reports it
   if (bad) {
     for (int i = tid; i < RK * R; i += kLpThreads) flow_b[i] = -1;
     for (int i = tid; i < RK; i += kLpThreads) load_b[i] = -1;
@@ -136,9 +146,15 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
     return wbase[r] + pr[T & 15] + pr[16 + ((T >> 4) & 15)] + pr[32 + ((T >> 8) & 15)] + pr[48 + ((T >> 12) & 15)];
   };
   const uint32_t nsets = 1u << RK;                     // Gray index i in [1, nsets) gives S = i ^ (i >> 1)
-  const uint32_t per = (nsets - 1 + kLpThreads - 1) / kLpThreads;
-  const uint32_t i0 = 1 + (uint32_t)tid * per;
-  const uint32_t i1 = min(nsets, i0 + per);
+  uint32_t lo = 1, hi = nsets;                         // this workgroup's Gray indices
+  if (kMode == 1) {
+    const uint32_t span = (nsets - 1 + parts - 1) / parts;
+    lo = min(nsets, 1 + (uint32_t)part * span);
+    hi = min(nsets, lo + span);
+  }
+  const uint32_t per = kMode == 2 ? 0 : (hi - lo + kLpThreads - 1) / kLpThreads;
+  const uint32_t i0 = lo + (uint32_t)tid * per;
+  const uint32_t i1 = min(hi, i0 + per);
   // best = the largest ceil(f(S) / |S|) so far (at least 0): a set beats it
   // exactly when f(S) > best * |S| (f <= 2^56, |S| <= 16), and only then is
   // the division made
@@ -193,6 +209,12 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   __syncthreads();
   long long lam = 0;
   for (int w = 0; w < kLpThreads / 64; ++w) lam = s_best[w] > lam ? s_best[w] : lam;
+  if constexpr (kMode == 1) {
+    if (tid == 0) load_b[part] = lam;
+    return;
+  }
+  if constexpr (kMode == 2)
+    for (int q = 0; q < parts; ++q) lam = load_b[q] > lam ? load_b[q] : lam;
   for (int i = tid; i < V * V; i += kLpThreads) {
     const int u = i / V, v = i - u * V;
     long long x = 0;
@@ -501,7 +523,17 @@ hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
                            int32_t* status, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  lp_solve_kernel<<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, lam, flow, rank_load, status);
+  if (RK < kLpSplitRanks || B > ((int64_t)1 << 31) / kLpParts - 1) {
+    lp_solve_kernel<0><<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, 1, lam, flow, rank_load,
+                                                               status);
+    return hipGetLastError();
+  }
+  lp_solve_kernel<1><<<(unsigned)(B * kLpParts), kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, kLpParts, lam,
+                                                                          flow, rank_load, status);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  lp_solve_kernel<2><<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, kLpParts, lam, flow, rank_load,
+                                                             status);
   return hipGetLastError();
 }
 
