@@ -312,9 +312,11 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
  *                                original of rep[g][j] (0 for empty slots)
  *   rank_load  [B][RK] int64     out: rank loads after the moves (max = lam)
  *   status     [B] int32         out: EPLB_S_OK or EPLB_S_BAD_TOPOLOGY
+ * Outputs must not overlap the inputs (with 12 or more ranks rank_load also
+ * carries partial results between the call's two launches).
  *
- * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array), EPLB_E_LIMIT
- * (E > 4096, RK > 16, R > 64), EPLB_E_HIP.
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output equal to an
+ * input), EPLB_E_LIMIT (E > 4096, RK > 16, R > 64), EPLB_E_HIP.
  */
 int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                       int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,

@@ -143,9 +143,17 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
                       void* stream) {
   if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || RK < 1 || R < 1) return EPLB_E_ARG;
   if (E > kMaxE || RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
-  if (B > 0 && (cnt == nullptr || home == nullptr || rep == nullptr || lam == nullptr || flow == nullptr ||
-                rank_load == nullptr || status == nullptr))
-    return EPLB_E_ARG;
+  if (B > 0) {
+    const void* in[3] = {cnt, home, rep};
+    const void* out[4] = {lam, flow, rank_load, status};
+    for (const void* a : in)
+      if (a == nullptr) return EPLB_E_ARG;
+    for (const void* a : out) {
+      if (a == nullptr) return EPLB_E_ARG;
+      for (const void* c : in)
+        if (a == c) return EPLB_E_ARG;
+    }
+  }
   hipError_t err = launch_lp_solve(cnt, home, rep, B, E, RK, R, lam, flow, rank_load, status, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }

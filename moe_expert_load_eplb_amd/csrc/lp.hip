@@ -10,7 +10,8 @@
 // the expert-parallel group are as even as possible.  Here: the least
 // largest rank load reachable with whole tokens, and one flow reaching it.
 //
-// One workgroup per problem (layer):
+// One workgroup per problem (layer; with 12 or more ranks, step 2 runs over
+// four workgroups per layer in a first launch):
 //   1. home loads base[r] and the capacity cap[o][g] of every rank pair,
 //      with LDS atomics; a bitmap catches an expert replicated twice;
 //   2. the optimum, from the supply-demand theorem (Gale, 1957): a bound lam

@@ -211,7 +211,7 @@ def test_lp_solve_validation(lib):
     good = [F[0], F[1], F[2], 58, 256, 8, 2, F[3], F[4], F[5], F[6], None]
     for pos, bad, code in [(3, -1, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (4, 4097, 5), (5, 17, 5), (6, 65, 5),
                            (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1), (9, None, 1),
-                           (10, None, 1)]:
+                           (10, None, 1), (9, F[0], 1), (7, F[2], 1)]:         # outputs equal to inputs
         args = list(good)
         args[pos] = bad
         assert lib.eplb_lp_solve(*args) == code, (pos, bad)
