@@ -68,6 +68,7 @@ def check_solution(cnt, home, rep, q):
 
 @pytest.mark.parametrize("RK,R,E,top", [(1, 1, 3, 10), (2, 1, 5, 10), (3, 2, 9, 50), (5, 3, 40, 1000),
                                         (8, 2, 256, 10**5), (8, 4, 64, 7), (11, 2, 100, 10**6),
+                                        (12, 3, 200, 10**5), (13, 2, 300, 10**3),
                                         (16, 4, 256, 10**4), (16, 1, 4096, 1 << 40)])
 def test_lp_solve_random(RK, R, E, top):
     rng = np.random.default_rng(RK * 100 + R)
