@@ -926,8 +926,8 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
 #pragma unroll
     for (int r = 0; r < K; ++r) {
       const int pos = r * 64 + lane;
-      u64 pu = (u64)__shfl_up((unsigned long long)u[r], 1);
-      int pc = __shfl_up(c[r], 1);
+      u64 pu = shr1_or64(0ull, u[r]);                // the previous position (DPP)
+      int pc = shr1_or(0, c[r]);
       if (r > 0) {
         const u64 lu = rdl64(u[r - 1], 63);
         const int lc = rdl(c[r - 1], 63);
