@@ -164,9 +164,12 @@ hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t 
 hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
                            int32_t* status, hipStream_t stream);
-hipError_t launch_ema_update(const int32_t* cnt, int64_t LE, int32_t shift, int64_t* ema, hipStream_t stream);
-hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream);
-hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream);
+// load = sum of the window's slots other than cur, slot cur = 0, n_invalid = 0
+hipError_t launch_hist_prep(int32_t* ring, int64_t LE, int32_t W, int64_t cur, int64_t* load, int64_t* n_invalid,
+                            int64_t L, hipStream_t stream);
+// ema = ema - floor(ema / 2^shift), cnt = 0, n_invalid = 0
+hipError_t launch_ema_prep(int32_t* cnt, int64_t LE, int32_t shift, int64_t* ema, int64_t* n_invalid, int64_t L,
+                           hipStream_t stream);
 hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                                 int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
                                 const int32_t* log2phy, const int32_t* logcnt, int32_t X, int32_t* out,

@@ -19,7 +19,7 @@ template <bool kStaged>
 __global__ __launch_bounds__(kStreamThreads) void hist_redirect_kernel(
     const int32_t* __restrict__ idx, StreamSplit sp, FastDiv kdiv, int32_t E, int32_t X, int32_t copies,
     const int32_t* __restrict__ log2phy, const int32_t* __restrict__ logcnt, int32_t* __restrict__ out,
-    int32_t* __restrict__ slot, int64_t* __restrict__ n_invalid) {
+    int32_t* __restrict__ slot, int64_t* __restrict__ acc, int64_t* __restrict__ n_invalid) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t layer = blockIdx.x / sp.chunks;
   const int64_t chunk = blockIdx.x - layer * sp.chunks;
@@ -102,10 +102,14 @@ __global__ __launch_bounds__(kStreamThreads) void hist_redirect_kernel(
   }
   __syncthreads();
   int32_t* cnt_out = slot + layer * E;
+  unsigned long long* acc_l = reinterpret_cast<unsigned long long*>(acc + layer * E);
   for (int e = tid; e < E; e += kStreamThreads) {
     int32_t s = 0;
     for (int c = 0; c < copies; ++c) s += counters[c * stride + e];
-    if (s) atomicAdd(&cnt_out[e], s);
+    if (s) {
+      atomicAdd(&cnt_out[e], s);
+      atomicAdd(&acc_l[e], (unsigned long long)s);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) inv += __shfl_xor(inv, off);
   if ((tid & 63) == 0 && inv)
@@ -117,12 +121,12 @@ __global__ __launch_bounds__(kStreamThreads) void hist_redirect_kernel(
 namespace {
 
 // Clear `slot` and n_invalid, then count and redirect every id in one pass.
+// Count the step's ids into `slot` (cleared) and add them to `acc` and
+// `n_invalid`, redirecting them on the way.
 hipError_t launch_count_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* slot,
-                                 int64_t* n_invalid, const int32_t* log2phy, const int32_t* logcnt, int32_t X,
-                                 int32_t* out, hipStream_t stream) {
-  const int64_t LE = L * (int64_t)E;
-  hipError_t err = launch_hist_clear(slot, LE, n_invalid, L, stream);
-  if (err != hipSuccess) return err;
+                                 int64_t* acc, int64_t* n_invalid, const int32_t* log2phy, const int32_t* logcnt,
+                                 int32_t X, int32_t* out, hipStream_t stream) {
+  hipError_t err = hipSuccess;
   const int64_t per_layer = T * (int64_t)K;
   if (per_layer > 0) {
     const StreamSplit sp = plan_stream(L, per_layer);
@@ -138,10 +142,10 @@ hipError_t launch_count_redirect(const int32_t* idx, int64_t L, int64_t T, int32
     const int64_t blocks = L * sp.chunks;
     if (staged)
       hist_redirect_kernel<true><<<(unsigned)blocks, kStreamThreads, lds, stream>>>(
-          idx, sp, kdiv, E, X, copies, log2phy, logcnt, out, slot, n_invalid);
+          idx, sp, kdiv, E, X, copies, log2phy, logcnt, out, slot, acc, n_invalid);
     else
       hist_redirect_kernel<false><<<(unsigned)blocks, kStreamThreads, lds, stream>>>(
-          idx, sp, kdiv, E, X, copies, log2phy, logcnt, out, slot, n_invalid);
+          idx, sp, kdiv, E, X, copies, log2phy, logcnt, out, slot, acc, n_invalid);
     err = hipGetLastError();
   }
   return err;
@@ -155,19 +159,20 @@ hipError_t launch_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_
                                 hipStream_t stream) {
   if (L == 0) return hipSuccess;
   const int64_t LE = L * (int64_t)E;
-  hipError_t err = launch_count_redirect(idx, L, T, K, E, ring + (step % W) * LE, n_invalid, log2phy, logcnt, X,
-                                         out, stream);
+  const int64_t cur = step % W;
+  hipError_t err = launch_hist_prep(ring, LE, W, cur, load, n_invalid, L, stream);
   if (err != hipSuccess) return err;
-  return launch_window_sum(ring, LE, W, load, stream);
+  return launch_count_redirect(idx, L, T, K, E, ring + cur * LE, load, n_invalid, log2phy, logcnt, X, out,
+                               stream);
 }
 
 hipError_t launch_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* count,
                                int32_t shift, int64_t* ema, int64_t* n_invalid, const int32_t* log2phy,
                                const int32_t* logcnt, int32_t X, int32_t* out, hipStream_t stream) {
   if (L == 0) return hipSuccess;
-  hipError_t err = launch_count_redirect(idx, L, T, K, E, count, n_invalid, log2phy, logcnt, X, out, stream);
+  hipError_t err = launch_ema_prep(count, L * (int64_t)E, shift, ema, n_invalid, L, stream);
   if (err != hipSuccess) return err;
-  return launch_ema_update(count, L * (int64_t)E, shift, ema, stream);
+  return launch_count_redirect(idx, L, T, K, E, count, ema, n_invalid, log2phy, logcnt, X, out, stream);
 }
 
 }  // namespace eplb

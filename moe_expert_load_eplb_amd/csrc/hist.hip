@@ -5,8 +5,10 @@
 // during the observation period (glossary of Part 2 of the EPLB README
 // translation, «DualPipe и EPLB», ai.flicky.cc); the prediction uses the
 // statistics of past steps, a moving average for instance (opening section of
-// Part 2).  Three kernels on one stream: clear this step's counts, count, then
-// sum the window (or update the moving average).
+// Part 2).  Two kernels on one stream: the first clears this step's counts
+// and sets the load to the sum of the window's OTHER steps (or the moving
+// average to its decayed value, ema - ema / 2^shift); the count then adds
+// each workgroup's totals to both the step's counts and the load.
 //
 // Counting is HBM-bound: 4 bytes read per routing id.  A few workgroups per
 // layer sweep the layer together with 16-byte non-temporal loads (all layers
@@ -14,7 +16,8 @@
 // LDS-resident counters; a workgroup keeps `copies` private copies of the E
 // counters (row stride E + 1, so the copies of one expert fall in different
 // LDS banks) to spread the increments of a popular expert.  At the end each
-// workgroup adds its E totals to the ring slot with one global atomic each.
+// workgroup adds its E totals to the ring slot and to the load with one
+// global atomic each.
 #include "eplb_internal.h"
 
 namespace eplb {
@@ -22,10 +25,36 @@ namespace eplb {
 namespace {
 
 
-__global__ __launch_bounds__(256) void hist_clear_kernel(int32_t* __restrict__ slot, int64_t LE,
-                                                         int64_t* __restrict__ n_invalid, int64_t L) {
+// load[i] = sum of ring[w][i] over the window's other slots; ring[cur][i] = 0;
+// n_invalid = 0.  The count kernel then adds the step's counts to both.
+__global__ __launch_bounds__(256) void hist_prep_kernel(int32_t* __restrict__ ring, int64_t LE, int32_t W,
+                                                        int64_t cur, int64_t* __restrict__ load,
+                                                        int64_t* __restrict__ n_invalid, int64_t L) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) slot[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) {
+    int64_t s = 0;
+    for (int w = 0; w < W; ++w)
+      if (w != cur) s += ring[(int64_t)w * LE + i];
+    load[i] = s;
+    ring[cur * LE + i] = 0;
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < L; i += stride) n_invalid[i] = 0;
+}
+
+// One step of the integer moving average, ema <- ema - floor(ema / 2^shift) +
+// cnt, in two parts: here the decay (and cnt = 0, n_invalid = 0), then the
+// count kernel adds the step's counts.  Unsigned arithmetic keeps a wrap
+// (values near 2^63, outside the documented range) defined; >> of the signed
+// value is the floor for negative values too.
+__global__ __launch_bounds__(256) void ema_prep_kernel(int32_t* __restrict__ cnt, int64_t LE, int32_t shift,
+                                                       int64_t* __restrict__ ema, int64_t* __restrict__ n_invalid,
+                                                       int64_t L) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) {
+    const int64_t e = ema[i];
+    ema[i] = (int64_t)((u64)e - (u64)(e >> shift));
+    cnt[i] = 0;
+  }
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < L; i += stride) n_invalid[i] = 0;
 }
 
@@ -37,6 +66,7 @@ __global__ __launch_bounds__(kStreamThreads) void hist_count_kernel(const int32_
                                                                      StreamSplit sp, int32_t E,
                                                                      int32_t copies,
                                                                      int32_t* __restrict__ slot,
+                                                                     int64_t* __restrict__ acc,
                                                                      int64_t* __restrict__ n_invalid) {
   extern __shared__ int32_t counters[];             // [copies][E + 1]
   const int64_t layer = blockIdx.x / sp.chunks;
@@ -84,37 +114,19 @@ __global__ __launch_bounds__(kStreamThreads) void hist_count_kernel(const int32_
   __syncthreads();
 
   int32_t* out = slot + layer * E;
+  unsigned long long* acc_l = reinterpret_cast<unsigned long long*>(acc + layer * E);
   for (int e = tid; e < E; e += kStreamThreads) {
     int32_t s = 0;
     for (int c = 0; c < copies; ++c) s += counters[c * stride + e];
-    if (s) atomicAdd(&out[e], s);
+    if (s) {
+      atomicAdd(&out[e], s);
+      atomicAdd(&acc_l[e], (unsigned long long)s);
+    }
   }
   // One 64-bit atomic per wave for the out-of-range ids.
   for (int off = 32; off > 0; off >>= 1) inv += __shfl_xor(inv, off);
   if ((tid & 63) == 0 && inv)
     atomicAdd(reinterpret_cast<unsigned long long*>(&n_invalid[layer]), (unsigned long long)inv);
-}
-
-__global__ __launch_bounds__(256) void window_sum_kernel(const int32_t* __restrict__ ring, int64_t LE,
-                                                         int32_t W, int64_t* __restrict__ load) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) {
-    int64_t s = 0;
-    for (int w = 0; w < W; ++w) s += ring[(int64_t)w * LE + i];
-    load[i] = s;
-  }
-}
-
-// One step of the integer moving average: ema <- ema - floor(ema / 2^shift) + cnt.
-// Unsigned arithmetic keeps a wrap (values near 2^63, outside the documented
-// range) defined; >> of the signed value is the floor for negative values too.
-__global__ __launch_bounds__(256) void ema_update_kernel(const int32_t* __restrict__ cnt, int64_t LE,
-                                                         int32_t shift, int64_t* __restrict__ ema) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += stride) {
-    const int64_t e = ema[i];
-    ema[i] = (int64_t)((u64)e - (u64)(e >> shift) + (u64)(int64_t)cnt[i]);
-  }
 }
 
 int grid_for(int64_t n, int threads) {
@@ -142,58 +154,55 @@ StreamSplit plan_stream(int64_t L, int64_t per_layer) {
   return s;
 }
 
-hipError_t launch_hist_clear(int32_t* slot, int64_t LE, int64_t* n_invalid, int64_t L, hipStream_t stream) {
-  hist_clear_kernel<<<grid_for(LE > L ? LE : L, 256), 256, 0, stream>>>(slot, LE, n_invalid, L);
+hipError_t launch_hist_prep(int32_t* ring, int64_t LE, int32_t W, int64_t cur, int64_t* load, int64_t* n_invalid,
+                            int64_t L, hipStream_t stream) {
+  hist_prep_kernel<<<grid_for(LE > L ? LE : L, 256), 256, 0, stream>>>(ring, LE, W, cur, load, n_invalid, L);
   return hipGetLastError();
 }
 
-hipError_t launch_window_sum(const int32_t* ring, int64_t LE, int32_t W, int64_t* load, hipStream_t stream) {
-  window_sum_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(ring, LE, W, load);
+hipError_t launch_ema_prep(int32_t* cnt, int64_t LE, int32_t shift, int64_t* ema, int64_t* n_invalid, int64_t L,
+                           hipStream_t stream) {
+  ema_prep_kernel<<<grid_for(LE > L ? LE : L, 256), 256, 0, stream>>>(cnt, LE, shift, ema, n_invalid, L);
   return hipGetLastError();
 }
 
-hipError_t launch_ema_update(const int32_t* cnt, int64_t LE, int32_t shift, int64_t* ema, hipStream_t stream) {
-  ema_update_kernel<<<grid_for(LE, 256), 256, 0, stream>>>(cnt, LE, shift, ema);
-  return hipGetLastError();
-}
+namespace {
 
-// Clear `slot` ([L][E]) and `n_invalid`, then count the step's ids into them.
-hipError_t launch_count(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
-                        int32_t* slot, int64_t* n_invalid, hipStream_t stream) {
-  const int64_t LE = L * (int64_t)E;
-  hipError_t err = launch_hist_clear(slot, LE, n_invalid, L, stream);
-  if (err != hipSuccess) return err;
-
+// Count the step's ids into `slot` ([L][E], cleared) and add them to `acc`
+// ([L][E] int64) and `n_invalid`.
+hipError_t launch_count(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* slot,
+                        int64_t* acc, int64_t* n_invalid, hipStream_t stream) {
   const int64_t per_layer = T * (int64_t)K;
-  if (per_layer > 0) {
-    const StreamSplit sp = plan_stream(L, per_layer);
-    int copies = 16;
-    while (copies > 1 && (int64_t)copies * (E + 1) * 4 > 32 * 1024) copies >>= 1;
-    const size_t lds = (size_t)copies * (E + 1) * sizeof(int32_t);
-    const int64_t blocks = L * sp.chunks;
-    hist_count_kernel<<<(unsigned)blocks, kStreamThreads, lds, stream>>>(idx, sp, E, copies, slot, n_invalid);
-    err = hipGetLastError();
-  }
-  return err;
+  if (per_layer == 0) return hipSuccess;
+  const StreamSplit sp = plan_stream(L, per_layer);
+  int copies = 16;
+  while (copies > 1 && (int64_t)copies * (E + 1) * 4 > 32 * 1024) copies >>= 1;
+  const size_t lds = (size_t)copies * (E + 1) * sizeof(int32_t);
+  const int64_t blocks = L * sp.chunks;
+  hist_count_kernel<<<(unsigned)blocks, kStreamThreads, lds, stream>>>(idx, sp, E, copies, slot, acc, n_invalid);
+  return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                        int32_t* ring, int32_t W, int64_t step, int64_t* load,
                        int64_t* n_invalid, hipStream_t stream) {
   if (L == 0) return hipSuccess;
   const int64_t LE = L * (int64_t)E;
-  hipError_t err = launch_count(idx, L, T, K, E, ring + (step % W) * LE, n_invalid, stream);
+  const int64_t cur = step % W;
+  hipError_t err = launch_hist_prep(ring, LE, W, cur, load, n_invalid, L, stream);
   if (err != hipSuccess) return err;
-  return launch_window_sum(ring, LE, W, load, stream);
+  return launch_count(idx, L, T, K, E, ring + cur * LE, load, n_invalid, stream);
 }
 
 hipError_t launch_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                            int32_t* cnt, int32_t shift, int64_t* ema, int64_t* n_invalid,
                            hipStream_t stream) {
   if (L == 0) return hipSuccess;
-  hipError_t err = launch_count(idx, L, T, K, E, cnt, n_invalid, stream);
+  hipError_t err = launch_ema_prep(cnt, L * (int64_t)E, shift, ema, n_invalid, L, stream);
   if (err != hipSuccess) return err;
-  return launch_ema_update(cnt, L * (int64_t)E, shift, ema, stream);
+  return launch_count(idx, L, T, K, E, cnt, ema, n_invalid, stream);
 }
 
 }  // namespace eplb
