@@ -398,7 +398,8 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
 // (16-byte aligned): the sorted words, the run's updated words, the histogram.
 constexpr int kWideMinPacks = 17;      // one register per lane: from here on the words are searched in LDS
 
-__device__ __forceinline__ int wave_excl_carry_scan(int v, int& carry) {   // inclusive scan + running carry
+// inclusive prefix sum over the lanes plus `carry`, which becomes the total so far
+__device__ __forceinline__ int wave_incl_sum_carry(int v, int& carry) {
   const int incl = wave_incl_sum(v) + carry;
   carry = rdl(incl, 63);
   return incl;
@@ -466,7 +467,7 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
 #pragma unroll
       for (int r = 0; r < K; ++r) {
         const int p = r * 64 + lane;
-        const int below = wave_excl_carry_scan(hist[p], carry);   // run packs with q_t <= p
+        const int below = wave_incl_sum_carry(hist[p], carry);   // run packs with q_t <= p
         pos[r] = (r == 0 && lane < mb) ? q - mb + crun : p - mb + below;
       }
       wave_lds_sync();
