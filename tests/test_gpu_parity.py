@@ -429,6 +429,55 @@ def test_fused_ragged(L, T, K, E):
     assert_same("counts again", host(ring[1]).astype(np.int64), cnt)
 
 
+def test_stream_entries_fuzz():
+    """40 random shapes through every streaming entry (histogram + window,
+    redirect, fused histogram + redirect, moving average, fused moving
+    average + redirect): ragged and empty layers, ids out of range, stale
+    ring slots, odd window positions, against the oracle."""
+    rng = np.random.default_rng(99)
+    for case in range(40):
+        L = int(rng.integers(1, 7))
+        T = int(rng.choice([0, 1, 3, int(rng.integers(1, 6000))]))
+        K = int(rng.integers(1, 10))
+        E = int(rng.choice([1, 2, 7, 64, 256, int(rng.integers(1, 700))]))
+        W = int(rng.integers(1, 6))
+        step = int(rng.integers(0, 50))
+        X = int(rng.integers(1, 6))
+        shift = int(rng.integers(0, 8))
+        note(f"stream fuzz {case}: L={L} T={T} K={K} E={E} W={W} step={step} X={X}")
+        idx_h = rng.integers(-2, E + 2, size=(L, T, K)).astype(np.int32)
+        logcnt = rng.integers(-1, X + 2, size=(L, E)).astype(np.int32)
+        log2phy = rng.integers(0, 5000, size=(L, E, X)).astype(np.int32)
+        ring_h = rng.integers(0, 1000, size=(W, L, E)).astype(np.int32)        # stale slots
+        cnt, invl = ora.load_hist(idx_h, E)
+        others = ring_h.astype(np.int64).sum(axis=0) - ring_h[step % W]
+        idx_d, l2p_d, cnt_d = gpu(idx_h), gpu(log2phy), gpu(logcnt)
+        ring = gpu(ring_h)
+        load, bad = eplb.load_hist(idx_d, E, ring, step)
+        torch.cuda.synchronize()
+        assert_same("slot", host(ring[step % W]).astype(np.int64), cnt)
+        assert_same("window", host(load), others + cnt)
+        assert_same("invalid", host(bad), invl)
+        want = ora.redirect(idx_h, log2phy, logcnt)
+        assert_same("redirect", host(eplb.redirect(idx_d, l2p_d, cnt_d)), want)
+        ring = gpu(ring_h)
+        load, bad, out = eplb.hist_redirect(idx_d, E, ring, step, l2p_d, cnt_d)
+        torch.cuda.synchronize()
+        assert_same("fused window", host(load), others + cnt)
+        assert_same("fused redirect", host(out), want)
+        ema_h = rng.integers(-(1 << 40), 1 << 40, size=(L, E)).astype(np.int64)
+        ema = gpu(ema_h)
+        ema, count, bad = eplb.load_ema(idx_d, E, ema, shift)
+        torch.cuda.synchronize()
+        assert_same("ema", host(ema), ora.ema_update(ema_h, cnt, shift).reshape(L, E))
+        assert_same("ema count", host(count).astype(np.int64), cnt)
+        ema = gpu(ema_h)
+        ema, count, bad, out = eplb.ema_redirect(idx_d, E, ema, shift, l2p_d, cnt_d)
+        torch.cuda.synchronize()
+        assert_same("fused ema", host(ema), ora.ema_update(ema_h, cnt, shift).reshape(L, E))
+        assert_same("fused ema redirect", host(out), want)
+
+
 @pytest.mark.parametrize("work", [wl.TINY_HIER, wl.DSV3_PREFILL], ids=lambda w: w.name)
 def test_fused_serving_loop(work):
     """A serving loop: step s is redirected with the placement from the window
