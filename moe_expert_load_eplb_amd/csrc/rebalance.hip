@@ -733,7 +733,7 @@ struct Smem {
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
   int32_t* rcls;   // [nscr][Rn]  per wave: class of each replica
   int32_t* nflag;  // [Np]  step-3 key form: 2 one word per pack, 1 64-bit sums, 0 128-bit sums
-  int32_t* flags;  // [4]
+  int32_t* flags;  // [4]  [0]: problem status; [2..3]: the total load (u64, 8-byte aligned)
 };
 
 __device__ Smem carve(unsigned char* base, const RbPlan& p) {
@@ -1018,7 +1018,10 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
   const int lane = lane_id();
 
   // ---- loads, range check
-  if (tid == 0) s.flags[0] = 0;
+  if (tid == 0) {
+    s.flags[0] = 0;
+    *reinterpret_cast<u64*>(s.flags + 2) = 0;
+  }
   __syncthreads();
   const int64_t* row = load + b * p.E;
   for (int e = tid; e < p.E; e += NT) {
@@ -1040,28 +1043,40 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
   if (p.gpn == 1) {
     for (int g = tid; g < p.Gp; g += NT) { s.gnode[g] = g; s.gslot[g] = 0; }
   } else {
+    u64* total = reinterpret_cast<u64*>(s.flags + 2);
     for (int g = wid; g < p.Gp; g += NW) {
       u64 sum = 0;
       for (int j = lane; j < p.S; j += 64) sum += s.w[g * p.S + j];
       sum = wave_sum64(sum);
-      if (lane == 0) s.gsum[g] = sum;
-    }
-    __syncthreads();
-    // heaviest first, equal loads in ascending group index (rank by counting)
-    for (int g = tid; g < p.Gp; g += NT) {
-      const u64 wg = s.gsum[g];
-      int rank = 0;
-      for (int h = 0; h < p.Gp; ++h) {
-        const u64 wh = s.gsum[h];
-        rank += (wh > wg || (wh == wg && h < g)) ? 1 : 0;
+      if (lane == 0) {
+        s.gsum[g] = sum;
+        atomicAdd(reinterpret_cast<unsigned long long*>(total), (unsigned long long)sum);
       }
-      s.gord[rank] = g;
     }
     __syncthreads();
+    // heaviest first, equal loads in ascending group index (rank by counting):
+    // by wave 0 itself for up to 64 groups, else by the whole workgroup
+    auto rank_groups = [&](int g0, int gstep) {
+      for (int g = g0; g < p.Gp; g += gstep) {
+        const u64 wg = s.gsum[g];
+        int rank = 0;
+        for (int h = 0; h < p.Gp; ++h) {
+          const u64 wh = s.gsum[h];
+          rank += (wh > wg || (wh == wg && h < g)) ? 1 : 0;
+        }
+        s.gord[rank] = g;
+      }
+    };
+    if (p.Gp > 64) {
+      rank_groups(tid, NT);
+      __syncthreads();
+    }
     if (wid == 0) {
-      u64 tot = 0;
-      for (int g = lane; g < p.Gp; g += 64) tot += s.gsum[g];
-      tot = wave_sum64(tot);
+      if (p.Gp <= 64) {
+        rank_groups(lane, 64);
+        wave_lds_sync();
+      }
+      const u64 tot = *total;
       const bool words = tot < (1ull << 48) - 1 && p.Np <= 256 && p.gpn <= 255;
       const u64* gsum = s.gsum;
       const int32_t* gord = s.gord;
@@ -1232,7 +1247,7 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.o_rcls = take(4ll * nscr * rn1, 4);
   if (off < end1) off = end1;
   p.o_nflag = take(4ll * Np, 4);
-  p.o_flags = take(16, 4);
+  p.o_flags = take(16, 8);
   off = (off + 15) / 16 * 16;
   if (off > kMaxLdsBytes) return EPLB_E_LIMIT;
   p.lds_bytes = (int32_t)off;
