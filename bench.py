@@ -49,6 +49,8 @@ def main() -> int:
     ap.add_argument("--cpu-layers", type=int, default=16,
                     help="layers of one step the oracle baseline histograms and redirects")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("serving",), default=None,
+                    help="run one phase alone (for a kernel trace of it) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs the path on a single MI355X "
@@ -66,7 +68,7 @@ def main() -> int:
     work = wl.STREAM_1M
     pl = work.placement
     L, T, K, E, W = work.layers, work.tokens, work.topk, pl.E, work.window
-    X = pl.max_count
+    X = eplb.max_count(E, pl.P, pl.G, pl.N)
     ids = L * T * K
     hist_bytes = 4 * ids
     redir_bytes = 8 * ids
@@ -98,19 +100,32 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
-    # warm-up: fills the window once and more
-    nwarm = max(args.warmup, W)
-    for s in range(nwarm):
+    # set-up: the window is filled with its W steps (histogram only), so the
+    # first timed rebalance sees a full window; then W' = --warmup untimed
+    # steps of the whole path
+    for s in range(W):
+        eplb.load_hist(steps[s], E, ring, s, load, n_invalid)
+    nfill = W
+    nwarm = args.warmup
+    for s in range(nfill, nfill + nwarm):
         step(s)
+    eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
     torch.cuda.synchronize()
     assert int(status.sum()) == 0, "rebalance reported a failed problem"
+    s_next = nfill + nwarm
+
+    if args.only == "serving":
+        rec = serving_loop(eplb, steps, E, ring, load, n_invalid, placement, out, pl, X, stream, s_next,
+                           args.steps, max(args.warmup, 3), redir_bytes)
+        print(json.dumps({"phase": "serving", "workload": work.name, **rec}), flush=True)
+        return 0
 
     # timed region: K steps, per-call HIP events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(nwarm + i, evs[i])
+        step(s_next + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     hist_ms = [e[0].elapsed_time(e[1]) for e in evs]
@@ -153,20 +168,8 @@ def main() -> int:
 
     # serving-loop step: one fused pass (count this step + redirect it with the
     # placement in force), then the rebalance that gives the next placement
-    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        s_ = nwarm + args.steps + i
-        e = sevs[i]
-        e[0].record(stream)
-        eplb.hist_redirect(steps[s_ % W], E, ring, s_, log2phy, logcnt, load, n_invalid, out)
-        e[1].record(stream)
-        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    serve_wall = time.perf_counter() - t0
-    fused_ms = [e[0].elapsed_time(e[1]) for e in sevs]
+    serving = serving_loop(eplb, steps, E, ring, load, n_invalid, placement, out, pl, X, stream,
+                           s_next + args.steps, args.steps, max(args.warmup, 3), redir_bytes)
 
     # the moving-average estimator instead of the window (count + EMA update),
     # and the per-rank load / imbalance of the placement in force
@@ -238,6 +241,30 @@ def main() -> int:
                                                        sk.placement.N, sk.placement.RK),
     }
 
+    # the same stream redirected through a placement of the global-policy
+    # decode shape (E=256, P=320 on 5 nodes x 8: up to 65 copies of an
+    # expert, X = 65) computed from the same window
+    gpl = wl.GLOBAL_DECODE.placement
+    Xg = eplb.max_count(E, gpl.P, gpl.G, gpl.N)
+    gplace = eplb.rebalance(load, gpl.P, gpl.G, gpl.N, gpl.RK, Xg)
+    torch.cuda.synchronize()
+    assert int(gplace[3].abs().sum()) == 0
+    gevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        gevs[i][0].record(stream)
+        eplb.redirect(steps[i % W], gplace[1], gplace[2], out=out)
+        gevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    g_ms = sum(e[0].elapsed_time(e[1]) for e in gevs) / args.steps
+    redirect_global_placement = {
+        "what": "eplb_redirect of the stream through the global-decode-shaped placement of the same window",
+        "placement": f"E={E} G={gpl.G} N={gpl.N} RK={gpl.RK} P={gpl.P} (global), X={Xg}",
+        "max_logcnt": int(gplace[2].max()),
+        "ms": round(g_ms, 4),
+        "GBps": round(redir_bytes / (g_ms * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(redir_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
     # a plain device-to-device copy of one step's ids (torch), for comparison
     # and as the known-size kernel that calibrates the HBM byte counters
     cal = torch.empty_like(steps[0])
@@ -263,6 +290,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": nwarm,
+        "window_fill_steps": nfill,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -285,14 +313,8 @@ def main() -> int:
             "step_ms_events": round(avg(step_ms), 4),
             "torch_d2d_copy_GBps": round(copy_gbs, 1),
         },
-        "serving_step": {
-            "what": "eplb_hist_redirect (count step s, redirect it with the placement in force) + eplb_rebalance",
-            "ms_per_step": round(serve_wall * 1e3 / args.steps, 4),
-            "fused_ms": round(avg(fused_ms), 4),
-            "fused_GBps": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9, 1),
-            "fused_frac_of_peak": round(redir_bytes / (avg(fused_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_step": redir_bytes,
-        },
+        "serving_step": serving,
+        "redirect_global_placement": redirect_global_placement,
         "load_ema": {
             "what": "eplb_load_ema (count the step, ema <- ema - (ema >> 4) + count)",
             "ms": round(avg(ema_ms), 4),
@@ -341,6 +363,53 @@ def main() -> int:
                                               placement, hist_bytes + redir_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def serving_loop(eplb, steps, E, ring, load, n_invalid, placement, out, pl, X, stream, s0, nsteps, nwarm,
+                 redir_bytes):
+    """The serving order: each step one fused pass (count step s into the
+    window and redirect it with the placement in force), then the rebalance
+    that gives the next step's placement.  `nwarm` untimed steps first (the
+    GPU leaves its idle clocks before the timed ones), then `nsteps` timed
+    ones: host clock around them, HIP events around each fused pass."""
+    import torch
+    W = len(steps)
+    phy2log, log2phy, logcnt, status = placement
+
+    def one(s_, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        eplb.hist_redirect(steps[s_ % W], E, ring, s_, log2phy, logcnt, load, n_invalid, out)
+        if ev is not None:
+            ev[1].record(stream)
+        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(nwarm):
+        one(s0 + i)
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsteps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        one(s0 + nwarm + i, sevs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms = [e[0].elapsed_time(e[1]) for e in sevs]
+    reb_ms = [e[1].elapsed_time(e[2]) for e in sevs]
+    mean = sum(fused_ms) / len(fused_ms)
+    return {
+        "what": "eplb_hist_redirect (count step s, redirect it with the placement in force) + eplb_rebalance",
+        "warmup_steps": nwarm,
+        "ms_per_step": round(wall * 1e3 / nsteps, 4),
+        "fused_ms": round(mean, 4),
+        "fused_ms_median": round(statistics.median(fused_ms), 4),
+        "fused_ms_first_last": [round(fused_ms[0], 4), round(fused_ms[-1], 4)],
+        "rebalance_ms": round(sum(reb_ms) / len(reb_ms), 4),
+        "fused_GBps": round(redir_bytes / (mean * 1e-3) / 1e9, 1),
+        "fused_frac_of_peak": round(redir_bytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": redir_bytes,
+    }
 
 
 def _loaded_hip_runtime() -> str:

@@ -27,6 +27,12 @@
  *     output buffers do not overlap.
  *   - A non-zero return code means nothing was enqueued (EPLB_E_HIP: a launch
  *     failed and earlier kernels of the same call may have run).
+ *   - Outputs must not share a byte with the inputs or with each other where
+ *     a call says so; the check compares address ranges and returns
+ *     EPLB_E_ARG.
+ *   - One call takes at most 2^22 layers (streaming calls) or 2^22 problems
+ *     (rebalance-like calls), else EPLB_E_LIMIT, so that each launch stays
+ *     below 2^32 work-items.
  *   - Conditions only the device can see are reported through output
  *     arguments (`n_invalid`, `status`), never by faulting.
  */
@@ -70,8 +76,8 @@ extern "C" {
  * place experts identically.
  *
  *   idx        [L][T][K] int32   logical expert id of each (layer, token, k)
- *   L, T, K                      layers, tokens, top-k (L, T >= 0, K >= 1,
- *                                T * K < 2^31)
+ *   L, T, K                      layers, tokens, top-k (0 <= L <= 2^22,
+ *                                T >= 0, K >= 1, T * K < 2^31)
  *   E                            logical experts per layer (1 .. 4096)
  *   ring       [W][L][E] int32   caller-owned history of per-step counts.
  *                                Zero it once before the first step; this
@@ -114,9 +120,10 @@ int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
  * load per replica goes to the lowest node-local expert index; one item per
  * pack is the identity assignment.
  *
- * Errors: EPLB_E_ARG (a size < 1, B < 0, or a NULL array), EPLB_E_DIV
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, or an output sharing
+ * a byte with the input or another output), EPLB_E_DIV
  * (E % G on the hierarchical path, RK % N', P % RK), EPLB_E_REDUNDANCY
- * (P < E), EPLB_E_CAPACITY (X too small), EPLB_E_LIMIT (E > 4096,
+ * (P < E), EPLB_E_CAPACITY (X too small), EPLB_E_LIMIT (B > 2^22, E > 4096,
  * P > 8192, X > 65535, more than 512 experts or 512 GPUs on one node (the
  * global policy counts all of them as one node), more than 512 nodes, a
  * possible replica count above 16128, or a working set above 64 KiB of
@@ -139,7 +146,8 @@ int32_t eplb_rebalance(const int64_t* load, int64_t B, int32_t E, int32_t P,
  *   idx        [L][T][K] int32   logical ids (as for eplb_load_hist)
  *   log2phy    [L][E][X] int32   from eplb_rebalance
  *   logcnt     [L][E] int32      from eplb_rebalance
- *   out        [L][T][K] int32   out: physical ids; must not overlap idx
+ *   out        [L][T][K] int32   out: physical ids; must not share a byte
+ *                                with idx
  */
 int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                       const int32_t* log2phy, const int32_t* logcnt, int32_t X,
@@ -227,8 +235,10 @@ int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, i
  * A problem with a load outside [0, 2^40], a phy2log entry outside [0, E) or
  * a referenced count below 1 gets NaN in all its outputs.
  *
- * Errors: EPLB_E_ARG (a size out of range or a NULL array), EPLB_E_DIV
- * (P % RK != 0), EPLB_E_HIP.
+ * Errors: EPLB_E_ARG (a size out of range, a NULL array, or an output sharing
+ * a byte with an input or the other output), EPLB_E_DIV (P % RK != 0),
+ * EPLB_E_LIMIT (E > 4096, so that the int64 total of the loads, at most
+ * E * 2^40, is exact as a double; B > 2^22), EPLB_E_HIP.
  */
 int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
                             int64_t B, int32_t E, int32_t P, int32_t RK,
@@ -270,11 +280,11 @@ int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const i
  *   moves        [B][3] int32    out: copies from the same rank, the same
  *                                node, another node
  *   status       [B] int32       out: EPLB_S_OK or EPLB_S_BAD_MAP
- * Outputs must not overlap the inputs.
+ * No output may share a byte with an input or another output.
  *
- * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output equal to an
- * input), EPLB_E_DIV (P % RK, RK % N), EPLB_E_LIMIT (E > 4096, P > 8192,
- * X > 65535), EPLB_E_HIP.
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output sharing a
+ * byte with an input or another output), EPLB_E_DIV (P % RK, RK % N),
+ * EPLB_E_LIMIT (E > 4096, P > 8192, X > 65535, B > 2^22), EPLB_E_HIP.
  */
 int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, const int32_t* new_log2phy,
                        int64_t B, int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X,
@@ -312,11 +322,13 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
  *                                original of rep[g][j] (0 for empty slots)
  *   rank_load  [B][RK] int64     out: rank loads after the moves (max = lam)
  *   status     [B] int32         out: EPLB_S_OK or EPLB_S_BAD_TOPOLOGY
- * Outputs must not overlap the inputs (with 12 or more ranks rank_load also
- * carries partial results between the call's two launches).
+ * No output may share a byte with an input or another output (with 12 or
+ * more ranks rank_load also carries partial results between the call's two
+ * launches).
  *
- * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output equal to an
- * input), EPLB_E_LIMIT (E > 4096, RK > 16, R > 64), EPLB_E_HIP.
+ * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output sharing a
+ * byte with an input or another output), EPLB_E_LIMIT (E > 4096, RK > 16,
+ * R > 64, B > 2^20 - 1), EPLB_E_HIP.
  */
 int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                       int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,
@@ -347,8 +359,9 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
  *   out        [L][T][K] int32   out: physical ids; must not overlap idx
  *
  * Errors: as for eplb_redirect; EPLB_E_ARG also for RK or R < 1, a NULL
- * array or workspace, or a workspace below the size needed; EPLB_E_LIMIT for
- * RK > 16, R > 64, or more than 2^30 segments of 2048 ids.
+ * array or workspace, a workspace below the size needed, or a workspace
+ * sharing a byte with idx or out; EPLB_E_LIMIT for RK > 16, R > 64, or more
+ * than 2^25 segments of 2048 ids over all layers.
  */
 int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
                          const int64_t* flow, int32_t RK, int32_t R, void* workspace, int64_t workspace_bytes,
@@ -357,6 +370,19 @@ int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, in
 /* Bytes of workspace eplb_lp_redirect needs: L * ceil(T*K / 2048) * E * 4,
  * or a negative EPLB_E_* code.  Host only. */
 int64_t eplb_lp_redirect_workspace_bytes(int64_t L, int64_t T, int32_t K, int32_t E);
+
+/*
+ * eplb_rebalance_max_count -- the largest replica count eplb_rebalance can
+ * give one logical expert, 1 + (P - E) / N' (N' = N if G % N == 0 else 1),
+ * which is the least log2phy width X it accepts, or a negative EPLB_E_*
+ * code (-EPLB_E_ARG for a size < 1, -EPLB_E_DIV for E % G on the
+ * hierarchical path, -EPLB_E_REDUNDANCY for P < E).  Host only.
+ *
+ * Follows: the appendix entry point of Part 2 (log2phy is as wide as the
+ * largest count) and the replication routine (a node adds (P - E) / N'
+ * replicas, at most all of them to one expert).
+ */
+int32_t eplb_rebalance_max_count(int32_t E, int32_t P, int32_t G, int32_t N);
 
 /* Human-readable name of an EPLB_E_* return code or EPLB_S_* status. */
 const char* eplb_status_string(int32_t code);

@@ -35,7 +35,7 @@ EPLB_S_BAD_TOPOLOGY = 19
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
            "eplb_load_ema", "eplb_ema_redirect", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
            "eplb_lp_redirect_workspace_bytes", "eplb_status_string",
-           "eplb_rebalance_lds_bytes")
+           "eplb_rebalance_lds_bytes", "eplb_rebalance_max_count")
 
 
 def _load() -> ctypes.CDLL:
@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.eplb_rebalance_lds_bytes.restype = i64
+    lib.eplb_rebalance_max_count.argtypes = [i32, i32, i32, i32]
+    lib.eplb_rebalance_max_count.restype = i32
     return lib
 
 
@@ -140,9 +142,12 @@ def load_hist(idx: torch.Tensor, E: int, ring: torch.Tensor, step: int,
 
 
 def max_count(E: int, P: int, G: int, N: int) -> int:
-    """Largest replica count a placement can give one expert: 1 + (P - E) / N'."""
-    nodes = N if G % N == 0 else 1
-    return 1 + (P - E) // nodes
+    """Largest replica count a placement can give one expert (the least
+    log2phy width rebalance accepts), from eplb_rebalance_max_count."""
+    n = lib.eplb_rebalance_max_count(int(E), int(P), int(G), int(N))
+    if n < 0:
+        raise EplbError(-n, "eplb_rebalance_max_count")
+    return n
 
 
 def rebalance(load: torch.Tensor, P: int, G: int, N: int, RK: int, X: int | None = None,
@@ -156,7 +161,7 @@ def rebalance(load: torch.Tensor, P: int, G: int, N: int, RK: int, X: int | None
         raise ValueError("load must be [B, E]")
     B, E = load.shape
     if X is None:
-        X = max(1, max_count(E, P, G, N))
+        X = max_count(E, P, G, N)
     dev = load.device
     if out is None:
         out = (torch.empty((B, P), dtype=torch.int32, device=dev),

@@ -7,14 +7,40 @@ using namespace eplb;
 
 namespace {
 
-constexpr int64_t kMaxLayers = int64_t(1) << 24;
 constexpr int64_t kMaxIdsPerLayer = (int64_t(1) << 31) - 1;
 
 int32_t check_stream_args(const void* idx, int64_t L, int64_t T, int32_t K, int32_t E) {
-  if (L < 0 || T < 0 || K < 1 || E < 1 || L > kMaxLayers) return EPLB_E_ARG;
+  if (L < 0 || T < 0 || K < 1 || E < 1) return EPLB_E_ARG;
   if (L > 0 && T > 0 && idx == nullptr) return EPLB_E_ARG;
-  if (E > kMaxE) return EPLB_E_LIMIT;
+  if (E > kMaxE || L > kMaxLayers) return EPLB_E_LIMIT;
   if (T > kMaxIdsPerLayer / K) return EPLB_E_RANGE;
+  return EPLB_OK;
+}
+
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// A call with B problems and these input and output ranges: every pointer
+// set, no output sharing a byte with an input or another output.
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+template <int NI, int NO>
+int32_t check_buffers(const Range (&in)[NI], const Range (&out)[NO]) {
+  for (const Range& a : in)
+    if (a.p == nullptr) return EPLB_E_ARG;
+  for (int i = 0; i < NO; ++i) {
+    if (out[i].p == nullptr) return EPLB_E_ARG;
+    for (const Range& c : in)
+      if (overlap(out[i].p, out[i].bytes, c.p, c.bytes)) return EPLB_E_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlap(out[i].p, out[i].bytes, out[j].p, out[j].bytes)) return EPLB_E_ARG;
+  }
   return EPLB_OK;
 }
 
@@ -37,13 +63,18 @@ int32_t eplb_rebalance(const int64_t* load, int64_t B, int32_t E, int32_t P,
                        int32_t G, int32_t N, int32_t RK, int32_t X,
                        int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
                        int32_t* status, void* stream) {
-  if (B < 0 || B > (int64_t(1) << 31) - 1) return EPLB_E_ARG;
+  if (B < 0) return EPLB_E_ARG;
   RbPlan plan;
   int32_t rc = rb_make_plan(E, P, G, N, RK, X, &plan);
   if (rc != EPLB_OK) return rc;
-  if (B > 0 && (load == nullptr || phy2log == nullptr || log2phy == nullptr || logcnt == nullptr ||
-                status == nullptr))
-    return EPLB_E_ARG;
+  if (B > kMaxProblems) return EPLB_E_LIMIT;
+  if (B > 0) {
+    const Range in[1] = {{load, B * E * 8}};
+    const Range out[4] = {{phy2log, B * P * 4}, {log2phy, B * E * (int64_t)X * 4}, {logcnt, B * E * 4},
+                          {status, B * 4}};
+    rc = check_buffers(in, out);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_rebalance(load, B, plan, phy2log, log2phy, logcnt, status, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
@@ -56,7 +87,7 @@ int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
   if (X < 1) return EPLB_E_ARG;
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (L > 0 && T > 0 && (const void*)out == (const void*)idx) return EPLB_E_ARG;
+  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
   hipError_t err = launch_redirect(idx, L, T, K, E, log2phy, logcnt, X, out, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
@@ -71,7 +102,7 @@ int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && (ring == nullptr || load == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (L > 0 && T > 0 && (const void*)out == (const void*)idx) return EPLB_E_ARG;
+  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
   hipError_t err = launch_hist_redirect(idx, L, T, K, E, ring, W, step, load, n_invalid, log2phy, logcnt, X,
                                         out, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -96,7 +127,7 @@ int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, i
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && (count == nullptr || ema == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (L > 0 && T > 0 && (const void*)out == (const void*)idx) return EPLB_E_ARG;
+  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
   hipError_t err = launch_ema_redirect(idx, L, T, K, E, count, shift, ema, n_invalid, log2phy, logcnt, X, out,
                                        (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -105,11 +136,15 @@ int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, i
 int32_t eplb_placement_load(const int64_t* load, const int32_t* phy2log, const int32_t* logcnt,
                             int64_t B, int32_t E, int32_t P, int32_t RK,
                             double* rank_load, double* imbalance, void* stream) {
-  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || P < 1 || RK < 1) return EPLB_E_ARG;
+  if (B < 0 || E < 1 || P < 1 || RK < 1) return EPLB_E_ARG;
   if (P % RK != 0) return EPLB_E_DIV;
-  if (B > 0 && (load == nullptr || phy2log == nullptr || logcnt == nullptr || rank_load == nullptr ||
-                imbalance == nullptr))
-    return EPLB_E_ARG;
+  if (E > kMaxE || B > kMaxProblems) return EPLB_E_LIMIT;    // E * 2^40 < 2^53: the total is exact as a double
+  if (B > 0) {
+    const Range in[3] = {{load, B * E * 8}, {phy2log, B * P * 4}, {logcnt, B * E * 4}};
+    const Range out[2] = {{rank_load, B * RK * 8}, {imbalance, B * 8}};
+    const int32_t rc = check_buffers(in, out);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_placement_load(load, phy2log, logcnt, B, E, P, RK, rank_load, imbalance,
                                          (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -119,19 +154,15 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
                        int64_t B, int32_t E, int32_t P, int32_t RK, int32_t N, int32_t X,
                        int32_t* phy2log, int32_t* log2phy, int32_t* src, int32_t* moves, int32_t* status,
                        void* stream) {
-  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || P < 1 || RK < 1 || N < 1 || X < 1) return EPLB_E_ARG;
+  if (B < 0 || E < 1 || P < 1 || RK < 1 || N < 1 || X < 1) return EPLB_E_ARG;
   if (P % RK != 0 || RK % N != 0) return EPLB_E_DIV;
-  if (E > kMaxE || P > kMaxP || X > kMaxX) return EPLB_E_LIMIT;
+  if (E > kMaxE || P > kMaxP || X > kMaxX || B > kMaxProblems) return EPLB_E_LIMIT;
   if (B > 0) {
-    const void* in[3] = {old_phy2log, new_phy2log, new_log2phy};
-    const void* out[5] = {phy2log, log2phy, src, moves, status};
-    for (const void* a : in)
-      if (a == nullptr) return EPLB_E_ARG;
-    for (const void* a : out) {
-      if (a == nullptr) return EPLB_E_ARG;
-      for (const void* c : in)
-        if (a == c) return EPLB_E_ARG;
-    }
+    const int64_t l2p = B * E * (int64_t)X * 4;
+    const Range in[3] = {{old_phy2log, B * P * 4}, {new_phy2log, B * P * 4}, {new_log2phy, l2p}};
+    const Range out[5] = {{phy2log, B * P * 4}, {log2phy, l2p}, {src, B * P * 4}, {moves, B * 12}, {status, B * 4}};
+    const int32_t rc = check_buffers(in, out);
+    if (rc != EPLB_OK) return rc;
   }
   hipError_t err = launch_rearrange(old_phy2log, new_phy2log, new_log2phy, B, E, P, RK, N, X, phy2log, log2phy,
                                     src, moves, status, (hipStream_t)stream);
@@ -141,18 +172,14 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
 int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
                       int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load, int32_t* status,
                       void* stream) {
-  if (B < 0 || B > (int64_t(1) << 31) - 1 || E < 1 || RK < 1 || R < 1) return EPLB_E_ARG;
-  if (E > kMaxE || RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
+  if (B < 0 || E < 1 || RK < 1 || R < 1) return EPLB_E_ARG;
+  if (E > kMaxE || RK > kLpMaxRanks || R > kLpMaxSlots || B > kLpMaxProblems) return EPLB_E_LIMIT;
   if (B > 0) {
-    const void* in[3] = {cnt, home, rep};
-    const void* out[4] = {lam, flow, rank_load, status};
-    for (const void* a : in)
-      if (a == nullptr) return EPLB_E_ARG;
-    for (const void* a : out) {
-      if (a == nullptr) return EPLB_E_ARG;
-      for (const void* c : in)
-        if (a == c) return EPLB_E_ARG;
-    }
+    const int64_t slots = B * RK * (int64_t)R;
+    const Range in[3] = {{cnt, B * E * 8}, {home, B * E * 4}, {rep, slots * 4}};
+    const Range out[4] = {{lam, B * 8}, {flow, slots * 8}, {rank_load, B * RK * 8}, {status, B * 4}};
+    const int32_t rc = check_buffers(in, out);
+    if (rc != EPLB_OK) return rc;
   }
   hipError_t err = launch_lp_solve(cnt, home, rep, B, E, RK, R, lam, flow, rank_load, status, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -172,15 +199,27 @@ int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, in
   if (RK < 1 || R < 1) return EPLB_E_ARG;
   if (RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
   const int64_t n = T * (int64_t)K;
-  if (L * lp_segments(n) > (int64_t(1) << 30)) return EPLB_E_LIMIT;
+  if (L * lp_segments(n) > kLpMaxSegments) return EPLB_E_LIMIT;
   if (L > 0 && n > 0) {
     if (rep == nullptr || flow == nullptr || out == nullptr || workspace == nullptr) return EPLB_E_ARG;
-    if ((const void*)out == (const void*)idx) return EPLB_E_ARG;
-    if (workspace_bytes < eplb_lp_redirect_workspace_bytes(L, T, K, E)) return EPLB_E_ARG;
+    const int64_t need = eplb_lp_redirect_workspace_bytes(L, T, K, E);
+    if (workspace_bytes < need) return EPLB_E_ARG;
+    if (overlap(out, L * n * 4, idx, L * n * 4) || overlap(workspace, need, idx, L * n * 4) ||
+        overlap(workspace, need, out, L * n * 4))
+      return EPLB_E_ARG;
   }
   hipError_t err = launch_lp_redirect(idx, L, n, E, rep, flow, RK, R, static_cast<int32_t*>(workspace), out,
                                       (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
+}
+
+int32_t eplb_rebalance_max_count(int32_t E, int32_t P, int32_t G, int32_t N) {
+  if (E < 1 || P < 1 || G < 1 || N < 1) return -EPLB_E_ARG;
+  const bool hier = G % N == 0;
+  if (hier && E % G != 0) return -EPLB_E_DIV;
+  if (P < E) return -EPLB_E_REDUNDANCY;
+  const int32_t nodes = hier ? N : 1;
+  return 1 + (P - E) / nodes;
 }
 
 int64_t eplb_rebalance_lds_bytes(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int32_t X) {

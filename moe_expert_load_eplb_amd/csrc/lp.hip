@@ -412,27 +412,29 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
   for (int c = lane; c < C; c += 64) dst[c] = cnt[c];
 }
 
-// One wave per (layer, compact number): the segments' counts, 64 segments
-// per pass, become exclusive prefixes by a wave scan.
+// One wave per (layer, compact number), grid-stride over them: the
+// segments' counts, 64 segments per pass, become exclusive prefixes by a
+// wave scan.
 __global__ __launch_bounds__(256) void lp_seg_scan_kernel(int32_t* __restrict__ seg, int64_t L, int64_t S,
                                                           int32_t C) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  if (t >= L * C) return;                              // whole wave
-  const int64_t l = t / C, c = t - l * C;
-  int32_t* p = seg + l * S * C + c;
-  int32_t carry = 0;
-  for (int64_t s0 = 0; s0 < S; s0 += 64) {
-    const int64_t sg = s0 + lane;
-    const int32_t v = sg < S ? p[sg * C] : 0;
-    int32_t incl = v;
+  const int64_t waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; t < L * C; t += waves) {
+    const int64_t l = t / C, c = t - l * C;
+    int32_t* p = seg + l * S * C + c;
+    int32_t carry = 0;
+    for (int64_t s0 = 0; s0 < S; s0 += 64) {
+      const int64_t sg = s0 + lane;
+      const int32_t v = sg < S ? p[sg * C] : 0;
+      int32_t incl = v;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t o = __shfl_up(incl, off);
-      incl += lane >= off ? o : 0;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        incl += lane >= off ? o : 0;
+      }
+      if (sg < S) p[sg * C] = carry + incl - v;
+      carry += __shfl(incl, 63);
     }
-    if (sg < S) p[sg * C] = carry + incl - v;
-    carry += __shfl(incl, 63);
   }
 }
 
@@ -511,7 +513,8 @@ hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t 
       idx, n, E, rep, RKR, C, S, LS, wpb_a, seg);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  lp_seg_scan_kernel<<<(unsigned)((L * C + 3) / 4), 256, 0, stream>>>(seg, L, S, C);
+  const int64_t scan_blocks = (L * C + 3) / 4;         // four waves per workgroup, grid-stride beyond 2^16
+  lp_seg_scan_kernel<<<(unsigned)(scan_blocks < 65536 ? scan_blocks : 65536), 256, 0, stream>>>(seg, L, S, C);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int wpb_c = lp_waves_per_block(E + 3 * C);
@@ -524,7 +527,7 @@ hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
                            int32_t* status, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  if (RK < kLpSplitRanks || B > ((int64_t)1 << 31) / kLpParts - 1) {
+  if (RK < kLpSplitRanks) {
     lp_solve_kernel<0><<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, 1, lam, flow, rank_load,
                                                                status);
     return hipGetLastError();

@@ -83,6 +83,19 @@ def policy(num_groups: int, num_nodes: int) -> tuple[int, int, bool]:
     return 1, 1, False
 
 
+def max_count(E: int, P: int, G: int, N: int) -> int:
+    """Largest replica count the policy can give one logical expert.
+
+    Within a node the replication step adds Pn - En = (P - E) / nodes
+    replicas; at most all of them go to one expert, which then has 1 + that
+    many copies ([EPLB-ru] appendix: the replication function's output width,
+    and the entry point's log2phy sized by the largest count).  ``nodes`` is
+    the policy's node count (1 on the global path).
+    """
+    _, Np, _ = policy(G, N)
+    return 1 + (P - E) // Np
+
+
 def argument_error(E: int, P: int, G: int, N: int, RK: int, X: int) -> str | None:
     """Name the first argument rule a rebalance call breaks, or None.
 

@@ -17,6 +17,7 @@ int main(void) {
       (any_fn)&eplb_rearrange,     (any_fn)&eplb_lp_solve,
       (any_fn)&eplb_lp_redirect,   (any_fn)&eplb_lp_redirect_workspace_bytes,
       (any_fn)&eplb_status_string, (any_fn)&eplb_rebalance_lds_bytes,
+      (any_fn)&eplb_rebalance_max_count,
   };
   size_t i;
   for (i = 0; i < sizeof fns / sizeof fns[0]; ++i) {
@@ -29,6 +30,8 @@ int main(void) {
   if (eplb_lp_redirect_workspace_bytes(58, 16384, 8, 256) != 58LL * 64 * 256 * 4) return 5;
   /* validation happens before any device work */
   if (eplb_rebalance(NULL, 1, 16, 24, 4, 2, 8, 5, NULL, NULL, NULL, NULL, NULL) != EPLB_E_ARG) return 6;
+  /* 288 physical on 4 nodes: 9 copies at most; 8 groups on 5 nodes: global, 65 */
+  if (eplb_rebalance_max_count(256, 288, 8, 4) != 9 || eplb_rebalance_max_count(256, 320, 8, 5) != 65) return 7;
   printf("abi_host ok: %zu entry points\n", sizeof fns / sizeof fns[0]);
   return 0;
 }

@@ -49,6 +49,8 @@ def lib():
     lib.eplb_status_string.restype = ctypes.c_char_p
     lib.eplb_rebalance_lds_bytes.argtypes = [i32] * 6
     lib.eplb_rebalance_lds_bytes.restype = i64
+    lib.eplb_rebalance_max_count.argtypes = [i32] * 4
+    lib.eplb_rebalance_max_count.restype = i32
     return lib
 
 
@@ -57,7 +59,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
                           "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect", "eplb_ema_redirect",
-                          "eplb_lp_redirect_workspace_bytes"}
+                          "eplb_lp_redirect_workspace_bytes", "eplb_rebalance_max_count"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -165,8 +167,9 @@ def test_ema_and_quality_validation(lib):
         assert lib.eplb_load_ema(*args) == code, (pos, bad)
     assert lib.eplb_load_ema(None, 0, 10, 8, 256, None, 62, None, None, None) == 0   # L = 0: nothing to do
     good = [FAKE, FAKE, FAKE, 58, 256, 288, 32, FAKE, FAKE, None]
-    for pos, bad, code in [(3, -1, 1), (3, 1 << 31, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (6, 5, 2),
-                           (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1)]:
+    for pos, bad, code in [(3, -1, 1), (3, (1 << 22) + 1, 5), (4, 0, 1), (4, 4097, 5), (5, 0, 1), (6, 0, 1),
+                           (6, 5, 2), (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1),
+                           (7, FAKE + 8, 1), (8, FAKE + 58 * 32 * 8 - 8, 1)]:
         args = list(good)
         args[pos] = bad
         assert lib.eplb_placement_load(*args) == code, (pos, bad)
@@ -256,8 +259,8 @@ def test_header_is_c99_and_every_entry_point_links(tmp_path):
     exe = _cc(os.path.join(ROOT, "tests", "c", "abi_host.c"), str(tmp_path / "abi_host"), ("-std=c99", "-pedantic"))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
-    assert "abi_host ok: 13 entry points" in r.stdout
-    assert len(declared_functions()) == 13
+    assert "abi_host ok: 14 entry points" in r.stdout
+    assert len(declared_functions()) == 14
 
 
 def test_ema_redirect_validation(lib):
@@ -269,3 +272,64 @@ def test_ema_redirect_validation(lib):
         args = list(good)
         args[pos] = bad
         assert lib.eplb_ema_redirect(*args) == code, (pos, bad)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_max_count_matches_oracle(lib, seed):
+    """eplb_rebalance_max_count is the oracle's capacity bound on random
+    shapes of both policies, and the least X eplb_rebalance accepts."""
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        N = int(rng.integers(1, 9))
+        G = int(rng.integers(1, 17))
+        E = G * int(rng.integers(1, 9)) if rng.random() < 0.8 else int(rng.integers(1, 100))
+        P = E + int(rng.integers(-3, 200))
+        Np = ora.policy(G, N)[1]
+        if P < 1 or P % Np:
+            continue                                   # (the GPU count rules are not this call's)
+        RK = Np
+        err = ora.argument_error(E, P, G, N, RK, 1 << 20)
+        got = lib.eplb_rebalance_max_count(E, P, G, N)
+        if err is not None:
+            assert got == -{"arg": 1, "div": 2, "redundancy": 3}[err], (E, P, G, N)
+            continue
+        want = ora.max_count(E, P, G, N)
+        assert got == want, (E, P, G, N)
+        if want > 1 and lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, want) > 0:
+            assert lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, want - 1) == -4
+    assert lib.eplb_rebalance_max_count(0, 24, 4, 2) == -1
+
+
+def test_launch_size_limits(lib):
+    """Calls that would launch 2^32 work-items or more are refused on the
+    host, before any kernel (and before a window or moving average is
+    touched)."""
+    big = (1 << 22) + 1
+    assert lib.eplb_load_hist(FAKE, big, 1, 1, 8, FAKE, 2, 0, FAKE + 64, FAKE + 128, None) == 5
+    assert lib.eplb_redirect(FAKE, big, 1, 1, 8, FAKE + 64, FAKE + 128, 2, FAKE << 30, None) == 5
+    assert lib.eplb_hist_redirect(FAKE, big, 1, 1, 8, FAKE, 2, 0, FAKE, FAKE, FAKE, FAKE, 2, FAKE << 20, None) == 5
+    assert lib.eplb_load_ema(FAKE, big, 1, 1, 8, FAKE, 2, FAKE, FAKE, None) == 5
+    assert lib.eplb_ema_redirect(FAKE, big, 1, 1, 8, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 2, FAKE << 20, None) == 5
+    F = [FAKE << (4 * i + 4) for i in range(8)]
+    assert lib.eplb_rebalance(F[0], big, 16, 24, 4, 2, 8, 5, F[1], F[2], F[3], F[4], None) == 5
+    assert lib.eplb_rearrange(F[0], F[1], F[2], big, 16, 24, 8, 2, 5, F[3], F[4], F[5], F[6], F[7], None) == 5
+    assert lib.eplb_lp_solve(F[0], F[1], F[2], 1 << 20, 16, 8, 2, F[3], F[4], F[5], F[6], None) == 5
+    # 2^25 segments of 2048 ids: the most one redirect by flows takes
+    assert lib.eplb_lp_redirect(F[0], 1 << 14, 2048 * 2048 + 1, 1, 8, F[1], F[2], 8, 2, F[3], 1 << 62, F[4],
+                                None) == 5
+
+
+def test_overlapping_buffers_rejected(lib):
+    """An output that shares any byte with an input (not only the same
+    pointer) is refused."""
+    n = 2 * 10 * 8 * 4
+    assert lib.eplb_redirect(FAKE, 2, 10, 8, 256, FAKE << 8, FAKE << 9, 9, FAKE + n - 4, None) == 1
+    assert lib.eplb_redirect(FAKE + 4, 2, 10, 8, 256, FAKE << 8, FAKE << 9, 9, FAKE + 4 - n + 4, None) == 1
+    F = [FAKE << (4 * i + 4) for i in range(8)]
+    # rebalance: status inside log2phy
+    assert lib.eplb_rebalance(F[0], 2, 16, 24, 4, 2, 8, 5, F[1], F[2], F[3], F[2] + 8, None) == 1
+    # lp_solve: flow overlapping rep
+    assert lib.eplb_lp_solve(F[0], F[1], F[2], 2, 16, 8, 2, F[3], F[2] + 4, F[5], F[6], None) == 1
+    # lp_redirect: workspace inside out
+    need = lib.eplb_lp_redirect_workspace_bytes(2, 5000, 2, 64)
+    assert lib.eplb_lp_redirect(F[0], 2, 5000, 2, 64, F[1], F[2], 8, 2, F[4] + 16, need, F[4], None) == 1

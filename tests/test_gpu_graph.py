@@ -42,7 +42,7 @@ class Loop:
         self.load = torch.zeros((L, E), dtype=torch.int64, device=DEV)
         self.bad = torch.zeros((L,), dtype=torch.int64, device=DEV)
         self.out = torch.zeros_like(self.idx)
-        X = pl.max_count
+        X = ora.max_count(pl.E, pl.P, pl.G, pl.N)
         # the placement in force before the first step: every expert once, in order, on a uniform load
         self.placement = eplb.rebalance(torch.ones((L, E), dtype=torch.int64, device=DEV), pl.P, pl.G, pl.N, pl.RK, X)
 
@@ -91,6 +91,6 @@ def test_graph_replay_matches_eager(work, tokens, W):
         assert np.array_equal(g[0], ora.redirect(idx_h, prev[1], prev[2]))
         assert np.array_equal(g[1], ora.window_load(hists, W))
         ref = ora.rebalance(g[1], work.placement.P, work.placement.G, work.placement.N, work.placement.RK,
-                            work.placement.max_count)
+                            ora.max_count(work.placement.E, work.placement.P, work.placement.G, work.placement.N))
         assert np.array_equal(g[3], ref["phy2log"]) and np.array_equal(g[5], ref["logcnt"])
         prev = g[3:]

@@ -82,10 +82,10 @@ def test_lp_solve_random(RK, R, E, top):
 @pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE], ids=lambda w: w.name)
 def test_lp_solve_topologies(work):
     """Batches of 16384 tokens x top-8 on the 8-GPU cube (the pages' r2o)
-    and the 16-GPU hypercube: all 58 layers checked, 12 against the oracle."""
+    and the 16-GPU hypercube: all 58 layers against the oracle."""
     idx, home, rep = wl.lp_inputs(work)
     cnt = np.stack([np.bincount(idx[l].ravel(), minlength=work.E) for l in range(work.layers)]).astype(np.int64)
-    q = solve_both(cnt, home, rep, rows=range(0, work.layers, 5))
+    q = solve_both(cnt, home, rep)
     check_solution(cnt, home, rep, q)
     base = np.stack([np.bincount(home[l], weights=cnt[l], minlength=work.RK) for l in range(work.layers)])
     assert (q["lam"] <= base.max(axis=1)).all() and (q["lam"] < base.max(axis=1)).any()
@@ -157,8 +157,8 @@ def test_lp_redirect_bad_layers():
 def test_lp_batch_end_to_end(work):
     """One batch through the whole LPLB-style path on the GPU: per-layer
     counts (eplb_load_hist, W = 1), the solve, the redirect; the redirect
-    matches the oracle on sampled layers, and on every layer the ids each
-    rank ends up serving add up to the solve's rank loads."""
+    matches the oracle on every layer, and on every layer the ids each rank
+    ends up serving add up to the solve's rank loads."""
     idx_h, home, rep = wl.lp_inputs(work)
     L, E, RK = work.layers, work.E, work.RK
     R = rep.shape[2]
@@ -170,8 +170,7 @@ def test_lp_batch_end_to_end(work):
     torch.cuda.synchronize()
     assert int(status.abs().sum()) == 0 and int(bad.sum()) == 0
     out_h, flow_h, load_h = out.cpu().numpy(), flow.cpu().numpy(), rank_load.cpu().numpy()
-    for l in (0, 29, 57):
-        assert_same(f"layer {l}", out_h[l:l + 1], ora.lp_redirect(idx_h[l:l + 1], rep[l:l + 1], flow_h[l:l + 1], E))
+    assert_same("lp_redirect", out_h, ora.lp_redirect(idx_h, rep, flow_h, E))
     rank_of = np.empty((L, E + RK * R), dtype=np.int64)
     rank_of[:, :E] = home
     rank_of[:, E:] = np.repeat(np.arange(RK), R)[None, :]

@@ -56,7 +56,7 @@ def rebalance_both(load, P, G, N, RK, X=None):
     load = np.asarray(load, dtype=np.int64)
     B, E = load.shape
     if X is None:
-        X = eplb.max_count(E, P, G, N)
+        X = ora.max_count(E, P, G, N)
     note(f"rebalance B={B} E={E} P={P} G={G} N={N} RK={RK} X={X}")
     outs = eplb.rebalance(gpu(load), P, G, N, RK, X)
     torch.cuda.synchronize()
@@ -147,22 +147,38 @@ def test_global_decode_full_path():
     assert_same("redirect", out, ora.redirect(steps[-1], ref["log2phy"], ref["logcnt"]))
 
 
+def _oracle_rows(args):
+    load, P, G, N, RK, X = args
+    return ora.rebalance(load, P, G, N, RK, X)
+
+
+def _oracle_rebalance_pool(load, P, G, N, RK, X, parts=16):
+    """The oracle on every row of ``load``, the rows split over a pool of
+    forked host processes (they run Python only and touch no GPU)."""
+    import multiprocessing
+    nw = max(1, min(parts, len(os.sched_getaffinity(0))))
+    chunks = [c for c in np.array_split(np.arange(load.shape[0]), nw) if len(c)]
+    with multiprocessing.get_context("fork").Pool(len(chunks)) as pool:
+        parts_out = pool.map(_oracle_rows, [(load[c], P, G, N, RK, X) for c in chunks])
+    return {k: np.concatenate([r[k] for r in parts_out]) for k in ("phy2log", "log2phy", "logcnt", "status")}
+
+
 def test_skewed_1024_rebalance():
+    """All 1024 problems of the skewed batch, element by element."""
     work = wl.SKEWED_1024
     pl = work.placement
     load = wl.skewed_loads()
-    X = pl.max_count
+    X = ora.max_count(pl.E, pl.P, pl.G, pl.N)
     note(f"rebalance skewed B={load.shape[0]}")
     outs = eplb.rebalance(gpu(load), pl.P, pl.G, pl.N, pl.RK, X)
     torch.cuda.synchronize()
     phy2log, log2phy, logcnt, status = (host(t) for t in outs)
     assert (status == 0).all()
-    assert (logcnt.sum(axis=1) == pl.P).all() and (logcnt >= 1).all()
-    sample = list(range(0, work.layers, 16)) + [1, 17, 1023]
-    ref = ora.rebalance(load[sample], pl.P, pl.G, pl.N, pl.RK, X)
+    note("oracle on all 1024 skewed problems")
+    ref = _oracle_rebalance_pool(load, pl.P, pl.G, pl.N, pl.RK, X)
     for name, g in (("phy2log", phy2log), ("log2phy", log2phy), ("logcnt", logcnt), ("status", status)):
-        assert_same(name, g[sample], ref[name])
-    for b in sample[:8]:
+        assert_same(name, g, ref[name])
+    for b in range(0, work.layers, 128):
         inv.check_placement(load[b], phy2log[b], log2phy[b], logcnt[b], pl.E, pl.P, pl.G, pl.N, pl.RK)
 
 
@@ -299,6 +315,32 @@ def test_random_shapes_fuzz():
             load = rng.integers((1 << 40) - 100, (1 << 40) + 1, size=(3, E))
         load[0, : E // 2] = 0
         rebalance_both(load.astype(np.int64), P, G, N, RK)
+
+
+@pytest.mark.parametrize("shape", [
+    (512, 16, 8, 64, 640),       # 16 groups onto 8 nodes; totals of 2^48 and above take the 64-bit sums
+    (128, 64, 32, 32, 160),      # 64 groups onto 32 nodes: runs found in LDS (17 to 64 nodes)
+    (128, 128, 64, 64, 192),     # 128 groups onto 64 nodes: more than 64 groups ranked by the whole workgroup
+    (256, 256, 128, 128, 384),   # 256 groups onto 128 nodes: eight registers of node packs
+    (1024, 256, 128, 128, 1280),  # the same with 8 experts per node
+])
+def test_step1_packing_forms(shape):
+    """Every form of the groups-onto-nodes packing, including the general
+    one for total loads of 2^48 and above, against the oracle."""
+    E, G, N, RK, P = shape
+    rng = np.random.default_rng(E + G + N)
+    top = 1 << 40
+    load = np.stack([
+        rng.integers(top - (1 << 30), top + 1, size=E),          # sums far above 2^48
+        rng.integers(0, 1 << 20, size=E),                         # small: the one-word form
+        rng.integers(0, 4, size=E),                               # many ties
+        np.zeros(E, dtype=np.int64),
+        (rng.zipf(1.2, size=E) * 4096).clip(0, top),
+        np.full(E, top),
+    ]).astype(np.int64)
+    if E >= 256:                                                  # the last row's total is E * 2^40
+        assert int(load[5].sum()) >= (1 << 48) - 1
+    rebalance_both(load, P, G, N, RK)
 
 
 def test_large_loads_and_exactness():
@@ -486,7 +528,7 @@ def test_fused_serving_loop(work):
     recomputed.  Every output matches the oracle run the same way."""
     pl = work.placement
     L, E, W = work.layers, pl.E, work.window
-    X = pl.max_count
+    X = ora.max_count(pl.E, pl.P, pl.G, pl.N)
     nsteps = 3
     steps = [wl.routing_step(work, s, tokens=min(work.tokens, 4096)) for s in range(nsteps)]
     ring = torch.zeros((W, L, E), dtype=torch.int32, device=DEV)

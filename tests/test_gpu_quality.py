@@ -201,7 +201,7 @@ def test_ema_dsv3_feeds_rebalance():
     ema0 = np.random.default_rng(3).integers(0, 1 << 20, size=(work.layers, pl.E)).astype(np.int64)
     ema_h, ema_ref = _ema_chain(work, steps, 3, ema0)
     outs = [host(t) for t in eplb.rebalance(gpu(ema_h), pl.P, pl.G, pl.N, pl.RK)]
-    ref = ora.rebalance(ema_ref, pl.P, pl.G, pl.N, pl.RK, pl.max_count)
+    ref = ora.rebalance(ema_ref, pl.P, pl.G, pl.N, pl.RK, ora.max_count(pl.E, pl.P, pl.G, pl.N))
     for name, g in zip(("phy2log", "log2phy", "logcnt", "status"), outs):
         assert_same(name, g, ref[name])
 

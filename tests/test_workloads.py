@@ -35,7 +35,14 @@ def test_skewed_loads():
 
 
 def test_placement_shapes():
-    assert wl.DSV3_PREFILL.placement.hierarchical and wl.DSV3_PREFILL.placement.max_count == 9
-    assert not wl.GLOBAL_DECODE.placement.hierarchical and wl.GLOBAL_DECODE.placement.max_count == 65
-    assert not wl.DSV3_DECODE_144.hierarchical
-    assert wl.SKEWED_1024.placement.max_count == 17
+    """The workloads' shapes take the policies the configurations name: the
+    prefill shape hierarchical with up to 9 copies of an expert, the decode
+    shapes global (8 groups on 5 and on 18 nodes), the skewed batch
+    hierarchical with up to 17."""
+    from oracle import eplb_oracle as ora
+    pre, dec, d144, sk = (wl.DSV3_PREFILL.placement, wl.GLOBAL_DECODE.placement, wl.DSV3_DECODE_144,
+                          wl.SKEWED_1024.placement)
+    assert ora.policy(pre.G, pre.N)[2] and ora.max_count(pre.E, pre.P, pre.G, pre.N) == 9
+    assert not ora.policy(dec.G, dec.N)[2] and ora.max_count(dec.E, dec.P, dec.G, dec.N) == 65
+    assert not ora.policy(d144.G, d144.N)[2]
+    assert ora.policy(sk.G, sk.N)[2] and ora.max_count(sk.E, sk.P, sk.G, sk.N) == 17

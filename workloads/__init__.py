@@ -36,19 +36,6 @@ class Placement:
     RK: int
     P: int
 
-    @property
-    def hierarchical(self) -> bool:
-        return self.G % self.N == 0
-
-    @property
-    def nodes_eff(self) -> int:
-        return self.N if self.hierarchical else 1
-
-    @property
-    def max_count(self) -> int:
-        """Largest replica count the policy can give one expert: 1 + (P-E)/nodes."""
-        return 1 + (self.P - self.E) // self.nodes_eff
-
 
 @dataclass(frozen=True)
 class Workload:
