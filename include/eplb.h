@@ -19,8 +19,10 @@
  *   - All array arguments are DEVICE pointers to contiguous, row-major memory
  *     that the caller allocates, owns and keeps alive until the work enqueued
  *     on `stream` has finished.  The library allocates, frees and synchronises
- *     nothing and keeps no state between calls (the one call that needs
- *     working memory, eplb_lp_redirect, takes it as an argument).
+ *     nothing and keeps no state between calls.  The one call that needs
+ *     working memory, eplb_lp_redirect, takes it as an argument; its variant
+ *     eplb_lp_redirect_noalloc uses a fixed array of the library on each GPU
+ *     instead.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; the return code reports host-side validation and launch
  *     only.  Calls on different streams may run concurrently provided their
@@ -370,6 +372,27 @@ int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, in
 /* Bytes of workspace eplb_lp_redirect needs: L * ceil(T*K / 2048) * E * 4,
  * or a negative EPLB_E_* code.  Host only. */
 int64_t eplb_lp_redirect_workspace_bytes(int64_t L, int64_t T, int32_t K, int32_t E);
+
+/*
+ * eplb_lp_redirect_noalloc -- eplb_lp_redirect for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It calls no allocating routine; its
+ * per-segment counts live in a fixed array of the library on each GPU
+ * (EPLB_NOALLOC_SCRATCH_BYTES, held until the process ends; its address is
+ * looked up on the first call on each device).
+ *
+ * Arguments, layouts, outputs and errors: as for eplb_lp_redirect, without
+ * the workspace; in addition EPLB_E_LIMIT when the counts need more than the
+ * array holds, L * ceil(T*K / 2048) * min(E, RK * R) * 4 bytes >
+ * EPLB_NOALLOC_SCRATCH_BYTES (for example 58 layers of 16384 tokens x top-8
+ * with 64 replica slots need 950,272 bytes), and EPLB_E_HIP if the array's
+ * address cannot be found.  All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (different streams or threads) race; calls on
+ * one stream are ordered and safe.  Nothing in the array needs clearing.
+ */
+#define EPLB_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+int32_t eplb_lp_redirect_noalloc(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
+                                 const int64_t* flow, int32_t RK, int32_t R, int32_t* out, void* stream);
 
 /*
  * eplb_rebalance_max_count -- the largest replica count eplb_rebalance can

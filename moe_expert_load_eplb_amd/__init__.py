@@ -35,7 +35,7 @@ EPLB_S_BAD_TOPOLOGY = 19
 EXPORTS = ("eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_hist_redirect",
            "eplb_load_ema", "eplb_ema_redirect", "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect",
            "eplb_lp_redirect_workspace_bytes", "eplb_status_string",
-           "eplb_rebalance_lds_bytes", "eplb_rebalance_max_count")
+           "eplb_rebalance_lds_bytes", "eplb_rebalance_max_count", "eplb_lp_redirect_noalloc")
 
 
 def _load() -> ctypes.CDLL:
@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
     lib.eplb_rebalance_lds_bytes.restype = i64
     lib.eplb_rebalance_max_count.argtypes = [i32, i32, i32, i32]
     lib.eplb_rebalance_max_count.restype = i32
+    lib.eplb_lp_redirect_noalloc.argtypes = [p, i64, i64, i32, i32, p, p, i32, i32, p, p]
+    lib.eplb_lp_redirect_noalloc.restype = i32
     return lib
 
 
@@ -417,4 +419,29 @@ def lp_redirect(idx: torch.Tensor, E: int, rep: torch.Tensor, flow: torch.Tensor
                               workspace.numel() * workspace.element_size(), _dev(out, torch.int32, "out"),
                               _stream(idx.device))
     _check(rc, "eplb_lp_redirect")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024
+
+
+def lp_redirect_noalloc(idx: torch.Tensor, E: int, rep: torch.Tensor, flow: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """lp_redirect without a workspace: the counts live in the library's
+    fixed per-GPU array (NOALLOC_SCRATCH_BYTES).  Calls that overlap in time
+    on one GPU race; calls on one stream are safe."""
+    if idx.dim() != 3 or rep.dim() != 3 or flow.dim() != 3:
+        raise ValueError("idx [L, T, K], rep [L, RK, R], flow [L, RK, R] expected")
+    L, T, K = idx.shape
+    _, RK, R = rep.shape
+    if rep.shape[0] != L or tuple(flow.shape) != tuple(rep.shape):
+        raise ValueError("rep and flow must be [L, RK, R] for idx's layers")
+    if out is None:
+        out = torch.empty_like(idx)
+    if out.shape != idx.shape:
+        raise ValueError("out must have idx's shape")
+    rc = lib.eplb_lp_redirect_noalloc(_dev(idx, torch.int32, "idx"), L, T, K, E, _dev(rep, torch.int32, "rep"),
+                                      _dev(flow, torch.int64, "flow"), RK, R, _dev(out, torch.int32, "out"),
+                                      _stream(idx.device))
+    _check(rc, "eplb_lp_redirect_noalloc")
     return out

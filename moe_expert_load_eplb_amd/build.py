@@ -25,7 +25,8 @@ REF_LIB = os.path.join(PKG, "libeplb_ref.so")
 REF_SOURCES = [os.path.join("ref", "stream_ref.hip")]
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip", "fused.hip", "quality.hip", "rearrange.hip", "lp.hip"]
+SOURCES = ["api.hip", "hist.hip", "rebalance.hip", "redirect.hip", "fused.hip", "quality.hip", "rearrange.hip", "lp.hip",
+           "lp_noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -46,6 +46,25 @@ int32_t check_buffers(const Range (&in)[NI], const Range (&out)[NO]) {
 
 }  // namespace
 
+namespace eplb {
+
+int32_t check_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
+                          const int64_t* flow, int32_t RK, int32_t R, const int32_t* out) {
+  int32_t rc = check_stream_args(idx, L, T, K, E);
+  if (rc != EPLB_OK) return rc;
+  if (RK < 1 || R < 1) return EPLB_E_ARG;
+  if (RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
+  const int64_t n = T * (int64_t)K;
+  if (L * lp_segments(n) > kLpMaxSegments) return EPLB_E_LIMIT;
+  if (L > 0 && n > 0) {
+    if (rep == nullptr || flow == nullptr || out == nullptr) return EPLB_E_ARG;
+    if (overlap(out, L * n * 4, idx, L * n * 4)) return EPLB_E_ARG;
+  }
+  return EPLB_OK;
+}
+
+}  // namespace eplb
+
 extern "C" {
 
 int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
@@ -194,19 +213,14 @@ int64_t eplb_lp_redirect_workspace_bytes(int64_t L, int64_t T, int32_t K, int32_
 int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
                          const int64_t* flow, int32_t RK, int32_t R, void* workspace, int64_t workspace_bytes,
                          int32_t* out, void* stream) {
-  int32_t rc = check_stream_args(idx, L, T, K, E);
+  int32_t rc = eplb::check_lp_redirect(idx, L, T, K, E, rep, flow, RK, R, out);
   if (rc != EPLB_OK) return rc;
-  if (RK < 1 || R < 1) return EPLB_E_ARG;
-  if (RK > kLpMaxRanks || R > kLpMaxSlots) return EPLB_E_LIMIT;
   const int64_t n = T * (int64_t)K;
-  if (L * lp_segments(n) > kLpMaxSegments) return EPLB_E_LIMIT;
   if (L > 0 && n > 0) {
-    if (rep == nullptr || flow == nullptr || out == nullptr || workspace == nullptr) return EPLB_E_ARG;
+    if (workspace == nullptr) return EPLB_E_ARG;
     const int64_t need = eplb_lp_redirect_workspace_bytes(L, T, K, E);
     if (workspace_bytes < need) return EPLB_E_ARG;
-    if (overlap(out, L * n * 4, idx, L * n * 4) || overlap(workspace, need, idx, L * n * 4) ||
-        overlap(workspace, need, out, L * n * 4))
-      return EPLB_E_ARG;
+    if (overlap(workspace, need, idx, L * n * 4) || overlap(workspace, need, out, L * n * 4)) return EPLB_E_ARG;
   }
   hipError_t err = launch_lp_redirect(idx, L, n, E, rep, flow, RK, R, static_cast<int32_t*>(workspace), out,
                                       (hipStream_t)stream);

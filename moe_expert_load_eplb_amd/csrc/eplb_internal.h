@@ -350,6 +350,16 @@ hipError_t launch_rearrange(const int32_t* old_p2l, const int32_t* new_p2l, cons
                             hipStream_t stream);
 int64_t rearrange_lds_bytes(int32_t E, int32_t P, int32_t N);
 int64_t lp_segments(int64_t n);
+// The argument rules of the redirect by flows, all but the workspace's:
+// EPLB_OK or an EPLB_E_* code.
+int32_t check_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,
+                          const int64_t* flow, int32_t RK, int32_t R, const int32_t* out);
+// Segment counts the redirect by flows keeps: one int32 per layer, 2048-id
+// segment and replicated expert (at most min(E, RK * R) of them).
+inline int64_t lp_redirect_counts(int64_t L, int64_t n, int32_t E, int32_t RK, int32_t R) {
+  const int64_t c = (int64_t)RK * R < E ? (int64_t)RK * R : E;
+  return L * lp_segments(n) * c;
+}
 hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t E, const int32_t* rep,
                               const int64_t* flow, int32_t RK, int32_t R, int32_t* seg, int32_t* out,
                               hipStream_t stream);

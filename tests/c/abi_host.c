@@ -17,7 +17,7 @@ int main(void) {
       (any_fn)&eplb_rearrange,     (any_fn)&eplb_lp_solve,
       (any_fn)&eplb_lp_redirect,   (any_fn)&eplb_lp_redirect_workspace_bytes,
       (any_fn)&eplb_status_string, (any_fn)&eplb_rebalance_lds_bytes,
-      (any_fn)&eplb_rebalance_max_count,
+      (any_fn)&eplb_rebalance_max_count, (any_fn)&eplb_lp_redirect_noalloc,
   };
   size_t i;
   for (i = 0; i < sizeof fns / sizeof fns[0]; ++i) {

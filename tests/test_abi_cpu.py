@@ -59,7 +59,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) >= {"eplb_load_hist", "eplb_rebalance", "eplb_redirect", "eplb_status_string",
                           "eplb_rebalance_lds_bytes", "eplb_hist_redirect", "eplb_load_ema",
                           "eplb_placement_load", "eplb_rearrange", "eplb_lp_solve", "eplb_lp_redirect", "eplb_ema_redirect",
-                          "eplb_lp_redirect_workspace_bytes", "eplb_rebalance_max_count"}
+                          "eplb_lp_redirect_workspace_bytes", "eplb_rebalance_max_count",
+                          "eplb_lp_redirect_noalloc"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in eplb.h but not exported"
 
@@ -259,8 +260,8 @@ def test_header_is_c99_and_every_entry_point_links(tmp_path):
     exe = _cc(os.path.join(ROOT, "tests", "c", "abi_host.c"), str(tmp_path / "abi_host"), ("-std=c99", "-pedantic"))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
-    assert "abi_host ok: 14 entry points" in r.stdout
-    assert len(declared_functions()) == 14
+    assert "abi_host ok: 15 entry points" in r.stdout
+    assert len(declared_functions()) == 15
 
 
 def test_ema_redirect_validation(lib):
@@ -333,3 +334,27 @@ def test_overlapping_buffers_rejected(lib):
     # lp_redirect: workspace inside out
     need = lib.eplb_lp_redirect_workspace_bytes(2, 5000, 2, 64)
     assert lib.eplb_lp_redirect(F[0], 2, 5000, 2, 64, F[1], F[2], 8, 2, F[4] + 16, need, F[4], None) == 1
+
+
+def test_lp_redirect_noalloc_validation(lib):
+    """The no-allocation redirect applies eplb_lp_redirect's rules and refuses
+    inputs whose counts need more than its fixed array, before any GPU call."""
+    f = lib.eplb_lp_redirect_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    F = [FAKE << (4 * i + 4) for i in range(6)]
+    limit = header_constants().get("EPLB_NOALLOC_SCRATCH_BYTES")
+    assert limit is None                                  # a parenthesised expression, checked below
+    assert "#define EPLB_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)" in open(HEADER).read()
+    good = [F[0], 58, 16384, 8, 256, F[1], F[2], 16, 4, F[3], None]
+    for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (7, 0, 1), (8, 0, 1),
+                           (7, 17, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
+                           (9, F[0] + 64, 1)]:
+        args = list(good)
+        args[pos] = bad
+        assert f(*args) == code, (pos, bad)
+    # 58 x 64 segments x 64 counts = 950,272 bytes fit; 4x the tokens do not
+    big = list(good)
+    big[2] = 16384 * 5
+    assert f(*big) == 5
+    assert f(None, 0, 16384, 8, 256, None, None, 16, 4, None, None) == 0      # nothing to do
