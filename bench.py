@@ -507,13 +507,13 @@ def small_workloads(eplb, wl, dev, stream):
 
 
 def lp_batches(eplb, wl, dev, stream):
-    """The LPLB-style per-batch path on its two topologies (8-GPU cube,
-    16-GPU hypercube; 58 layers x 16384 tokens x top-8): device time of the
-    exact solve for all layers and of the redirect by its flows, and how far
-    the largest rank load drops."""
+    """The LPLB-style per-batch path on the pages' topologies (8-GPU cube,
+    16-GPU hypercube, a torus of 4 nodes x 8 GPUs; 58 layers x 16384 tokens x
+    top-8): device time of the exact solve for all layers and of the redirect
+    by its flows, and how far the largest rank load drops."""
     import torch
     out = {}
-    for work in (wl.LPLB_CUBE, wl.LPLB_HYPERCUBE):
+    for work in (wl.LPLB_CUBE, wl.LPLB_HYPERCUBE, wl.LPLB_TORUS):
         idx_h, home_h, rep_h = wl.lp_inputs(work)
         L, E = work.layers, work.E
         idx = torch.from_numpy(idx_h).to(dev)

@@ -317,19 +317,19 @@ int32_t eplb_rearrange(const int32_t* old_phy2log, const int32_t* new_phy2log, c
  *   rep        [B][RK][R] int32  expert replicated in slot j of rank g, or -1;
  *                                an expert has at most one replica (a replica
  *                                on its own home rank carries nothing)
- *   B, E, RK, R                  problems, experts, ranks (1 .. 16), slots
+ *   B, E, RK, R                  problems, experts, ranks (1 .. 64), slots
  *                                per rank (1 .. 64)
  *   lam        [B] int64         out: the least reachable largest rank load
  *   flow       [B][RK][R] int64  out: tokens slot (g, j) takes from the
  *                                original of rep[g][j] (0 for empty slots)
  *   rank_load  [B][RK] int64     out: rank loads after the moves (max = lam)
  *   status     [B] int32         out: EPLB_S_OK or EPLB_S_BAD_TOPOLOGY
- * No output may share a byte with an input or another output (with 12 or
- * more ranks rank_load also carries partial results between the call's two
+ * No output may share a byte with an input or another output (with 12 to
+ * 16 ranks rank_load also carries partial results between the call's two
  * launches).
  *
  * Errors: EPLB_E_ARG (a size < 1, B < 0, a NULL array, an output sharing a
- * byte with an input or another output), EPLB_E_LIMIT (E > 4096, RK > 16,
+ * byte with an input or another output), EPLB_E_LIMIT (E > 4096, RK > 64,
  * R > 64, B > 2^20 - 1), EPLB_E_HIP.
  */
 int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* rep, int64_t B, int32_t E,
@@ -352,7 +352,7 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
  *   idx        [L][T][K] int32   logical ids of the batch
  *   rep        [L][RK][R] int32  replica slots (as for eplb_lp_solve)
  *   flow       [L][RK][R] int64  tokens each slot takes (eplb_lp_solve)
- *   RK, R                        ranks (1 .. 16) and slots per rank (1 .. 64)
+ *   RK, R                        ranks (1 .. 64) and slots per rank (1 .. 64)
  *   workspace                    caller-owned device memory of at least
  *                                eplb_lp_redirect_workspace_bytes(L, T, K, E)
  *                                bytes (per-segment counts; contents on entry
@@ -362,7 +362,7 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
  *
  * Errors: as for eplb_redirect; EPLB_E_ARG also for RK or R < 1, a NULL
  * array or workspace, a workspace below the size needed, or a workspace
- * sharing a byte with idx or out; EPLB_E_LIMIT for RK > 16, R > 64, or more
+ * sharing a byte with idx or out; EPLB_E_LIMIT for RK > 64, R > 64, or more
  * than 2^25 segments of 2048 ids over all layers.
  */
 int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,

@@ -20,7 +20,8 @@ constexpr int kMaxCount = 16128;                 // replica count bound (< 131^2
 constexpr int kMaxP = 8192;                      // physical experts per problem
 constexpr int32_t kStatusBadMap = 18;            // rearrangement: an entry out of range
 constexpr int32_t kStatusBadTopology = 19;       // redistribution: an id, home or count out of range
-constexpr int kLpMaxRanks = 16;                  // ranks of one redistribution problem (2^RK rank sets)
+constexpr int kLpMaxRanks = 64;                  // ranks of one redistribution problem (one wave, a lane per rank)
+constexpr int kLpEnumRanks = 16;                 // up to here the optimum may come from enumerating 2^RK rank sets
 constexpr int kLpMaxSlots = 64;                  // replica slots per rank
 constexpr int kLpSeg = 2048;                     // ids per wave in the redirect by flows
 // Launch sizes: one launch covers at most 2^32 - 1 work-items.  The largest

@@ -40,7 +40,7 @@ namespace eplb {
 namespace {
 
 constexpr int kLpThreads = 1024;
-constexpr int kLpMaxV = kLpMaxRanks + 2;
+constexpr int kLpMaxV = kLpEnumRanks + 2;
 constexpr int kLpMaxAugment = 1 << 16;     // far above the Edmonds-Karp bound V * E for V <= 18
 constexpr int kLpSplitRanks = 12;          // from 2^12 rank sets on, step 2 is spread over kLpParts workgroups
 constexpr int kLpParts = 4;                // (<= kLpSplitRanks: the bounds sit in a layer's rank_load row)
@@ -61,13 +61,13 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
     const int64_t* __restrict__ cnt, const int32_t* __restrict__ home, const int32_t* __restrict__ rep,
     int32_t E, int32_t RK, int32_t R, int32_t parts, int64_t* __restrict__ lam_out, int64_t* __restrict__ flow_out,
     int64_t* __restrict__ load_out, int32_t* __restrict__ status) {
-  __shared__ unsigned long long base[kLpMaxRanks];
-  __shared__ unsigned long long cap[kLpMaxRanks * kLpMaxRanks];      // cap[o * RK + g]
+  __shared__ unsigned long long base[kLpEnumRanks];
+  __shared__ unsigned long long cap[kLpEnumRanks * kLpEnumRanks];      // cap[o * RK + g]
   __shared__ long long res[kLpMaxV * kLpMaxV];                        // residual, res[u * V + v]
   __shared__ uint32_t seen_bits[kMaxE / 32];
   __shared__ long long s_best[kLpThreads / 64];
-  __shared__ long long psym[kLpMaxRanks * 4 * 16];                   // [r][quarter][4-bit subset]
-  __shared__ long long wbase[kLpMaxRanks];                            // base[r] - cap(r -> every other rank)
+  __shared__ long long psym[kLpEnumRanks * 4 * 16];                   // [r][quarter][4-bit subset]
+  __shared__ long long wbase[kLpEnumRanks];                            // base[r] - cap(r -> every other rank)
 
   const int64_t b = kMode == 1 ? blockIdx.x / parts : blockIdx.x;
   const int part = kMode == 1 ? (int)(blockIdx.x - b * parts) : 0;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   //          = cap(r -> all) - sum over g in T of (cap[r][g] + cap[g][r]),
   // and that sum is read from psym[r][q][T's bits q*4 .. q*4+3] for the
   // four quarters q of the ranks (one LDS round trip per step).
-  for (int i = tid; i < kLpMaxRanks * 4 * 16; i += kLpThreads) {
+  for (int i = tid; i < kLpEnumRanks * 4 * 16; i += kLpThreads) {
     const int r = i >> 6, q = (i >> 4) & 3, m = i & 15;
     long long v = 0;
     if (r < RK)
@@ -330,6 +330,243 @@ __global__ __launch_bounds__(kLpThreads) void lp_solve_kernel(
   }
 }
 
+// ---------------------------------------------------------------- the optimum by cuts (any RK <= 64)
+// The same optimum and flow without enumerating rank sets.  Start from the
+// lower bounds of the set of all ranks, ceil(total / RK), and of each rank
+// alone (its load minus all it can hand on), and run the
+// maximum flow of the feasibility network at lam.  If it falls short of what
+// the ranks above lam must shed, the ranks still reachable from the source
+// form a set S with load(S) - cap(S -> rest) > lam * |S| (the cut that
+// bounds the flow), so lam' = ceil((load(S) - cap(S -> rest)) / |S|) is a
+// larger lower bound; repeat until the flow is feasible (Dinkelbach's method
+// on the supply-demand bound: each round raises lam, never past the
+// optimum).  The last flow is a fresh shortest-augmenting-path flow at the
+// optimum, with the same predecessor rule, so it is the flow of step 3 above.
+//
+// One wave holds the network, a lane per rank (RK <= 64); the source and
+// the sink are implicit: lane v keeps its residuals from the source and to
+// the sink in registers, and `in` = the ranks u with residual u -> v.  A
+// search never passes through the source (seen from the start) or the sink
+// (the search ends there), so the reverse edges into them never matter.
+constexpr int kLpDkThreads = 256;
+constexpr int kLpMaxRounds = 1 << 12;          // rounds of the cut iteration (each one raises lam)
+
+__host__ __device__ inline size_t lp_dk_lds_bytes(int RK, int E) {
+  return (size_t)RK * RK * 16 + (size_t)RK * 8 + (((size_t)E + 31) / 32) * 4;
+}
+
+__global__ __launch_bounds__(kLpDkThreads) void lp_solve_dk_kernel(
+    const int64_t* __restrict__ cnt, const int32_t* __restrict__ home, const int32_t* __restrict__ rep, int32_t E,
+    int32_t RK, int32_t R, int64_t* __restrict__ lam_out, int64_t* __restrict__ flow_out,
+    int64_t* __restrict__ load_out, int32_t* __restrict__ status) {
+  extern __shared__ __align__(16) unsigned char lp_dk_smem[];
+  unsigned long long* cap = reinterpret_cast<unsigned long long*>(lp_dk_smem);         // [RK][RK]
+  long long* res = reinterpret_cast<long long*>(cap + RK * RK);                          // [RK][RK] residual
+  unsigned long long* base = reinterpret_cast<unsigned long long*>(res + RK * RK);      // [RK]
+  uint32_t* seen_bits = reinterpret_cast<uint32_t*>(base + RK);                          // [(E + 31) / 32]
+  __shared__ long long s_lam;
+  __shared__ int s_fail;
+
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t* c = cnt + b * E;
+  const int32_t* h = home + b * E;
+  const int32_t* rp = rep + b * (int64_t)RK * R;
+  int64_t* flow_b = flow_out + b * (int64_t)RK * R;
+  int64_t* load_b = load_out + b * RK;
+
+  for (int i = tid; i < RK; i += kLpDkThreads) base[i] = 0;
+  for (int i = tid; i < RK * RK; i += kLpDkThreads) cap[i] = 0;
+  for (int i = tid; i < (E + 31) / 32; i += kLpDkThreads) seen_bits[i] = 0;
+  __syncthreads();
+
+  // ---- home loads and rank-pair capacities (as in lp_solve_kernel)
+  int bad = 0;
+  for (int e = tid; e < E; e += kLpDkThreads) {
+    const int64_t x = c[e];
+    const int32_t r = h[e];
+    const bool ok = x >= 0 && x <= kLoadMax && (uint32_t)r < (uint32_t)RK;
+    bad |= !ok;
+    if (ok) atomicAdd(&base[r], (unsigned long long)x);
+  }
+  for (int i = tid; i < RK * R; i += kLpDkThreads) {
+    const int32_t x = rp[i];
+    if (x == -1) continue;
+    if ((uint32_t)x >= (uint32_t)E) { bad = 1; continue; }
+    const uint32_t bit = 1u << (x & 31);
+    if (atomicOr(&seen_bits[x >> 5], bit) & bit) { bad = 1; continue; }
+    const int32_t o = h[x], g = i / R;
+    const int64_t v = c[x];
+    if ((uint32_t)o < (uint32_t)RK && o != g && v >= 0 && v <= kLoadMax)
+      atomicAdd(&cap[o * RK + g], (unsigned long long)v);
+  }
+  bad = __syncthreads_or(bad);
+  if (bad) {
+    for (int i = tid; i < RK * R; i += kLpDkThreads) flow_b[i] = -1;
+    for (int i = tid; i < RK; i += kLpDkThreads) load_b[i] = -1;
+    if (tid == 0) {
+      lam_out[b] = -1;
+      status[b] = kStatusBadTopology;
+    }
+    return;
+  }
+
+  if (tid < 64) {
+    const bool node = lane < RK;
+    const long long bv = node ? (long long)base[lane] : 0;
+    long long total = bv;
+    for (int off = 32; off > 0; off >>= 1) total += __shfl_xor(total, off);
+    // lower bounds from the set of all ranks and from each rank alone
+    // (its load minus all it can hand on)
+    long long single = 0;
+    if (node) {
+      single = bv;
+      for (int g = 0; g < RK; ++g) single -= (long long)cap[lane * RK + g];
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const long long o = __shfl_xor(single, off);
+      single = o > single ? o : single;
+    }
+    long long lam = (total + RK - 1) / RK;               // total >= 0
+    lam = single > lam ? single : lam;
+    int fail = 0;
+    for (int round = 0;; ++round) {
+      if (round == kLpMaxRounds) { fail = 1; break; }
+      // ---- the feasibility network at lam
+      long long rs = node && bv > lam ? bv - lam : 0;    // source -> lane
+      long long rt = node && lam > bv ? lam - bv : 0;    // lane -> sink
+      long long need = rs;
+      for (int off = 32; off > 0; off >>= 1) need += __shfl_xor(need, off);
+      uint64_t in = 0;
+      for (int u = 0; u < RK; ++u) {
+        const long long cu = node ? (long long)cap[u * RK + lane] : 0;
+        if (node) res[u * RK + lane] = cu;
+        in |= (uint64_t)(cu > 0) << u;
+      }
+      lp_wave_sync();
+      // ---- maximum flow by shortest augmenting paths
+      long long flow = 0;
+      uint64_t seen = 0;
+      int it = 0;
+      for (; it < kLpMaxAugment; ++it) {
+        int parent = -1;                                 // 64: the source
+        uint64_t frontier = __builtin_amdgcn_ballot_w64(rs > 0);
+        seen = frontier;
+        if (rs > 0) parent = 64;
+        int last = -1;                                   // the path's rank next to the sink
+        while (frontier) {
+          const uint64_t ts = __builtin_amdgcn_ballot_w64(((frontier >> lane) & 1ull) && rt > 0);
+          if (ts) { last = __builtin_ctzll(ts); break; }
+          const uint64_t cand = node && !((seen >> lane) & 1ull) ? (in & frontier) : 0;
+          if (cand) parent = __builtin_ctzll(cand);
+          const uint64_t found = __builtin_amdgcn_ballot_w64(cand != 0);
+          seen |= found;
+          frontier = found;
+        }
+        if (last < 0) break;
+        // residual of the tree edge into each lane, then the path from the sink back
+        long long fwd = 0, bwd = 0;
+        if (parent >= 0 && parent < 64) {
+          fwd = res[parent * RK + lane];
+          bwd = res[lane * RK + parent];
+        } else if (parent == 64) {
+          fwd = rs;
+        }
+        long long bn = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rt >> 32), last) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)rt, last));
+        uint64_t path = 0;
+        int child = -1;
+        for (int v = last;;) {
+          const int pv = __builtin_amdgcn_readlane(parent, v);
+          const long long fv = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(fwd >> 32), v) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readlane((int)fwd, v));
+          bn = fv < bn ? fv : bn;
+          path |= 1ull << v;
+          if (pv == 64) break;
+          child = lane == pv ? v : child;
+          v = pv;
+        }
+        lp_wave_sync();
+        if ((path >> lane) & 1ull) {
+          if (parent == 64) {
+            rs -= bn;
+          } else {
+            const long long nf = fwd - bn;
+            res[parent * RK + lane] = nf;
+            res[lane * RK + parent] = bwd + bn;
+            if (nf == 0) in &= ~(1ull << parent);
+          }
+        }
+        if (child >= 0) in |= 1ull << child;             // the reverse of the edge lane -> child
+        if (lane == last) rt -= bn;
+        flow += bn;
+        lp_wave_sync();
+      }
+      if (it == kLpMaxAugment) { fail = 1; break; }
+      if (flow == need) break;                           // feasible: lam is the optimum
+      // the ranks reachable from the source: load(S) - cap(S -> rest) > lam |S|
+      long long f = 0;
+      if ((seen >> lane) & 1ull) {
+        f = bv;
+        for (int g = 0; g < RK; ++g)
+          if (!((seen >> g) & 1ull)) f -= (long long)cap[lane * RK + g];
+      }
+      for (int off = 32; off > 0; off >>= 1) f += __shfl_xor(f, off);
+      const int k = __popcll(seen);
+      const long long next = (f + k - 1) / k;            // f > lam * k >= 0
+      if (next <= lam) { fail = 1; break; }              // cannot happen; never loops
+      lam = next;
+    }
+    if (lane == 0) {
+      s_lam = lam;
+      s_fail = fail;
+    }
+  }
+  __syncthreads();
+  if (s_fail) {
+    for (int i = tid; i < RK * R; i += kLpDkThreads) flow_b[i] = -1;
+    for (int i = tid; i < RK; i += kLpDkThreads) load_b[i] = -1;
+    if (tid == 0) {
+      lam_out[b] = -1;
+      status[b] = kStatusBadTopology;
+    }
+    return;
+  }
+  // ---- net flow per rank pair, split over the pair's slots in slot order
+  for (int i = tid; i < RK * RK; i += kLpDkThreads) {
+    const int o = i / RK, g = i - o * RK;
+    const long long n = o == g ? 0 : (long long)cap[o * RK + g] - res[o * RK + g];
+    long long left = n > 0 ? n : 0;
+    for (int j = 0; j < R; ++j) {
+      const int32_t x = rp[g * R + j];
+      const int ox = x >= 0 ? h[x] : g;
+      if (o == g) {
+        if (ox == g) flow_b[g * R + j] = 0;
+      } else if (ox == o) {
+        const long long cx = c[x];
+        const long long f = left < cx ? left : cx;
+        left -= f;
+        flow_b[g * R + j] = f;
+      }
+    }
+  }
+  for (int r = tid; r < RK; r += kLpDkThreads) {
+    long long l = (long long)base[r];
+    for (int g = 0; g < RK; ++g) {
+      if (g == r) continue;
+      const long long out_n = (long long)cap[r * RK + g] - res[r * RK + g];
+      const long long in_n = (long long)cap[g * RK + r] - res[g * RK + r];
+      l -= out_n > 0 ? out_n : 0;
+      l += in_n > 0 ? in_n : 0;
+    }
+    load_b[r] = l;
+  }
+  if (tid == 0) {
+    lam_out[b] = s_lam;
+    status[b] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- redirect by the flows
 // Occurrence i (in (token, k) order within the layer) of a replicated expert
 // x goes to x's replica when i < flow, else to the original.  Only the
@@ -527,6 +764,11 @@ hipError_t launch_lp_solve(const int64_t* cnt, const int32_t* home, const int32_
                            int32_t RK, int32_t R, int64_t* lam, int64_t* flow, int64_t* rank_load,
                            int32_t* status, hipStream_t stream) {
   if (B == 0) return hipSuccess;
+  if (RK > kLpEnumRanks) {
+    lp_solve_dk_kernel<<<(unsigned)B, kLpDkThreads, lp_dk_lds_bytes(RK, E), stream>>>(cnt, home, rep, E, RK, R, lam,
+                                                                                       flow, rank_load, status);
+    return hipGetLastError();
+  }
   if (RK < kLpSplitRanks) {
     lp_solve_kernel<0><<<(unsigned)B, kLpThreads, 0, stream>>>(cnt, home, rep, E, RK, R, 1, lam, flow, rank_load,
                                                                status);

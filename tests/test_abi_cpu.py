@@ -213,7 +213,7 @@ def test_rearrange_validation(lib):
 def test_lp_solve_validation(lib):
     F = [FAKE + 64 * i for i in range(8)]
     good = [F[0], F[1], F[2], 58, 256, 8, 2, F[3], F[4], F[5], F[6], None]
-    for pos, bad, code in [(3, -1, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (4, 4097, 5), (5, 17, 5), (6, 65, 5),
+    for pos, bad, code in [(3, -1, 1), (4, 0, 1), (5, 0, 1), (6, 0, 1), (4, 4097, 5), (5, 65, 5), (6, 65, 5),
                            (0, None, 1), (1, None, 1), (2, None, 1), (7, None, 1), (8, None, 1), (9, None, 1),
                            (10, None, 1), (9, F[0], 1), (7, F[2], 1)]:         # outputs equal to inputs
         args = list(good)
@@ -230,7 +230,7 @@ def test_lp_redirect_validation(lib):
     assert lib.eplb_lp_redirect_workspace_bytes(-1, 10, 8, 256) == -1
     good = [F[0], 58, 16384, 8, 256, F[1], F[2], 8, 2, F[3], need, F[4], None]
     for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (7, 0, 1), (8, 0, 1),
-                           (7, 17, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
+                           (7, 65, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
                            (11, None, 1), (11, F[0], 1), (10, need - 1, 1)]:
         args = list(good)
         args[pos] = bad
@@ -348,7 +348,7 @@ def test_lp_redirect_noalloc_validation(lib):
     assert "#define EPLB_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)" in open(HEADER).read()
     good = [F[0], 58, 16384, 8, 256, F[1], F[2], 16, 4, F[3], None]
     for pos, bad, code in [(1, -1, 1), (3, 0, 1), (4, 0, 1), (4, 4097, 5), (2, 1 << 28, 6), (7, 0, 1), (8, 0, 1),
-                           (7, 17, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
+                           (7, 65, 5), (8, 65, 5), (0, None, 1), (5, None, 1), (6, None, 1), (9, None, 1),
                            (9, F[0] + 64, 1)]:
         args = list(good)
         args[pos] = bad

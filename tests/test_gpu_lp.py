@@ -69,7 +69,10 @@ def check_solution(cnt, home, rep, q):
 @pytest.mark.parametrize("RK,R,E,top", [(1, 1, 3, 10), (2, 1, 5, 10), (3, 2, 9, 50), (5, 3, 40, 1000),
                                         (8, 2, 256, 10**5), (8, 4, 64, 7), (11, 2, 100, 10**6),
                                         (12, 3, 200, 10**5), (13, 2, 300, 10**3),
-                                        (16, 4, 256, 10**4), (16, 1, 4096, 1 << 40)])
+                                        (16, 4, 256, 10**4), (16, 1, 4096, 1 << 40),
+                                        (17, 2, 200, 10**5), (24, 3, 512, 10**6), (32, 2, 1024, 10**4),
+                                        (32, 64, 4096, 10**3), (48, 2, 2048, 10**6), (63, 1, 500, 10**3),
+                                        (64, 4, 4096, 1 << 40), (64, 64, 4096, 10**5)])
 def test_lp_solve_random(RK, R, E, top):
     rng = np.random.default_rng(RK * 100 + R)
     cnt, home, rep = oracle_pins._lp_random(rng, RK, R, E, B=6, top=top, fill=0.8)
@@ -79,10 +82,11 @@ def test_lp_solve_random(RK, R, E, top):
     check_solution(cnt, home, rep, q)
 
 
-@pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE], ids=lambda w: w.name)
+@pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE, wl.LPLB_TORUS], ids=lambda w: w.name)
 def test_lp_solve_topologies(work):
-    """Batches of 16384 tokens x top-8 on the 8-GPU cube (the pages' r2o)
-    and the 16-GPU hypercube: all 58 layers against the oracle."""
+    """Batches of 16384 tokens x top-8 on the 8-GPU cube (the pages' r2o),
+    the 16-GPU hypercube and a 4 x 8-GPU torus: all 58 layers against the
+    oracle."""
     idx, home, rep = wl.lp_inputs(work)
     cnt = np.stack([np.bincount(idx[l].ravel(), minlength=work.E) for l in range(work.layers)]).astype(np.int64)
     q = solve_both(cnt, home, rep)
@@ -116,7 +120,8 @@ def test_lp_solve_degenerate_and_bad():
 
 @pytest.mark.parametrize("L,T,K,E,RK,R", [(2, 5000, 8, 64, 8, 2), (3, 1, 3, 5, 2, 1), (1, 2048, 1, 256, 8, 2),
                                           (2, 4097, 2, 1, 1, 1), (1, 33333, 3, 4096, 16, 4),
-                                          (4, 700, 7, 300, 11, 3)])
+                                          (4, 700, 7, 300, 11, 3), (2, 5000, 8, 4096, 64, 4),
+                                          (1, 3000, 4, 300, 40, 3), (1, 9000, 2, 4096, 64, 64)])
 def test_lp_redirect_random(L, T, K, E, RK, R):
     """Segments of 2048 ids cut anywhere (ragged tails, one id, several
     segments), out-of-range ids, flows of 0, above the count and negative,
@@ -153,7 +158,7 @@ def test_lp_redirect_bad_layers():
     assert (got[1:] == -1).all() and (got[0] >= 0).all()
 
 
-@pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE], ids=lambda w: w.name)
+@pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE, wl.LPLB_TORUS], ids=lambda w: w.name)
 def test_lp_batch_end_to_end(work):
     """One batch through the whole LPLB-style path on the GPU: per-layer
     counts (eplb_load_hist, W = 1), the solve, the redirect; the redirect

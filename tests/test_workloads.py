@@ -46,3 +46,21 @@ def test_placement_shapes():
     assert not ora.policy(dec.G, dec.N)[2] and ora.max_count(dec.E, dec.P, dec.G, dec.N) == 65
     assert not ora.policy(d144.G, d144.N)[2]
     assert ora.policy(sk.G, sk.N)[2] and ora.max_count(sk.E, sk.P, sk.G, sk.N) == 17
+
+
+def test_lplb_topologies():
+    """The r2o tables: the cube of the pages' usage example, the hypercube
+    (slot d of rank g on rank g xor 2^d) and the torus (slot 0 on the
+    previous GPU of the node, slot 1 on the same GPU of the previous node)."""
+    assert wl.CUBE_R2O[0] == (3, 6) and len(wl.CUBE_R2O) == 8
+    h = wl.hypercube_r2o(16)
+    assert all(h[g][d] == g ^ (1 << d) for g in range(16) for d in range(4))
+    t = wl.torus_r2o(4, 8)
+    assert len(t) == 32
+    for r, (a, b) in enumerate(t):
+        n, g = divmod(r, 8)
+        assert a == n * 8 + (g + 7) % 8 and b == ((n + 3) % 4) * 8 + g
+    # every rank's experts are replicated once inside its node and once on the next node
+    for o in range(32):
+        names = [(r, j) for r in range(32) for j in range(2) if t[r][j] == o]
+        assert sorted(j for _, j in names) == [0, 1]

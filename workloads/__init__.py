@@ -221,6 +221,19 @@ def hypercube_r2o(RK: int) -> tuple:
     return tuple(tuple(g ^ (1 << d) for d in range(dims)) for g in range(RK))
 
 
+def torus_r2o(nodes: int, per_node: int) -> tuple:
+    """Torus over `nodes` nodes of `per_node` GPUs (rank n * per_node + g):
+    slot 0 of a rank replicates an expert of the previous GPU of its node,
+    slot 1 one of the same GPU of the previous node, so every GPU has one
+    expert copied onto a neighbour in its node and one onto a GPU of the
+    next node."""
+    out = []
+    for n in range(nodes):
+        for g in range(per_node):
+            out.append((n * per_node + (g - 1) % per_node, ((n - 1) % nodes) * per_node + g))
+    return tuple(out)
+
+
 @dataclass
 class LpWorkload:
     """Per-batch redistribution inputs: ids of one batch per layer, experts
@@ -240,6 +253,8 @@ LPLB_CUBE = LpWorkload(name="lplb_cube_58L_e256_8x2", wid=5, layers=58, E=256, R
                        tokens=16384, topk=8, param=1.1)
 LPLB_HYPERCUBE = LpWorkload(name="lplb_hypercube_58L_e256_16x4", wid=6, layers=58, E=256, RK=16,
                             r2o=hypercube_r2o(16), tokens=16384, topk=8, param=1.1)
+LPLB_TORUS = LpWorkload(name="lplb_torus_58L_e256_4x8x2", wid=7, layers=58, E=256, RK=32, r2o=torus_r2o(4, 8),
+                        tokens=16384, topk=8, param=1.1)
 
 
 def lp_inputs(w: LpWorkload, layers: range | None = None, tokens: int | None = None):
