@@ -781,6 +781,63 @@ __device__ void write_failed(const RbPlan& p, int64_t b, int32_t code, int32_t* 
 
 // ---------------------------------------------------------------- per-node phases
 
+// After replication on the first 64 positions only (the window): the final
+// order of all En > 64 experts of node n into s.srt.  Only the top Rn <= 64
+// experts can take a replica (the expert at position p is preceded by the
+// originals of the p experts before it, so its k-th replica ranks at least
+// p + k - 1 among the picks), so the picks on the window are those on all
+// positions and the other experts keep count 1 and their order.  The two
+// sorted runs are merged: window expert l (lane l) finds by binary search
+// how many tail experts precede it, cnt_l; tail expert j is preceded by the
+// window experts with cnt_l <= j (a histogram of the cnt_l and its prefix
+// sums).  Scratch: the node's part of the step-3 key array (not yet used).
+template <int K>
+__device__ void merge_window(const RbPlan& p, const Smem& s, int n, const u64 (&u)[K], const int (&ci)[K]) {
+  const int lane = lane_id();
+  const int En = p.En;
+  const int T = En - 64;                             // tail experts
+  u64* tk = reinterpret_cast<u64*>(s.kexp + n * En); // [T] tail keys u << 9 | (511 - index)
+  int* hs = reinterpret_cast<int*>(tk + T);          // [T + 1] histogram, then its prefix sums
+#pragma unroll
+  for (int r = 1; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    if (pos < En) tk[pos - 64] = (u[r] << 9) | (u64)(511 - (ci[r] & 0xffff));
+  }
+  for (int x = lane; x <= T; x += 64) hs[x] = 0;
+  wave_lds_sync();
+  // window expert: tail experts before it (a prefix of the tail)
+  const u64 cl = (u64)(uint32_t)(ci[0] >> 16);
+  const u64 rhs = (u[0] << 9) + (u64)(511 - (ci[0] & 0xffff));
+  int lo = 0;
+  int step = 1;
+  while (step * 2 <= T) step *= 2;
+  for (; step > 0; step >>= 1) {
+    if (lo + step <= T) {
+      const u64 t = tk[lo + step - 1];
+      if ((t & ~(u64)511) * cl + (t & 511) > rhs) lo += step;
+    }
+  }
+  atomicAdd(&hs[lo], 1);
+  wave_lds_sync();
+  int carry = 0;
+  for (int x0 = 0; x0 <= T; x0 += 64) {
+    const int x = x0 + lane;
+    const int v = x <= T ? hs[x] : 0;
+    const int incl = wave_incl_sum(v) + carry;
+    carry = rdl(incl, 63);
+    if (x <= T) hs[x] = incl;                       // window experts with cnt_l <= x
+  }
+  wave_lds_sync();
+  int32_t* srt = s.srt + n * En;
+  srt[lane + lo] = ci[0] & 0xffff;
+#pragma unroll
+  for (int r = 1; r < K; ++r) {
+    const int pos = r * 64 + lane;
+    if (pos < En) srt[(pos - 64) + hs[pos - 64]] = ci[r] & 0xffff;
+  }
+  wave_lds_sync();
+}
+
 // Step 2 and the denominators of node n (one wave): the node's experts in
 // load order go through replication; counts, the final order and the exact
 // step-3 keys are stored.
@@ -802,7 +859,18 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
       ci[r] = (1 << 16) | 0xffff;
     }
   }
-  replicate_sorted<K>(u, ci, p.Rn, s.rep + n * p.Rn);
+  bool window = false;
+  if constexpr (K > 1) window = p.Rn <= 64;          // En > 64 here
+  if (window) {
+    u64 uw[1] = {u[0]};
+    int cw[1] = {ci[0]};
+    replicate_sorted<1>(uw, cw, p.Rn, s.rep + n * p.Rn);
+    u[0] = uw[0];
+    ci[0] = cw[0];
+    merge_window<K>(p, s, n, u, ci);
+  } else {
+    replicate_sorted<K>(u, ci, p.Rn, s.rep + n * p.Rn);
+  }
 
   u64 sum = 0;
   int cmax = 1;
@@ -813,7 +881,7 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
       const int i = ci[r] & 0xffff;
       const int c = ci[r] >> 16;
       s.cnt[n * En + i] = c;
-      s.srt[n * En + pos] = i;
+      if (!window) s.srt[n * En + pos] = i;
       sum += u[r];
       cmax = max(cmax, c);
     }
@@ -1001,8 +1069,11 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
 
 // ---------------------------------------------------------------- kernel
 
-template <int KR, int KP>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, 512), amdgpu_waves_per_eu(KR * KP <= 2 ? 8 : 1)))
+// kFull: the many-problem form of the smallest shapes, held to 64 VGPRs so
+// that eight waves fit per SIMD (at the cost of a few spilled values); with
+// at most one workgroup per CU the uncapped form is used.
+template <int KR, int KP, bool kFull>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 512), amdgpu_waves_per_eu(kFull && KR * KP <= 2 ? 8 : 1)))
 void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
                                                          int32_t* __restrict__ phy2log,
                                                          int32_t* __restrict__ log2phy,
@@ -1160,23 +1231,33 @@ int regs_for(int n) {          // registers per lane to hold n sorted positions
 
 typedef void (*RbKernel)(const int64_t*, RbPlan, int32_t*, int32_t*, int32_t*, int32_t*);
 
-template <int KR>
+template <int KR, bool kFull>
 RbKernel pick_kp(int KP) {
   switch (KP) {
-    case 1: return rebalance_kernel<KR, 1>;
-    case 2: return rebalance_kernel<KR, 2>;
-    case 4: return rebalance_kernel<KR, 4>;
-    default: return rebalance_kernel<KR, 8>;
+    case 1: return rebalance_kernel<KR, 1, kFull>;
+    case 2: return rebalance_kernel<KR, 2, kFull>;
+    case 4: return rebalance_kernel<KR, 4, kFull>;
+    default: return rebalance_kernel<KR, 8, kFull>;
   }
 }
 
-RbKernel pick_kernel(int KR, int KP) {
+template <bool kFull>
+RbKernel pick_kr(int KR, int KP) {   // kFull = false only
   switch (KR) {
-    case 1: return pick_kp<1>(KP);
-    case 2: return pick_kp<2>(KP);
-    case 4: return pick_kp<4>(KP);
-    default: return pick_kp<8>(KP);
+    case 1: return pick_kp<1, kFull>(KP);
+    case 2: return pick_kp<2, kFull>(KP);
+    case 4: return pick_kp<4, kFull>(KP);
+    default: return pick_kp<8, kFull>(KP);
   }
+}
+
+// Up to one workgroup per CU (256 CUs): the uncapped instantiations.
+constexpr int64_t kRbFewProblems = 256;
+
+RbKernel pick_kernel(int KR, int KP, int64_t B) {
+  if (B > kRbFewProblems && KR * KP <= 2)           // the only shapes the cap changes
+    return KR == 2 ? rebalance_kernel<2, 1, true> : KP == 2 ? rebalance_kernel<1, 2, true> : rebalance_kernel<1, 1, true>;
+  return pick_kr<false>(KR, KP);
 }
 
 }  // namespace
@@ -1259,7 +1340,7 @@ hipError_t launch_rebalance(const int64_t* load, int64_t B, const RbPlan& plan,
                             int32_t* phy2log, int32_t* log2phy, int32_t* logcnt,
                             int32_t* status, hipStream_t stream) {
   if (B == 0) return hipSuccess;
-  pick_kernel(plan.KR, plan.KP)<<<(unsigned)B, plan.threads, plan.lds_bytes, stream>>>(
+  pick_kernel(plan.KR, plan.KP, B)<<<(unsigned)B, plan.threads, plan.lds_bytes, stream>>>(
       load, plan, phy2log, log2phy, logcnt, status);
   return hipGetLastError();
 }

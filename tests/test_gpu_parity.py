@@ -262,6 +262,11 @@ def test_decode_144_global():
     (90, 1, 1, 90, 180),
     (256, 8, 1, 200, 800),    # 200 packs of 4 over four registers
     (256, 1, 1, 256, 512),    # 256 packs: every pack index of the one-word form
+    (65, 5, 1, 5, 70),        # replication on the first 64 experts, one expert behind them
+    (128, 1, 1, 16, 160),     # 32 replicas among 128 experts
+    (512, 1, 1, 8, 576),      # 64 replicas among 512 experts (eight registers)
+    (384, 6, 2, 16, 512),     # two nodes of 192 experts, 64 replicas each
+    (256, 8, 3, 40, 320),     # global: 64 replicas among 256 (the decode shape)
 ])
 def test_shapes_random(shape):
     E, G, N, RK, P = shape
