@@ -271,7 +271,7 @@ def test_ema_redirect_ragged(L, T, K, E, shift):
 def test_ema_redirect_full_size():
     """One step of the streaming workload (58 x 2^20 x 8 ids) with its
     placement: identical to eplb_load_ema followed by eplb_redirect, and to
-    the oracle on sampled layers."""
+    the oracle on every layer."""
     work = wl.STREAM_1M
     pl = work.placement
     L, E = work.layers, pl.E
@@ -285,8 +285,10 @@ def test_ema_redirect_full_size():
     torch.cuda.synchronize()
     for name, a, b in (("ema", ema_a, ema_b), ("count", cnt_a, cnt_b), ("invalid", bad_a, bad_b), ("out", out_a, out_b)):
         assert bool(torch.equal(a, b)), f"{name}: fused differs from the two separate calls"
-    idx_h = host(idx[[0, 57]])
-    ref = ora.redirect(idx_h, host(placement[1][[0, 57]]), host(placement[2][[0, 57]]))
-    assert_same("sampled layers", host(out_b[[0, 57]]), ref)
+    idx_h = host(idx)
+    l2p_h, cnt_h, out_h = host(placement[1]), host(placement[2]), host(out_b)
     c, _ = ora.load_hist(idx_h, E)
-    assert_same("sampled counts", host(cnt_b[[0, 57]]).astype(np.int64), c)
+    assert_same("counts", host(cnt_b).astype(np.int64), c)
+    for l in range(L):
+        assert_same(f"redirect layer {l}", out_h[l:l + 1],
+                    ora.redirect(idx_h[l:l + 1], l2p_h[l:l + 1], cnt_h[l:l + 1]))
