@@ -35,10 +35,15 @@
 //                With 4 or more packs in the one-word form, RUNS of items
 //                go at once: item j+s takes the pack at position s while
 //                that pack stays below every earlier item's updated pack,
-//                which each lane checks for its own item in parallel.
+//                which each lane checks for its own item in parallel; up to
+//                64 packs are then re-sorted by a sorting network across
+//                the lanes, more in LDS.
 //   replication  positions hold experts ordered by (load per replica desc,
 //                index asc).  The expert at position 0 gets the replica and
-//                is re-inserted the same way.
+//                is re-inserted the same way.  With 24 to 64 replicas on a
+//                node they are all taken at once instead (the D'Hondt form:
+//                the first Rn of the candidates u / k in the greedy's own
+//                order, found by counting and a sorting network).
 // After replication the experts are already in the order step 3 visits them
 // (per-replica load desc); the stable order of the node's physical experts
 // (equal loads in ascending physical index) follows from prefix sums over
@@ -379,7 +384,7 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
   return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// pack_words for 17 to 64 * K packs (K <= 4 registers), with runs of items
+// pack_words for 65 to 64 * K packs (K = 2..4 registers), with runs of items
 // placed at once.  The packs' words are sorted and all distinct (a full or
 // absent pack is a sentinel: all-ones sum and its pack bits, above every
 // real word; real sums stay below 2^48 - 1).  Item j+s goes to the s-th
@@ -396,7 +401,6 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
 // new position in LDS.  The result is the sequential greedy's, item for
 // item.  scr: 64 * K + 64 words and 64 * K + 1 counters of this wave's LDS
 // (16-byte aligned): the sorted words, the run's updated words, the histogram.
-constexpr int kWideMinPacks = 17;      // one register per lane: from here on the words are searched in LDS
 
 // inclusive prefix sum over the lanes plus `carry`, which becomes the total so far
 __device__ __forceinline__ int wave_incl_sum_carry(int v, int& carry) {
@@ -484,15 +488,17 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
   }
 }
 
-// The same runs for at most M <= 16 packs, all in registers and DPP moves.
+// The same runs for at most M <= 64 packs, all in registers and cross-lane
+// moves (DPP within rows of 16, ds_bpermute across them).
 // The m real packs sit sorted in lanes 0..m-1 (open packs first, then full
 // ones) and lanes m..63 hold absent-pack sentinels above them.  Lane s of a
 // run takes item j+s exactly while its own word is below the updated word of
 // every earlier lane (that is, s < q_t for every t < s), so the run is found
 // from the exclusive prefix minimum of the updated words; then the run's
 // updated words and the other packs' words are put back in order by a
-// bitonic sorting network over the first M lanes.  The next run's keys are
-// fetched (ds_bpermute) while the network runs.
+// bitonic sorting network over the first M lanes (6, 10, 15 or 21 stages for
+// 8, 16, 32 or 64).  The next run's keys are fetched (ds_bpermute) while the
+// network runs.
 constexpr int kFewMinPacks = 4;        // fewer packs: runs are at most that long, the sequential form is faster
 
 // partner of each lane in a sorting-network stage: lane ^ kX within rows of 16
@@ -509,17 +515,26 @@ __device__ __forceinline__ int xlane(int x) {
   }
   return x;
 }
+// lane ^ kX over the whole wave: within rows by DPP (row_ror:8 for 8), across
+// rows by ds_bpermute
+template <int kX>
+__device__ __forceinline__ int xlane64(int x) {
+  if constexpr (kX == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);   // row_ror:8
+  else if constexpr (kX >= 16) return __shfl(x, lane_id() ^ kX);
+  else return xlane<kX>(x);
+}
 // one compare-exchange stage: the lane whose `kLow` bit is clear keeps the
 // smaller word of the pair (all words distinct)
 template <int kX, int kLow>
 __device__ __forceinline__ u64 cx_stage(u64 x) {
-  const int lo = xlane<kX>((int)(uint32_t)x);
-  const int hi = xlane<kX>((int)(uint32_t)(x >> 32));
+  const int lo = xlane64<kX>((int)(uint32_t)x);
+  const int hi = xlane64<kX>((int)(uint32_t)(x >> 32));
   const u64 px = ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
   const bool lower = (lane_id() & kLow) == 0;
   return (lower == (px < x)) ? px : x;
 }
-// ascending sort of the words in each block of M lanes (M = 8 or 16)
+// ascending sort of the words in each block of M lanes (M = 8, 16, 32, 64):
+// merges of 2, 4, ..., M lanes, each a mirror stage and then half-cleaners
 template <int M>
 __device__ __forceinline__ u64 sort_lanes(u64 x) {
   x = cx_stage<1, 1>(x);
@@ -528,8 +543,23 @@ __device__ __forceinline__ u64 sort_lanes(u64 x) {
   x = cx_stage<7, 4>(x);
   x = cx_stage<2, 2>(x);
   x = cx_stage<1, 1>(x);
-  if constexpr (M == 16) {
+  if constexpr (M >= 16) {
     x = cx_stage<15, 8>(x);
+    x = cx_stage<4, 4>(x);
+    x = cx_stage<2, 2>(x);
+    x = cx_stage<1, 1>(x);
+  }
+  if constexpr (M >= 32) {
+    x = cx_stage<31, 16>(x);
+    x = cx_stage<8, 8>(x);
+    x = cx_stage<4, 4>(x);
+    x = cx_stage<2, 2>(x);
+    x = cx_stage<1, 1>(x);
+  }
+  if constexpr (M == 64) {
+    x = cx_stage<63, 32>(x);
+    x = cx_stage<16, 16>(x);
+    x = cx_stage<8, 8>(x);
     x = cx_stage<4, 4>(x);
     x = cx_stage<2, 2>(x);
     x = cx_stage<1, 1>(x);
@@ -551,13 +581,17 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
       u64 us = w + k;
       if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
       u64 pmin = us;                               // prefix minimum of us within the first M lanes
-      pmin = min(pmin, dpp64<0x111>(~0ull, pmin));
-      pmin = min(pmin, dpp64<0x112>(~0ull, pmin));
-      pmin = min(pmin, dpp64<0x114>(~0ull, pmin));
-      if constexpr (M == 16) pmin = min(pmin, dpp64<0x118>(~0ull, pmin));
+      if constexpr (M <= 16) {
+        pmin = min(pmin, dpp64<0x111>(~0ull, pmin));
+        pmin = min(pmin, dpp64<0x112>(~0ull, pmin));
+        pmin = min(pmin, dpp64<0x114>(~0ull, pmin));
+        if constexpr (M == 16) pmin = min(pmin, dpp64<0x118>(~0ull, pmin));
+      } else {
+        pmin = wave_scan_incl<u64>(pmin, ~0ull, [](u64 a, u64 b) { return a < b ? a : b; });
+      }
       const u64 before = shr1_or64(~0ull, pmin);  // over the lanes before this one
       const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < tn && real && w < before);
-      const int mb = __builtin_ctzll(~vm);         // lane 0 is always valid, lane m never
+      const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);   // lane 0 is always valid; all 64 only when m = 64
       if (lane < mb) res[t0 + j + lane] = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
       j += mb;
       k = shfl64(kk, (j + lane) & 63);
@@ -584,12 +618,10 @@ __device__ void pack_words(KeyOf key_of, int n, int m, int cap, int32_t* res, u6
     return;
   }
   if constexpr (K == 1) {
-    if (m >= kWideMinPacks) {
-      pack_words_wide<1>(key_of, n, m, cap, res, scr);
-      return;
-    }
     if (m >= kFewMinPacks) {
-      if (m > 8) pack_words_few<16>(key_of, n, m, cap, res);
+      if (m > 32) pack_words_few<64>(key_of, n, m, cap, res);
+      else if (m > 16) pack_words_few<32>(key_of, n, m, cap, res);
+      else if (m > 8) pack_words_few<16>(key_of, n, m, cap, res);
       else pack_words_few<8>(key_of, n, m, cap, res);
       return;
     }
@@ -710,6 +742,151 @@ __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep
     ci[r] = (ci[r] & ~0xffff) | (511 - (ci[r] & 0xffff));
     u[r] >>= 9;
   }
+}
+
+// ---------------------------------------------------------------- replication by selection
+// The greedy's replicas taken at once (the D'Hondt form of step 2).  Expert
+// e's k-th extra replica is the candidate (e, k) of value u_e / k; the greedy
+// hands out candidates in the order value desc, expert index asc, k asc
+// (each expert's own candidates come in that order, and every step takes the
+// first of the experts' next candidates), so its Rn replicas are the first Rn
+// candidates in that order, and its creation order is theirs.  On one
+// register of experts (lanes sorted by load desc, index asc, count 1 each;
+// lanes without an expert hold load 0 and index 0xffff) and Rn <= 64:
+//  1. the replica count x0 of the expert in lane 0 (the first in the order):
+//     the largest k <= Rn whose candidate (0, k) has fewer than Rn
+//     candidates ahead of it.  Lane e has floor((u_e k - t_e) / u_0) of its
+//     own ahead of (0, k), t_e = 0 when its index is below lane 0's (it wins
+//     ties) else 1, computed with a double reciprocal and an exact integer
+//     correction; a binary search over k;
+//  2. every candidate ahead of (0, x0) is taken and none behind (0, x0 + 1);
+//     a lane has at most one between the two (its k there lie in an
+//     interval of length u_e / u_0 <= 1), and the first Rn - rank(0, x0) - 1
+//     of those are taken, ranked by counting over the lanes that have one;
+//  3. the taken candidates, one per lane, go through a 64-lane sorting
+//     network for the creation order (rep[r] = index | k << 16, as the
+//     sequential chain records them);
+//  4. the experts go through the same network for their final order (load
+//     per replica desc, index asc).
+// Elements of the network are (u, m << 16 | tb): the one with the larger
+// u / m comes first, ties to the smaller tb; one 64-bit compare of
+// (u_a m_b) << 16 | (0xffff - tb_a) against the same with a and b swapped
+// decides (u <= 2^40, m <= 65: below 2^63).  A lane takes its partner's
+// element only when that one strictly comes first (lower lane of the pair)
+// or strictly second (upper lane), so equal elements are never duplicated.
+constexpr int kSelectMinPicks = 24;    // fewer replicas: the sequential chain is as short
+
+template <int kX, int kLow>
+__device__ __forceinline__ void cx_ratio(u64& u, int& p) {
+  const int plo = xlane64<kX>((int)(uint32_t)u);
+  const int phi = xlane64<kX>((int)(uint32_t)(u >> 32));
+  const int pp = xlane64<kX>(p);
+  const u64 pu = ((u64)(uint32_t)phi << 32) | (uint32_t)plo;
+  const u64 km = ((u * (u64)(uint32_t)(pp >> 16)) << 16) | (u64)(uint32_t)(0xffff - (p & 0xffff));
+  const u64 kt = ((pu * (u64)(uint32_t)(p >> 16)) << 16) | (u64)(uint32_t)(0xffff - (pp & 0xffff));
+  const bool lower = (lane_id() & kLow) == 0;
+  const bool take = lower ? kt > km : km > kt;
+  u = take ? pu : u;
+  p = take ? pp : p;
+}
+// first-to-last order over the 64 lanes: merges of 2, 4, ..., 64 lanes, each
+// a mirror stage and then half-cleaners
+__device__ __forceinline__ void sort_ratio64(u64& u, int& p) {
+  cx_ratio<1, 1>(u, p);
+  cx_ratio<3, 2>(u, p);
+  cx_ratio<1, 1>(u, p);
+  cx_ratio<7, 4>(u, p);
+  cx_ratio<2, 2>(u, p);
+  cx_ratio<1, 1>(u, p);
+  cx_ratio<15, 8>(u, p);
+  cx_ratio<4, 4>(u, p);
+  cx_ratio<2, 2>(u, p);
+  cx_ratio<1, 1>(u, p);
+  cx_ratio<31, 16>(u, p);
+  cx_ratio<8, 8>(u, p);
+  cx_ratio<4, 4>(u, p);
+  cx_ratio<2, 2>(u, p);
+  cx_ratio<1, 1>(u, p);
+  cx_ratio<63, 32>(u, p);
+  cx_ratio<16, 16>(u, p);
+  cx_ratio<8, 8>(u, p);
+  cx_ratio<4, 4>(u, p);
+  cx_ratio<2, 2>(u, p);
+  cx_ratio<1, 1>(u, p);
+}
+
+// (u, ci) as replicate_sorted<1> takes and leaves them (ci = count << 16 |
+// index); rep: Rn ints of LDS, also the scratch of the expansion.
+__device__ void replicate_select(u64& u, int& ci, int Rn, int32_t* rep) {
+  const int lane = lane_id();
+  const int ie = ci & 0xffff;
+  const u64 u0 = rdl64(u, 0);
+  int x;                                  // replicas taken by this lane's expert
+  if (u0 == 0) {
+    x = lane == 0 ? Rn : 0;               // all loads zero: the lowest index takes every replica
+  } else {
+    const int i0 = rdl(ie, 0);
+    const bool live = lane != 0 && u != 0;
+    const u64 t = ie < i0 ? 0 : 1;
+    const double r0 = 1.0 / (double)u0;
+    auto ahead = [&](int k) -> int {      // this lane's candidates ahead of (0, k)
+      const u64 num = live ? u * (u64)(uint32_t)k - t : 0;
+      u64 q = (u64)((double)num * r0);    // num < 2^47: within one of the quotient
+      if (q * u0 > num) q -= 1;
+      else if ((q + 1) * u0 <= num) q += 1;
+      return (int)q;
+    };
+    int lo = 1;
+    int hi = Rn;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mid - 1 + rdl(wave_incl_sum(ahead(mid)), 63) < Rn) lo = mid;
+      else hi = mid - 1;
+    }
+    const int a = ahead(lo);
+    const int b = ahead(lo + 1);
+    const int need = Rn - (lo - 1 + rdl(wave_incl_sum(a), 63)) - 1;
+    const bool cand = b > a;
+    const u64 cmask = ballot(cand);
+    x = lane == 0 ? lo : a;
+    if (need > 0) {
+      if (need == __popcll(cmask)) {
+        x += cand ? 1 : 0;
+      } else {
+        int r = 0;                        // candidates ahead of this lane's
+        for (u64 m = cmask; m != 0; m &= m - 1) {
+          const int f = __builtin_ctzll(m);
+          const u64 uf = rdl64(u, f);
+          const u64 bf = (u64)(uint32_t)rdl(b, f);
+          const int jf = rdl(ie, f);
+          const u64 l = uf * (u64)(uint32_t)b;
+          const u64 rr = u * bf;
+          r += (l > rr || (l == rr && jf < ie)) ? 1 : 0;
+        }
+        x += (cand && r < need) ? 1 : 0;
+      }
+    }
+  }
+  // one lane per replica: lane s < Rn takes replica k = s - off + 1 of the
+  // expert whose range [off, off + x) holds s (a marker at each range start,
+  // then a running maximum)
+  const int off = wave_incl_sum(x) - x;
+  if (lane < Rn) rep[lane] = 0;
+  wave_lds_sync();
+  if (x > 0) rep[off] = lane + 1;
+  wave_lds_sync();
+  const int mk = lane < Rn ? rep[lane] : 0;
+  const int o = max(wave_incl_max(mk) - 1, 0);
+  const u64 uo = shfl64(u, o);
+  const int io = __shfl(ie, o);
+  const int k = lane - __shfl(off, o) + 1;
+  u64 su = lane < Rn ? uo : 0;
+  int sp = lane < Rn ? (k << 16) | (io << 7) | k : (1 << 16) | 0xffff;
+  sort_ratio64(su, sp);
+  if (lane < Rn) rep[lane] = ((sp & 0xffff) >> 7) | ((sp & 127) << 16);
+  int fp = ((x + 1) << 16) | ie;
+  sort_ratio64(u, fp);
+  ci = fp;
 }
 
 // ---------------------------------------------------------------- LDS carving
@@ -861,13 +1038,14 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   }
   bool window = false;
   if constexpr (K > 1) window = p.Rn <= 64;          // En > 64 here
-  if (window) {
+  if (K == 1 || window) {
     u64 uw[1] = {u[0]};
     int cw[1] = {ci[0]};
-    replicate_sorted<1>(uw, cw, p.Rn, s.rep + n * p.Rn);
+    if (p.Rn >= kSelectMinPicks && p.Rn <= 64) replicate_select(uw[0], cw[0], p.Rn, s.rep + n * p.Rn);
+    else replicate_sorted<1>(uw, cw, p.Rn, s.rep + n * p.Rn);
     u[0] = uw[0];
     ci[0] = cw[0];
-    merge_window<K>(p, s, n, u, ci);
+    if (window) merge_window<K>(p, s, n, u, ci);
   } else {
     replicate_sorted<K>(u, ci, p.Rn, s.rep + n * p.Rn);
   }
@@ -1302,14 +1480,13 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.o_cnt = take(4ll * E, 4);
   p.o_srt = take(4ll * E, 4);
   p.o_rep = take(4ll * Np * rn1, 4);
-  // lane-parallel packing scratch: step 3 in the one-word form with more than
-  // 16 GPUs per node (or more than 64), step 1 with 17 to 64 nodes
-  const bool wide3 = p.KP <= 4 && (p.KP > 1 || p.RKn >= kWideMinPacks);
-  const bool wide1 = p.KN == 1 && Np >= kWideMinPacks && p.gpn > 1;
+  // lane-parallel packing scratch: step 3 in the one-word form with 65 to
+  // 256 GPUs per node (up to 64 packs run in registers)
+  const bool wide3 = p.KP > 1 && p.KP <= 4;
   const int kw = wide3 ? p.KP : 1;
   const int64_t pk_bytes = (8ll * (64 * kw + 64) + 4ll * (64 * kw + 1) + 15) / 16 * 16;
   p.pk_words = (int32_t)(pk_bytes / 8);
-  p.o_pk = (wide3 || wide1) ? take(pk_bytes * nscr, 16) : 0;
+  p.o_pk = wide3 ? take(pk_bytes * nscr, 16) : 0;
   // Two overlaid regions: the loads and step-1 arrays die once the mlog
   // order is built; the per-wave step-3 scratch is used only after that.
   const int64_t base = (off + 15) / 16 * 16;

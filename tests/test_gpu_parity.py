@@ -279,6 +279,50 @@ def test_shapes_random(shape):
     rebalance_both(load, P, G, N, RK)
 
 
+def _selection_loads(E, seed):
+    """Load patterns that stress the replicas-at-once form of step 2: zeros,
+    equal loads, small-integer ties, exact ratio ties (multiples of one
+    base), loads near 2^40, Zipf, one hot expert, and the heaviest expert
+    holding the highest index (it loses every tie of value)."""
+    rng = np.random.default_rng(seed)
+    rows = [
+        np.zeros(E),
+        np.full(E, 7),
+        rng.integers(0, 4, size=E),
+        rng.integers(1, 30) * rng.choice([1, 2, 3, 4, 6, 12, 60], size=E),
+        rng.integers((1 << 40) - 64, (1 << 40) + 1, size=E),
+        (rng.zipf(1.2, size=E) * 1000).clip(0, 1 << 40),
+        np.where(np.arange(E) == rng.integers(0, E), 1 << 40, 1),
+        np.arange(E) * 3,
+        (E - np.arange(E)) * 5,
+        rng.integers(0, 1000, size=E) * rng.integers(0, 2, size=E),
+        np.where(np.arange(E) % 2 == 0, 12, 0),
+        np.where(np.arange(E) >= E - 2, 360, rng.choice([0, 40, 60, 90, 120, 180], size=E)),
+    ]
+    return np.stack(rows).astype(np.int64)
+
+
+@pytest.mark.parametrize("shape", [
+    (64, 1, 1, 8, 88),          # 24 replicas among 64 experts (the smallest count taken at once)
+    (40, 1, 1, 8, 104),         # 64 replicas among 40 experts
+    (33, 3, 1, 11, 66),         # 33 among 33
+    (128, 2, 2, 16, 192),       # two nodes of 64 experts, 32 replicas each
+    (100, 4, 2, 10, 150),       # two nodes of 50, 25 each
+    (512, 8, 8, 64, 1024),      # eight nodes of 64, 64 each
+    (1, 1, 1, 1, 25),           # one expert, 24 replicas
+    (2, 1, 1, 2, 66),           # two experts, 64 replicas
+    (130, 2, 2, 26, 234),       # two nodes of 65: one expert behind the first 64
+    (200, 8, 1, 8, 264),        # 64 replicas among 200 experts
+    (256, 8, 18, 144, 288),     # global: 32 replicas among 256 (the 144-GPU decode shape)
+    (256, 8, 3, 40, 320),       # global: 64 among 256 (the decode shape)
+])
+def test_replication_by_selection(shape):
+    """Nodes with 24 to 64 replicas, where step 2 takes its replicas at once
+    instead of one by one, against the oracle's one-by-one greedy."""
+    E, G, N, RK, P = shape
+    rebalance_both(_selection_loads(E, E * 7 + P), P, G, N, RK)
+
+
 def _fuzz_shapes(rng, count):
     """Valid placement shapes of every kind: hierarchical and global, 1 to 200
     GPUs per node (the sequential, register-run and LDS-run packing forms, one
