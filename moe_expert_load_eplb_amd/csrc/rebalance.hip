@@ -767,52 +767,75 @@ __device__ void replicate_sorted(u64 (&u)[K], int (&ci)[K], int Rn, int32_t* rep
 //     network for the creation order (rep[r] = index | k << 16, as the
 //     sequential chain records them);
 //  4. the experts go through the same network for their final order (load
-//     per replica desc, index asc).
-// Elements of the network are (u, m << 16 | tb): the one with the larger
-// u / m comes first, ties to the smaller tb; one 64-bit compare of
-// (u_a m_b) << 16 | (0xffff - tb_a) against the same with a and b swapped
-// decides (u <= 2^40, m <= 65: below 2^63).  A lane takes its partner's
-// element only when that one strictly comes first (lower lane of the pair)
-// or strictly second (upper lane), so equal elements are never duplicated.
+//     per replica desc, index asc), carrying their source lane, from which
+//     load and count are fetched.
+// The networks order exact integer keys: for c <= 65 and u <= 2^40,
+// floor(u * 8192 / c) is strictly monotone in u / c (two distinct values
+// differ by at least 1 / (c_a c_b) >= 1 / 4225) and equal for equal values,
+// so ((2^53 - floor(u * 8192 / c)) << 9) | index (below 2^63) puts the larger
+// u / c first and breaks ties of value to the smaller index, with one 64-bit
+// compare per stage.  Each element carries a 32-bit payload along.
 constexpr int kSelectMinPicks = 24;    // fewer replicas: the sequential chain is as short
 
-template <int kX, int kLow>
-__device__ __forceinline__ void cx_ratio(u64& u, int& p) {
-  const int plo = xlane64<kX>((int)(uint32_t)u);
-  const int phi = xlane64<kX>((int)(uint32_t)(u >> 32));
-  const int pp = xlane64<kX>(p);
-  const u64 pu = ((u64)(uint32_t)phi << 32) | (uint32_t)plo;
-  const u64 km = ((u * (u64)(uint32_t)(pp >> 16)) << 16) | (u64)(uint32_t)(0xffff - (p & 0xffff));
-  const u64 kt = ((pu * (u64)(uint32_t)(p >> 16)) << 16) | (u64)(uint32_t)(0xffff - (pp & 0xffff));
-  const bool lower = (lane_id() & kLow) == 0;
-  const bool take = lower ? kt > km : km > kt;
-  u = take ? pu : u;
-  p = take ? pp : p;
+// floor(u * 8192 / c): floor(u / c) by a double reciprocal (within one of it,
+// u <= 2^40) and a remainder check, then the fraction's 13 bits the same way
+__device__ __forceinline__ u64 ratio_floor(u64 u, uint32_t c) {
+  const double rc = 1.0 / (double)c;
+  u64 q = (u64)((double)u * rc);
+  int64_t r = (int64_t)u - (int64_t)(q * c);
+  if (r < 0) {
+    q -= 1;
+    r += c;
+  } else if (r >= (int64_t)c) {
+    q += 1;
+    r -= c;
+  }
+  const uint32_t rs = (uint32_t)r << 13;
+  uint32_t f = (uint32_t)((double)rs * rc);
+  if ((f + 1) * c <= rs) f += 1;
+  return (q << 13) | f;
 }
-// first-to-last order over the 64 lanes: merges of 2, 4, ..., 64 lanes, each
-// a mirror stage and then half-cleaners
-__device__ __forceinline__ void sort_ratio64(u64& u, int& p) {
-  cx_ratio<1, 1>(u, p);
-  cx_ratio<3, 2>(u, p);
-  cx_ratio<1, 1>(u, p);
-  cx_ratio<7, 4>(u, p);
-  cx_ratio<2, 2>(u, p);
-  cx_ratio<1, 1>(u, p);
-  cx_ratio<15, 8>(u, p);
-  cx_ratio<4, 4>(u, p);
-  cx_ratio<2, 2>(u, p);
-  cx_ratio<1, 1>(u, p);
-  cx_ratio<31, 16>(u, p);
-  cx_ratio<8, 8>(u, p);
-  cx_ratio<4, 4>(u, p);
-  cx_ratio<2, 2>(u, p);
-  cx_ratio<1, 1>(u, p);
-  cx_ratio<63, 32>(u, p);
-  cx_ratio<16, 16>(u, p);
-  cx_ratio<8, 8>(u, p);
-  cx_ratio<4, 4>(u, p);
-  cx_ratio<2, 2>(u, p);
-  cx_ratio<1, 1>(u, p);
+__device__ __forceinline__ u64 ratio_key(u64 u, uint32_t c, int index) {
+  return (((1ull << 53) - ratio_floor(u, c)) << 9) | (u64)(uint32_t)index;
+}
+// one compare-exchange stage on (key, payload): the lane whose kLow bit is
+// clear keeps the smaller key; a lane moves only on a strict compare, so
+// equal keys never duplicate a payload
+template <int kX, int kLow>
+__device__ __forceinline__ void cx_kv(u64& k, int& v) {
+  const int plo = xlane64<kX>((int)(uint32_t)k);
+  const int phi = xlane64<kX>((int)(uint32_t)(k >> 32));
+  const int pv = xlane64<kX>(v);
+  const u64 pk = ((u64)(uint32_t)phi << 32) | (uint32_t)plo;
+  const bool lower = (lane_id() & kLow) == 0;
+  const bool take = lower ? pk < k : pk > k;
+  k = take ? pk : k;
+  v = take ? pv : v;
+}
+// ascending order of the keys over the 64 lanes: merges of 2, 4, ..., 64
+// lanes, each a mirror stage and then half-cleaners
+__device__ __forceinline__ void sort_kv64(u64& k, int& v) {
+  cx_kv<1, 1>(k, v);
+  cx_kv<3, 2>(k, v);
+  cx_kv<1, 1>(k, v);
+  cx_kv<7, 4>(k, v);
+  cx_kv<2, 2>(k, v);
+  cx_kv<1, 1>(k, v);
+  cx_kv<15, 8>(k, v);
+  cx_kv<4, 4>(k, v);
+  cx_kv<2, 2>(k, v);
+  cx_kv<1, 1>(k, v);
+  cx_kv<31, 16>(k, v);
+  cx_kv<8, 8>(k, v);
+  cx_kv<4, 4>(k, v);
+  cx_kv<2, 2>(k, v);
+  cx_kv<1, 1>(k, v);
+  cx_kv<63, 32>(k, v);
+  cx_kv<16, 16>(k, v);
+  cx_kv<8, 8>(k, v);
+  cx_kv<4, 4>(k, v);
+  cx_kv<2, 2>(k, v);
+  cx_kv<1, 1>(k, v);
 }
 
 // (u, ci) as replicate_sorted<1> takes and leaves them (ci = count << 16 |
@@ -880,13 +903,22 @@ __device__ void replicate_select(u64& u, int& ci, int Rn, int32_t* rep) {
   const u64 uo = shfl64(u, o);
   const int io = __shfl(ie, o);
   const int k = lane - __shfl(off, o) + 1;
-  u64 su = lane < Rn ? uo : 0;
-  int sp = lane < Rn ? (k << 16) | (io << 7) | k : (1 << 16) | 0xffff;
-  sort_ratio64(su, sp);
-  if (lane < Rn) rep[lane] = ((sp & 0xffff) >> 7) | ((sp & 127) << 16);
-  int fp = ((x + 1) << 16) | ie;
-  sort_ratio64(u, fp);
-  ci = fp;
+  // creation order (the payload is the record); with every load zero, lane
+  // 0's replicas k = 1..Rn are in order already (value 0, index, then k)
+  u64 pk = lane < Rn ? ratio_key(uo, (uint32_t)k, io) : ~0ull;
+  int pv = io | (k << 16);
+  if (u0 != 0) sort_kv64(pk, pv);
+  if (lane < Rn) rep[lane] = pv;
+  // final order of the experts (the payload is the source lane); lanes
+  // without an expert sort last
+  u64 fk = ie != 0xffff ? ratio_key(u, (uint32_t)(x + 1), ie) : ~0ull;
+  int src = lane;
+  sort_kv64(fk, src);
+  const u64 uf = shfl64(u, src);
+  const int cf = __shfl(x + 1, src);
+  const int jf = __shfl(ie, src);
+  u = uf;
+  ci = (cf << 16) | jf;
 }
 
 // ---------------------------------------------------------------- LDS carving
@@ -1022,18 +1054,29 @@ template <int K>
 __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   const int lane = lane_id();
   const int En = p.En;
+  // the node's experts by (load desc, local index asc): up to 64 sorted here
+  // in one register, as ~(key + 1) ascending for the unique keys
+  // load << 9 | (511 - local index) (loads <= 2^40, local indices < 512;
+  // lanes past En: all ones); larger nodes ranked by the workgroup into srt
   u64 u[K];
   int ci[K];
+  if constexpr (K == 1) {
+    const u64 v = lane < En ? ~(((s.wl[n * En + lane] << 9) | (u64)(511 - lane)) + 1) : ~0ull;
+    const u64 key = ~sort_lanes<64>(v) - 1;
+    u[0] = lane < En ? key >> 9 : 0;
+    ci[0] = (1 << 16) | (lane < En ? 511 - (int)(key & 511) : 0xffff);
+  } else {
 #pragma unroll
-  for (int r = 0; r < K; ++r) {
-    const int pos = r * 64 + lane;
-    if (pos < En) {
-      const int i = s.srt[n * En + pos];
-      u[r] = s.wl[n * En + i];
-      ci[r] = (1 << 16) | i;
-    } else {
-      u[r] = 0;
-      ci[r] = (1 << 16) | 0xffff;
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      if (pos < En) {
+        const int i = s.srt[n * En + pos];
+        u[r] = s.wl[n * En + i];
+        ci[r] = (1 << 16) | i;
+      } else {
+        u[r] = 0;
+        ci[r] = (1 << 16) | 0xffff;
+      }
     }
   }
   bool window = false;
@@ -1358,34 +1401,37 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
     s.wl[m] = s.w[e];
   }
   __syncthreads();
-  // experts of each node by (load desc, local index asc), ranked by counting
-  // over the unique keys load << 9 | (511 - local index) (loads <= 2^40,
-  // local indices < 512); the keys take the place of the logical-order
-  // loads, which are dead once the mlog order is built
-  u64* key = s.w;
-  for (int m = tid; m < p.E; m += NT) {
-    const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-    key[m] = (s.wl[m] << 9) | (u64)(511 - (m - n * p.En));
-  }
-  __syncthreads();
-  for (int m = tid; m < p.E; m += NT) {
-    const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-    const int i = m - n * p.En;
-    const u64* kn = key + n * p.En;
-    const u64 ki = kn[i];
-    int rank = 0;
-    int h = 0;
-    for (; h + 8 <= p.En; h += 8) {            // eight reads in flight
-      u64 a[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) a[k] = kn[h + k];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rank += a[k] > ki ? 1 : 0;
+  if constexpr (KR > 1) {
+    // nodes of more than 64 experts: their experts by (load desc, local index
+    // asc), ranked by the whole workgroup, counting over the unique keys
+    // load << 9 | (511 - local index) (loads <= 2^40, local indices < 512); the
+    // keys take the place of the logical-order loads, dead once the mlog order
+    // is built.  Smaller nodes are sorted by their own wave in step 2.
+    u64* key = s.w;
+    for (int m = tid; m < p.E; m += NT) {
+      const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
+      key[m] = (s.wl[m] << 9) | (u64)(511 - (m - n * p.En));
     }
-    for (; h < p.En; ++h) rank += kn[h] > ki ? 1 : 0;
-    s.srt[n * p.En + rank] = i;
+    __syncthreads();
+    for (int m = tid; m < p.E; m += NT) {
+      const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
+      const int i = m - n * p.En;
+      const u64* kn = key + n * p.En;
+      const u64 ki = kn[i];
+      int rank = 0;
+      int h = 0;
+      for (; h + 8 <= p.En; h += 8) {            // eight reads in flight
+        u64 a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = kn[h + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rank += a[k] > ki ? 1 : 0;
+      }
+      for (; h < p.En; ++h) rank += kn[h] > ki ? 1 : 0;
+      s.srt[n * p.En + rank] = i;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- step 2 and the denominators, one wave per node
   for (int n = wid; n < p.Np; n += NW) node_replicate<KR>(p, s, n);
