@@ -1403,32 +1403,43 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
   __syncthreads();
   if constexpr (KR > 1) {
     // nodes of more than 64 experts: their experts by (load desc, local index
-    // asc), ranked by the whole workgroup, counting over the unique keys
-    // load << 9 | (511 - local index) (loads <= 2^40, local indices < 512); the
-    // keys take the place of the logical-order loads, dead once the mlog order
-    // is built.  Smaller nodes are sorted by their own wave in step 2.
-    u64* key = s.w;
-    for (int m = tid; m < p.E; m += NT) {
-      const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-      key[m] = (s.wl[m] << 9) | (u64)(511 - (m - n * p.En));
+    // asc) through the unique keys load << 9 | (511 - local index) (loads <=
+    // 2^40, local indices < 512), as v = ~(key + 1) ascending.  Each run of
+    // 64 of a node's experts is sorted by one wave (into the logical-order
+    // loads' place, dead once the mlog order is built); an expert's rank in
+    // its node is then its place in its run plus, for every other run, the
+    // number of that run's values below its own (binary search).  Smaller
+    // nodes are sorted by their own wave in step 2.
+    u64* sv = s.w;
+    const int runs = (p.En + 63) >> 6;
+    for (int c = wid; c < p.Np * runs; c += NW) {
+      const int n = c / runs;
+      const int j = (c - n * runs) * 64 + lane;
+      const u64 v = j < p.En ? ~(((s.wl[n * p.En + j] << 9) | (u64)(511 - j)) + 1) : ~0ull;
+      const u64 sorted = sort_lanes<64>(v);
+      if (j < p.En) sv[n * p.En + j] = sorted;
     }
     __syncthreads();
-    for (int m = tid; m < p.E; m += NT) {
-      const int n = (int)fastdiv_apply((uint32_t)m, p.fd_En);
-      const int i = m - n * p.En;
-      const u64* kn = key + n * p.En;
-      const u64 ki = kn[i];
-      int rank = 0;
-      int h = 0;
-      for (; h + 8 <= p.En; h += 8) {            // eight reads in flight
-        u64 a[8];
+    for (int c = wid; c < p.Np * runs; c += NW) {
+      const int n = c / runs;
+      const int r = c - n * runs;
+      const int j = r * 64 + lane;
+      if (j < p.En) {
+        const u64* sn = sv + n * p.En;
+        const u64 v = sn[j];
+        int rank = lane;
+        for (int o = 0; o < runs; ++o) {
+          if (o == r) continue;
+          const u64* a = sn + o * 64;
+          const int len = min(64, p.En - o * 64);
+          int lo = 0;                                // values of run o below v
 #pragma unroll
-        for (int k = 0; k < 8; ++k) a[k] = kn[h + k];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rank += a[k] > ki ? 1 : 0;
+          for (int step = 64; step >= 1; step >>= 1)
+            if (lo + step <= len && a[lo + step - 1] < v) lo += step;
+          rank += lo;
+        }
+        s.srt[n * p.En + rank] = 511 - (int)((~v - 1) & 511);
       }
-      for (; h < p.En; ++h) rank += kn[h] > ki ? 1 : 0;
-      s.srt[n * p.En + rank] = i;
     }
     __syncthreads();
   }
