@@ -600,6 +600,62 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
   }
 }
 
+// pack_words_few on 32-bit words, sum << 8 | pack << 4 | items, for 4 to 16
+// packs of at most 14 items and sums below 2^24 - 1 (a full or absent pack is
+// kSent32 with its pack bits and items 0xF): one DPP move, one compare and
+// one select per network stage instead of two of each.  key_of(t) = key << 8
+// | 1.
+template <int kX, int kLow>
+__device__ __forceinline__ uint32_t cx_stage32(uint32_t x) {
+  const uint32_t px = (uint32_t)xlane<kX>((int)x);
+  const bool lower = (lane_id() & kLow) == 0;
+  return (lower == (px < x)) ? px : x;
+}
+template <int M>
+__device__ __forceinline__ uint32_t sort_lanes32(uint32_t x) {
+  x = cx_stage32<1, 1>(x);
+  x = cx_stage32<3, 2>(x);
+  x = cx_stage32<1, 1>(x);
+  x = cx_stage32<7, 4>(x);
+  x = cx_stage32<2, 2>(x);
+  x = cx_stage32<1, 1>(x);
+  if constexpr (M == 16) {
+    x = cx_stage32<15, 8>(x);
+    x = cx_stage32<4, 4>(x);
+    x = cx_stage32<2, 2>(x);
+    x = cx_stage32<1, 1>(x);
+  }
+  return x;
+}
+template <int M, class KeyOf>
+__device__ void pack_words_few32(KeyOf key_of, int n, int m, int cap, int32_t* res) {
+  constexpr uint32_t kSent32 = 0xFFFFFF00u;
+  const int lane = lane_id();
+  uint32_t w = lane < m ? ((uint32_t)lane << 4) : (kSent32 | ((uint32_t)(lane & 15) << 4) | 0xFu);
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int tn = n - t0 < 64 ? n - t0 : 64;
+    const uint32_t kk = lane < tn ? key_of(t0 + lane) : 0u;
+    uint32_t k = kk;                               // lane s: key of item j + s
+    for (int j = 0; j < tn; ) {
+      const bool real = w < kSent32;
+      uint32_t us = w + k;
+      if ((int)(us & 0xF) == cap) us = kSent32 | (us & 0xF0u) | 0xFu;
+      uint32_t pmin = us;                          // prefix minimum of us within the first M lanes
+      pmin = min(pmin, (uint32_t)dpp<0x111>(-1, (int)pmin));
+      pmin = min(pmin, (uint32_t)dpp<0x112>(-1, (int)pmin));
+      pmin = min(pmin, (uint32_t)dpp<0x114>(-1, (int)pmin));
+      if constexpr (M == 16) pmin = min(pmin, (uint32_t)dpp<0x118>(-1, (int)pmin));
+      const uint32_t before = (uint32_t)shr1_or(-1, (int)pmin);   // over the lanes before this one
+      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < tn && real && w < before);
+      const int mb = __builtin_ctzll(~vm);         // lane 0 is always valid, lane M never
+      if (lane < mb) res[t0 + j + lane] = (int)((w >> 4) & 0xF) * cap + (int)(w & 0xF);
+      j += mb;
+      k = (uint32_t)__shfl((int)kk, (j + lane) & 63);
+      w = sort_lanes32<M>(lane < mb ? us : w);
+    }
+  }
+}
+
 // The same packing with each pack in ONE 64-bit word, sum << 16 | pack << 8 |
 // items, for sums below 2^48 - 1, at most 256 packs and at most 255 items per
 // pack.  Words of different packs differ in the pack bits, so one unsigned
@@ -941,7 +997,7 @@ struct Smem {
   int32_t* ordr;   // [nscr][Pn]  per wave: item (local expert | rank << 16) in visiting order
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
   int32_t* rcls;   // [nscr][Rn]  per wave: class of each replica
-  int32_t* nflag;  // [Np]  step-3 key form: 2 one word per pack, 1 64-bit sums, 0 128-bit sums
+  int32_t* nflag;  // [Np]  step-3 key form: 3 one 32-bit word per pack, 2 one 64-bit word, 1 64-bit sums, 0 128-bit sums
   int32_t* flags;  // [4]  [0]: problem status; [2..3]: the total load (u64, 8-byte aligned)
 };
 
@@ -1152,8 +1208,10 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
   const u128 total = mul_u128_u64(D, sum, ovf);
   if (lane == 0) {
     if (ovf || (total >> 127) != 0) s.flags[0] = EPLB_S_OVERFLOW;
-    // key width for step 3: one word per pack, 64-bit sums, or 128-bit sums
-    s.nflag[n] = total < (((u128)1 << 48) - 1) && p.RKn <= 256 && p.ppr <= 255 ? 2 : ((u64)(total >> 64) == 0 ? 1 : 0);
+    // key width for step 3: one 32-bit word per pack, one 64-bit word, 64-bit sums, or 128-bit sums
+    const bool w32 = total < (u128)((1u << 24) - 1) && p.RKn >= kFewMinPacks && p.RKn <= 16 && p.ppr <= 14;
+    s.nflag[n] = w32 ? 3 : total < (((u128)1 << 48) - 1) && p.RKn <= 256 && p.ppr <= 255 ? 2
+                                                                                        : ((u64)(total >> 64) == 0 ? 1 : 0);
   }
 #pragma unroll
   for (int r = 0; r < K; ++r) {
@@ -1263,7 +1321,11 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
     }
     wave_lds_sync();
     const u128* kexp = s.kexp + n * En;
-    if (width == 2) {
+    if (KP == 1 && width == 3) {
+      auto key = [=](int t) { return ((uint32_t)kexp[ordr[t] & 0xffff] << 8) | 1u; };
+      if (p.RKn > 8) pack_words_few32<16>(key, Pn, p.RKn, p.ppr, ores);
+      else pack_words_few32<8>(key, Pn, p.RKn, p.ppr, ores);
+    } else if (width >= 2) {
       auto key = [=](int t) { return ((u64)kexp[ordr[t] & 0xffff] << 16) | 1ull; };
       pack_words<KP>(key, Pn, p.RKn, p.ppr, ores, s.pk + ws * p.pk_words);
     } else if (width == 1) {

@@ -323,6 +323,28 @@ def test_replication_by_selection(shape):
     rebalance_both(_selection_loads(E, E * 7 + P), P, G, N, RK)
 
 
+@pytest.mark.parametrize("shape", [
+    (256, 8, 4, 32, 288),       # DeepSeek-V3 prefill: 8 GPUs per node, 9 slots each
+    (128, 4, 2, 32, 160),       # 16 GPUs per node, 5 slots each
+    (96, 4, 4, 16, 128),        # 4 GPUs per node, 8 slots each
+    (64, 2, 1, 8, 112),         # 8 GPUs, 14 slots each (the 32-bit form's largest pack)
+    (64, 2, 1, 8, 120),         # 8 GPUs, 15 slots each (beyond it: the 64-bit words)
+])
+def test_step3_word_widths(shape):
+    """The same shapes with loads scaled so that the node totals (times the
+    lcm of the counts) fall below 2^24, below 2^48 and above it: step 3
+    packs with 32-bit words, 64-bit words and wider sums, each against the
+    oracle."""
+    E, G, N, RK, P = shape
+    rng = np.random.default_rng(E + P)
+    base = (rng.zipf(1.3, size=(4, E)) * 7).clip(0, 1000)
+    base[1] = rng.integers(0, 1000, size=E)
+    base[2] = np.arange(E) % 13
+    base[3, : E // 2] = 0
+    for scale in (1, 1 << 11, 1 << 12, 1 << 22, 1 << 30):
+        rebalance_both((base * scale).clip(0, 1 << 40).astype(np.int64), P, G, N, RK)
+
+
 def _fuzz_shapes(rng, count):
     """Valid placement shapes of every kind: hierarchical and global, 1 to 200
     GPUs per node (the sequential, register-run and LDS-run packing forms, one
