@@ -1414,7 +1414,15 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
       for (int g = g0; g < p.Gp; g += gstep) {
         const u64 wg = s.gsum[g];
         int rank = 0;
-        for (int h = 0; h < p.Gp; ++h) {
+        int h = 0;
+        for (; h + 8 <= p.Gp; h += 8) {            // eight reads in flight
+          u64 a[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) a[k] = s.gsum[h + k];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rank += (a[k] > wg || (a[k] == wg && h + k < g)) ? 1 : 0;
+        }
+        for (; h < p.Gp; ++h) {
           const u64 wh = s.gsum[h];
           rank += (wh > wg || (wh == wg && h < g)) ? 1 : 0;
         }
@@ -1434,7 +1442,11 @@ void rebalance_kernel(const int64_t* __restrict__ load, RbPlan p,
       const bool words = tot < (1ull << 48) - 1 && p.Np <= 256 && p.gpn <= 255;
       const u64* gsum = s.gsum;
       const int32_t* gord = s.gord;
-      if (words) {
+      if (tot < (1u << 24) - 1 && p.Np >= kFewMinPacks && p.Np <= 16 && p.gpn <= 14) {
+        auto key = [=](int t) { return ((uint32_t)gsum[gord[t]] << 8) | 1u; };
+        if (p.Np > 8) pack_words_few32<16>(key, p.Gp, p.Np, p.gpn, s.gres);
+        else pack_words_few32<8>(key, p.Gp, p.Np, p.gpn, s.gres);
+      } else if (words) {
         auto key = [=](int t) { return (gsum[gord[t]] << 16) | 1ull; };
         if (p.KN == 1) pack_words<1>(key, p.Gp, p.Np, p.gpn, s.gres, s.pk);
         else pack_words<8>(key, p.Gp, p.Np, p.gpn, s.gres, s.pk);
