@@ -157,15 +157,13 @@ def main() -> int:
         hip.hipStreamSynchronize(stream.cuda_stream)
         lat_c.append((time.perf_counter() - a) * 1e6)
         assert rc == 0
-    reb_dev = []
-    for _ in range(50):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement)
-        e1.record(stream)
-        e1.synchronize()
-        reb_dev.append(e0.elapsed_time(e1) * 1e3)
-    reb_b2b = back_to_back_us(stream, lambda: eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement))
+    # device time: events around one C call with prepared arguments (the
+    # host's launch latency of that call is inside), around one Python
+    # binding call (adds the binding's argument checks), and per call with
+    # the calls enqueued back to back
+    reb_dev = events_us(stream, lambda: eplb.lib.eplb_rebalance(*c_args))
+    reb_dev_py = events_us(stream, lambda: eplb.rebalance(load, pl.P, pl.G, pl.N, pl.RK, X, out=placement))
+    reb_b2b = back_to_back_us(stream, lambda: eplb.lib.eplb_rebalance(*c_args))
 
     # serving-loop step: one fused pass (count this step + redirect it with the
     # placement in force), then the rebalance that gives the next placement
@@ -221,15 +219,10 @@ def main() -> int:
         outs = eplb.rebalance(ld, P, G, N, RK, Xo)
         torch.cuda.synchronize()
         assert int(outs[3].abs().sum()) == 0
-        ts = []
-        for _ in range(20):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            eplb.rebalance(ld, P, G, N, RK, Xo, out=outs)
-            b.record(stream)
-            b.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        b2b = back_to_back_us(stream, lambda: eplb.rebalance(ld, P, G, N, RK, Xo, out=outs))
+        args_ = (ld.data_ptr(), ld.shape[0], ld.shape[1], P, G, N, RK, Xo, *[t.data_ptr() for t in outs],
+                 stream.cuda_stream)
+        ts = events_us(stream, lambda: eplb.lib.eplb_rebalance(*args_))
+        b2b = back_to_back_us(stream, lambda: eplb.lib.eplb_rebalance(*args_))
         return {"device_us_median": round(statistics.median(ts), 2), "device_us_back_to_back": b2b}
     gd = wl.GLOBAL_DECODE
     gload = torch.from_numpy(wl.zipf_loads(gd.layers, gd.placement.E, gd.param,
@@ -348,6 +341,7 @@ def main() -> int:
         "rebalance_58_layers": {
             "shape": "E=256 G=8 N=4 RK=32 P=288 (hierarchical), 58 problems",
             "device_us_median": round(statistics.median(reb_dev), 2),
+            "device_us_median_python_call": round(statistics.median(reb_dev_py), 2),
             "device_us_back_to_back": reb_b2b,
             "api_to_completion_us_median": round(statistics.median(lat), 2),
             "c_abi_call_to_completion_us_median": round(statistics.median(lat_c), 2),
@@ -373,6 +367,21 @@ def main() -> int:
                                               placement, hist_bytes + redir_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def events_us(stream, call, n=50):
+    """HIP events on `stream` around each of n single calls (the GPU idle
+    before each), in us."""
+    import torch
+    out = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return out
 
 
 def back_to_back_us(stream, call, n=20, reps=5):
