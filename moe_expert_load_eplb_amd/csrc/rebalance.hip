@@ -37,7 +37,9 @@
 //                that pack stays below every earlier item's updated pack,
 //                which each lane checks for its own item in parallel; up to
 //                64 packs are then re-sorted by a sorting network across
-//                the lanes, more in LDS.
+//                the lanes, more in LDS.  A pack is one 64-bit word (sum,
+//                pack, items), or one 32-bit word when the sums stay below
+//                2^24 on at most 16 packs.
 //   replication  positions hold experts ordered by (load per replica desc,
 //                index asc).  The expert at position 0 gets the replica and
 //                is re-inserted the same way.  With 24 to 64 replicas on a
