@@ -234,6 +234,10 @@ def main() -> int:
                                                             gd.placement.N, gd.placement.RK),
         "skewed_1024x_e512_p640_8x8_us": reb_device_us(sload, sk.placement.P, sk.placement.G,
                                                        sk.placement.N, sk.placement.RK),
+        # the degenerate window: no expert received a token (every replica on
+        # expert 0, every per-replica load 0)
+        "global_decode_58L_zero_loads_us": reb_device_us(torch.zeros_like(gload), gd.placement.P, gd.placement.G,
+                                                         gd.placement.N, gd.placement.RK),
     }
 
     # the same stream redirected through a placement of the global-policy

@@ -386,6 +386,25 @@ __device__ __forceinline__ u64 shfl64(u64 x, int src) {
   return ((u64)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
+// The rest of a packing once every remaining item has load 0 (its key adds
+// only an item, so the sums, and with them the order of the packs, no
+// longer change): the greedy fills the packs in their current order, each
+// up to its capacity.  A pack at sorted position s with `fr` free slots and
+// `before` free slots ahead of it takes items first + before .. + fr - 1,
+// arriving after its `items` items.
+__device__ __forceinline__ void fill_zero_keys_from(int fr, int before, int pack, int items, int first, int n,
+                                                    int cap, int32_t* res) {
+  for (int q = 0; q < fr; ++q) {
+    const int t = first + before + q;
+    if (t < n) res[t] = pack * cap + items + q;
+  }
+}
+// the same for packs held one per lane (positions = lanes)
+__device__ __forceinline__ void fill_zero_keys(int fr, int pack, int items, int first, int n, int cap,
+                                               int32_t* res) {
+  fill_zero_keys_from(fr, wave_incl_sum(fr) - fr, pack, items, first, n, cap, res);
+}
+
 // pack_words for 65 to 64 * K packs (K = 2..4 registers), with runs of items
 // placed at once.  The packs' words are sorted and all distinct (a full or
 // absent pack is a sentinel: all-ones sum and its pack bits, above every
@@ -432,7 +451,8 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
-    for (int j = 0; j < tn; ) {
+    const int nz = __popcll(__builtin_amdgcn_ballot_w64(lane < tn && kk != 1ull));   // items of load > 0 first
+    for (int j = 0; j < nz; ) {
       const int it = j + lane;                     // this lane's candidate item
       const u64 k = shfl64(kk, it & 63);
       const bool real = w[0] < kSent;
@@ -454,7 +474,7 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
       }
       const int q = b == NG ? NP : GS * b + fine;  // words below us
       const int pm = shr1_or(1 << 20, wave_incl_min(q));   // minimum of q over the lanes before
-      const u64 vm = __builtin_amdgcn_ballot_w64(it < tn && real && lane < pm);
+      const u64 vm = __builtin_amdgcn_ballot_w64(it < nz && real && lane < pm);
       const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);      // lane 0 is always valid
       if (lane < mb) res[t0 + j + lane] = (int)((w[0] >> 8) & 0xff) * cap + (int)(w[0] & 0xff);
       wave_lds_sync();
@@ -486,6 +506,17 @@ __device__ void pack_words_wide(KeyOf key_of, int n, int m, int cap, int32_t* re
 #pragma unroll
       for (int r = 0; r < K; ++r) w[r] = sw[r * 64 + lane];
       j += mb;
+    }
+    if (nz < tn) {                                 // the rest has load 0
+      int carry = 0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int items = (int)(w[r] & 0xff);
+        const int fr = r * 64 + lane < m && w[r] < kSent ? cap - items : 0;
+        const int before = wave_incl_sum_carry(fr, carry) - fr;
+        fill_zero_keys_from(fr, before, (int)((w[r] >> 8) & 0xff), items, t0 + nz, n, cap, res);
+      }
+      return;
     }
   }
 }
@@ -577,8 +608,9 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
+    const int nz = __popcll(__builtin_amdgcn_ballot_w64(lane < tn && kk != 1ull));   // items of load > 0 first
     u64 k = kk;                                    // lane s: key of item j + s
-    for (int j = 0; j < tn; ) {
+    for (int j = 0; j < nz; ) {
       const bool real = w < kSent;
       u64 us = w + k;
       if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
@@ -592,12 +624,17 @@ __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res
         pmin = wave_scan_incl<u64>(pmin, ~0ull, [](u64 a, u64 b) { return a < b ? a : b; });
       }
       const u64 before = shr1_or64(~0ull, pmin);  // over the lanes before this one
-      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < tn && real && w < before);
+      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < nz && real && w < before);
       const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);   // lane 0 is always valid; all 64 only when m = 64
       if (lane < mb) res[t0 + j + lane] = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
       j += mb;
       k = shfl64(kk, (j + lane) & 63);
       w = sort_lanes<M>(lane < mb ? us : w);
+    }
+    if (nz < tn) {                                 // the rest has load 0
+      const int items = (int)(w & 0xff);
+      fill_zero_keys(lane < M && w < kSent ? cap - items : 0, (int)((w >> 8) & 0xff), items, t0 + nz, n, cap, res);
+      return;
     }
   }
 }
@@ -637,8 +674,9 @@ __device__ void pack_words_few32(KeyOf key_of, int n, int m, int cap, int32_t* r
   for (int t0 = 0; t0 < n; t0 += 64) {
     const int tn = n - t0 < 64 ? n - t0 : 64;
     const uint32_t kk = lane < tn ? key_of(t0 + lane) : 0u;
+    const int nz = __popcll(__builtin_amdgcn_ballot_w64(lane < tn && kk != 1u));   // items of load > 0 first
     uint32_t k = kk;                               // lane s: key of item j + s
-    for (int j = 0; j < tn; ) {
+    for (int j = 0; j < nz; ) {
       const bool real = w < kSent32;
       uint32_t us = w + k;
       if ((int)(us & 0xF) == cap) us = kSent32 | (us & 0xF0u) | 0xFu;
@@ -648,12 +686,17 @@ __device__ void pack_words_few32(KeyOf key_of, int n, int m, int cap, int32_t* r
       pmin = min(pmin, (uint32_t)dpp<0x114>(-1, (int)pmin));
       if constexpr (M == 16) pmin = min(pmin, (uint32_t)dpp<0x118>(-1, (int)pmin));
       const uint32_t before = (uint32_t)shr1_or(-1, (int)pmin);   // over the lanes before this one
-      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < tn && real && w < before);
+      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < nz && real && w < before);
       const int mb = __builtin_ctzll(~vm);         // lane 0 is always valid, lane M never
       if (lane < mb) res[t0 + j + lane] = (int)((w >> 4) & 0xF) * cap + (int)(w & 0xF);
       j += mb;
       k = (uint32_t)__shfl((int)kk, (j + lane) & 63);
       w = sort_lanes32<M>(lane < mb ? us : w);
+    }
+    if (nz < tn) {                                 // the rest has load 0
+      const int items = (int)(w & 0xF);
+      fill_zero_keys(lane < M && w < kSent32 ? cap - items : 0, (int)((w >> 4) & 0xF), items, t0 + nz, n, cap, res);
+      return;
     }
   }
 }
@@ -995,7 +1038,7 @@ struct Smem {
   int32_t* gres;   // [Gp]  packing result per visiting rank
   int32_t* rep;    // [Np][Rn]
   u64* pk;         // [nscr][pk_words]  per wave: lane-parallel packing scratch
-  int32_t* posaux; // [nscr][3 * En]  per wave: class start, item offset, position of expert
+  int32_t* posaux; // [nscr][3 * En]  per wave: class start (and class size), item offset, position of expert
   int32_t* ordr;   // [nscr][Pn]  per wave: item (local expert | rank << 16) in visiting order
   int32_t* ores;   // [nscr][Pn]  per wave: packing result per visiting rank
   int32_t* rcls;   // [nscr][Rn]  per wave: class of each replica
@@ -1249,7 +1292,7 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
   } else {
     int32_t* ordr = s.ordr + ws * Pn;
     int32_t* ores = s.ores + ws * Pn;
-    int32_t* cstart = s.posaux + ws * 3 * En;   // class start of each position
+    int32_t* cstart = s.posaux + ws * 3 * En;   // class start of each position (a start: | class size << 16)
     int32_t* coff = cstart + En;                 // item offset of each position
     int32_t* posof = coff + En;                  // position of each local expert
     int32_t* rcls = s.rcls + ws * (Rn > 0 ? Rn : 1);
@@ -1273,6 +1316,8 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
     // in visiting order: the originals (ascending local index, which is
     // ascending position), then the replicas of its experts in creation order.
     int carry_off = 0, carry_start = 0;
+    int stv[K];                                      // class start of each position
+    u64 tiem[K];                                     // positions that tie with the one before
 #pragma unroll
     for (int r = 0; r < K; ++r) {
       const int pos = r * 64 + lane;
@@ -1284,6 +1329,7 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
         if (lane == 0) { pu = lu; pc = lc; }
       }
       const bool tie = pos > 0 && pos < En && u[r] * (u64)(uint32_t)pc == pu * (u64)(uint32_t)c[r];
+      tiem[r] = ballot(tie);
       const int st = max(wave_incl_max((pos < En && !tie) ? pos : -1), carry_start);
       const int incl = wave_incl_sum(pos < En ? c[r] : 0) + carry_off;
       if (pos < En) {
@@ -1291,19 +1337,26 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
         coff[pos] = incl - c[r];
         posof[li[r]] = pos;
       }
+      stv[r] = st;
       carry_off = rdl(incl, 63);
       carry_start = rdl(st, 63);
+    }
+    // the last position of each class (the next one does not tie) puts the
+    // class size in the high half of its start's entry, after every start
+    // above is written; readers mask the low half
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      const u64 next_ties = (tiem[r] >> 1) | (r + 1 < K ? (tiem[r + 1 < K ? r + 1 : r] & 1ull) << 63 : 0ull);
+      if (pos < En && ((next_ties >> lane) & 1ull) == 0) cstart[stv[r]] = stv[r] | ((pos - stv[r] + 1) << 16);
     }
     wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < K; ++r) {              // originals
       const int pos = r * 64 + lane;
-      if (pos < En) {
-        const int st = cstart[pos];
-        ordr[coff[st] + (pos - st)] = li[r];
-      }
+      if (pos < En) ordr[coff[stv[r]] + (pos - stv[r])] = li[r];
     }
-    for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]];
+    for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]] & 0xffff;
     wave_lds_sync();
     for (int rr = lane; rr < Rn; rr += 64) {   // replicas
       const int cls = rcls[rr];
@@ -1317,9 +1370,7 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
         for (int k = 0; k < 8; ++k) before += a[k] == cls ? 1 : 0;
       }
       for (; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
-      int size = 1;
-      while (cls + size < En && cstart[cls + size] == cls) ++size;
-      ordr[coff[cls] + size + before] = rep[rr];   // local index | rank << 16
+      ordr[coff[cls] + (cstart[cls] >> 16) + before] = rep[rr];   // local index | rank << 16
     }
     wave_lds_sync();
     const u128* kexp = s.kexp + n * En;

@@ -345,6 +345,25 @@ def test_step3_word_widths(shape):
         rebalance_both((base * scale).clip(0, 1 << 40).astype(np.int64), P, G, N, RK)
 
 
+@pytest.mark.parametrize("shape", [
+    (8, 8, 8, 504, 3528),       # one expert per node, 441 copies of it (counts past 128: the general lcm)
+    (24, 24, 8, 432, 3456),     # three experts per node on 54 GPUs of 8 slots
+    (1152, 4, 4, 240, 1200),    # 288 experts per node on 60 GPUs (64,312 B of LDS, at the budget)
+])
+def test_shapes_at_the_lds_budget(shape):
+    """Shapes whose working set is just below the 64 KB LDS budget (17 to 64
+    GPUs per node need no packing scratch), with zero, equal, skewed and
+    large loads, against the oracle."""
+    E, G, N, RK, P = shape
+    rng = np.random.default_rng(E + P)
+    load = rng.integers(0, 1000, size=(4, E)).astype(np.int64)
+    load[0] = 0
+    load[1] = 5
+    load[2] = (rng.zipf(1.2, size=E) * 100).clip(0, 1 << 40)
+    load[3] = rng.integers((1 << 40) - 1000, (1 << 40) + 1, size=E)
+    rebalance_both(load, P, G, N, RK)
+
+
 def _fuzz_shapes(rng, count):
     """Valid placement shapes of every kind: hierarchical and global, 1 to 200
     GPUs per node (the sequential, register-run and LDS-run packing forms, one
