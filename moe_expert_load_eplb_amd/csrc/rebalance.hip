@@ -1229,6 +1229,35 @@ __device__ void node_replicate(const RbPlan& p, const Smem& s, int n) {
       if ((int)t.q[i] > cmax) break;
       if ((present & t.mult[i]) != 0) D *= t.p[i];   // lcm(1..64) < 2^93: no overflow
     }
+  } else if (cmax <= 128) {
+    // the counts up to 64 as above, then the lcm with each distinct count
+    // above 64 (at most Pn / 65 of them) by Euclid on c and D mod c
+    u64 present = 0, high = 0;
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      const int pos = r * 64 + lane;
+      const int c = ci[r] >> 16;
+      if (pos < En && c <= 64) present |= 1ull << (c - 1);
+      if (pos < En && c > 64) high |= 1ull << (c - 65);
+    }
+    present = wave_or64(present);
+    high = wave_or64(high);
+    constexpr SmallPrimePowers t = make_small_prime_powers();
+#pragma unroll
+    for (int i = 0; i < t.n; ++i)
+      if ((present & t.mult[i]) != 0) D *= t.p[i];
+    for (u64 m = high; m != 0; m &= m - 1) {
+      const uint32_t c = 65 + (uint32_t)__builtin_ctzll(m);
+      const int dg = (uint32_t)(D >> 96) != 0 ? 4 : (uint32_t)(D >> 64) != 0 ? 3 : (uint32_t)(D >> 32) != 0 ? 2 : 1;
+      uint32_t a = c;
+      uint32_t b = (uint32_t)(D - div_by_count(D, dg, c) * c);   // D mod c
+      while (b != 0) {
+        const uint32_t t2 = a % b;
+        a = b;
+        b = t2;
+      }
+      D = mul_u128_u64(D, c / a, ovf);
+    }
   } else {
     for (int t = 0; t < kPrimePowers.count && (int)kPrimePowers.q[t] <= cmax; ++t) {
       const uint32_t q = kPrimePowers.q[t];

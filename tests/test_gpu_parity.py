@@ -364,6 +364,18 @@ def test_shapes_at_the_lds_budget(shape):
     rebalance_both(load, P, G, N, RK)
 
 
+@pytest.mark.parametrize("shape,rows", [
+    ((3, 1, 1, 3, 300), [[5, 4, 3], [1, 1, 1], [0, 0, 0], [7, 0, 3], [9, 6, 2]]),
+    ((4, 1, 1, 4, 400), [[5, 4, 3, 2], [1, 1, 1, 1], [8, 0, 6, 3], [100, 99, 98, 97]]),
+])
+def test_counts_above_64(shape, rows):
+    """Replica counts between 65 and 128 (several distinct ones: the lcm of
+    the counts up to 64 by prime powers, then each larger count by Euclid)
+    and beyond 128 (the general prime-power table), against the oracle."""
+    E, G, N, RK, P = shape
+    rebalance_both(np.array(rows, dtype=np.int64), P, G, N, RK)
+
+
 def _fuzz_shapes(rng, count):
     """Valid placement shapes of every kind: hierarchical and global, 1 to 200
     GPUs per node (the sequential, register-run and LDS-run packing forms, one
