@@ -414,9 +414,10 @@ REF_SHAPES = {   # (threads, vectors in flight, workgroups per layer)
 
 
 def stream_ceilings(dev, stream, steps, out, L, W, reps=8):
-    """Best time of libeplb_ref.so's copy (non-temporal stores) and read-only
-    streams over one step's ids laid out as L layer rows, over REF_SHAPES,
-    cycling the same step buffers the kernels read."""
+    """Best time of libeplb_ref.so's copy (non-temporal loads; non-temporal or
+    sc1 nt buffer stores) and read-only streams over one step's ids laid out
+    as L layer rows, over REF_SHAPES, cycling the same step buffers the
+    kernels read."""
     import ctypes
     import torch
     ref = ctypes.CDLL(os.path.join(ROOT, "moe_expert_load_eplb_amd", "libeplb_ref.so"))
@@ -425,26 +426,31 @@ def stream_ceilings(dev, stream, steps, out, L, W, reps=8):
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     nbytes = steps[0].numel() * 4
     res = {}
-    for kind, mode, moved in (("copy", 1, 2 * nbytes), ("read", 0, nbytes)):
+    stores = {1: "non-temporal stores", 3: "sc1 nt buffer stores"}
+    for kind, modes, moved in (("copy", (1, 3), 2 * nbytes), ("read", (0,), nbytes)):
         best = None
-        for t, u, c in REF_SHAPES[kind]:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for i in range(reps):
-                evs[i][0].record(stream)
-                rc = ref.eplb_ref_stream(mode, steps[i % W].data_ptr(), (out if mode else sink).data_ptr(), nbytes, L,
-                                         t, u, c, stream.cuda_stream)
-                evs[i][1].record(stream)
-                assert rc == 0, f"reference stream failed ({rc})"
-            torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b) for a, b in evs[2:]) / (reps - 2)
-            if best is None or ms < best[0]:
-                best = (ms, t, u, c)
-        ms, t, u, c = best
+        for mode in modes:
+            for t, u, c in REF_SHAPES[kind]:
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                for i in range(reps):
+                    evs[i][0].record(stream)
+                    rc = ref.eplb_ref_stream(mode, steps[i % W].data_ptr(), (out if mode else sink).data_ptr(), nbytes,
+                                             L, t, u, c, stream.cuda_stream)
+                    evs[i][1].record(stream)
+                    assert rc == 0, f"reference stream failed ({rc})"
+                torch.cuda.synchronize()
+                ms = sum(a.elapsed_time(b) for a, b in evs[2:]) / (reps - 2)
+                if best is None or ms < best[0]:
+                    best = (ms, t, u, c, mode)
+        ms, t, u, c, mode = best
         res[kind] = {"GBps": round(moved / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
                      "shape": f"{L * c} workgroups x {t} threads x {u} vectors in flight",
                      "frac_of_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    res["what"] = ("best of a plain copy (non-temporal loads and stores) and of a read-only pass over one step's ids, "
-                   "laid out as the streaming kernels read them, over a few launch shapes")
+        if kind == "copy":
+            res[kind]["stores"] = stores[mode]
+    res["what"] = ("best of a plain copy (non-temporal loads; non-temporal or sc1 nt buffer stores) and of a "
+                   "read-only pass over one step's ids, laid out as the streaming kernels read them, over a few "
+                   "launch shapes")
     return res
 
 

@@ -229,6 +229,11 @@ inline LayerMapLds layer_map_plan(int E, int X, size_t budget) {
 // share one token row.  Ids before the first 16-byte boundary and after the
 // last are done by workgroup 0; a destination on another 16-byte phase than
 // the source goes id by id.
+// Raw (untyped) buffer descriptors for gfx950: word 3 of the resource, and
+// the cache-policy bits of a streaming store (sc1 = device scope, nt).
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kStoreSc1Nt = 16 | 2;
+
 template <int NT, int U, class Op>
 __device__ __forceinline__ void stream_map(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int64_t n,
                                            int64_t chunk, int64_t step, FastDiv kdiv, bool k4, Op op) {
@@ -251,7 +256,7 @@ __device__ __forceinline__ void stream_map(const int32_t* __restrict__ src, int3
   const i32x4* s4 = reinterpret_cast<const i32x4*>(src + head);
   i32x4* d4 = reinterpret_cast<i32x4*>(dst + head);
   const uint32_t fb = (uint32_t)head;            // position (within the layer) of s4[0]
-  auto sweep = [&](auto one_row) {
+  auto sweep = [&](auto one_row, auto store) {
     auto map4 = [&](const i32x4& x, int64_t v) {   // positions below 2^31: the vector exists
       const uint32_t f = fb + (uint32_t)(v << 2);
       i32x4 y;
@@ -278,12 +283,23 @@ __device__ __forceinline__ void stream_map(const int32_t* __restrict__ src, int3
 #pragma unroll
       for (int u = 0; u < U; ++u) y[u] = map4(x[u], v + u * step);
 #pragma unroll
-      for (int u = 0; u < U; ++u) __builtin_nontemporal_store(y[u], d4 + v + u * step);
+      for (int u = 0; u < U; ++u) store(y[u], v + u * step);
     }
-    for (; v < n4; v += step) __builtin_nontemporal_store(map4(__builtin_nontemporal_load(s4 + v), v), d4 + v);
+    for (; v < n4; v += step) store(map4(__builtin_nontemporal_load(s4 + v), v), v);
   };
-  if (k4 && head == 0) sweep(std::true_type{});
-  else sweep(std::false_type{});
+  auto run = [&](auto store) {
+    if (k4 && head == 0) sweep(std::true_type{}, store);
+    else sweep(std::false_type{}, store);
+  };
+  if (n4 < ((int64_t)1 << 27)) {
+    // below 2 GiB of vectors: buffer stores with the device-scope and
+    // non-temporal bits (sc1 nt), which stream to HBM a few per cent faster
+    // than plain non-temporal stores; the descriptor spans the layer's vectors
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(d4, 0, (int)(n4 * 16), kRawBufferWord3);
+    run([&](const i32x4& y, int64_t v) { __builtin_amdgcn_raw_buffer_store_b128(y, rd, (int)(v * 16), 0, kStoreSc1Nt); });
+  } else {
+    run([&](const i32x4& y, int64_t v) { __builtin_nontemporal_store(y, d4 + v); });
+  }
 }
 
 // One routing id into a workgroup's LDS counters: column e, or column E (the

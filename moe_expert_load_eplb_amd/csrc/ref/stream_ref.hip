@@ -7,7 +7,8 @@
 // The bytes are `layers` equal rows.  Workgroup b takes row b / chunks and,
 // as the streaming kernels of the library do, the row's 16-byte vectors
 // (b % chunks) * NT + tid + k * chunks * NT, U of them in flight per
-// iteration, with non-temporal loads; stores are non-temporal or plain.
+// iteration, with non-temporal loads; stores are non-temporal, plain, or
+// buffer stores with the sc1 nt cache bits (as the library's redirect).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,13 +16,22 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-template <int NT, int U, bool kNtStore>
+// kStore: 0 plain, 1 non-temporal, 2 buffer store with the device-scope and
+// non-temporal bits (sc1 nt; rows below 2 GiB), the store the library's
+// streaming kernels use
+template <int NT, int U, int kStore>
 __global__ __launch_bounds__(NT) void ref_copy_kernel(const i32x4* __restrict__ src, i32x4* __restrict__ dst,
                                                       int64_t n4l, int32_t chunks) {
   const int64_t row = blockIdx.x / chunks;
   const int64_t chunk = blockIdx.x - row * chunks;
   const i32x4* s = src + row * n4l;
   i32x4* d = dst + row * n4l;
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(d, 0, (int)(kStore == 2 ? n4l * 16 : 0), 0x00020000);
+  auto store = [&](const i32x4& x, int64_t v) {
+    if constexpr (kStore == 2) __builtin_amdgcn_raw_buffer_store_b128(x, rd, (int)(v * 16), 0, 16 | 2);
+    else if constexpr (kStore == 1) __builtin_nontemporal_store(x, d + v);
+    else d[v] = x;
+  };
   const int64_t step = (int64_t)chunks * NT;
   int64_t v = chunk * NT + threadIdx.x;
   for (; v + (U - 1) * step < n4l; v += U * step) {
@@ -29,16 +39,9 @@ __global__ __launch_bounds__(NT) void ref_copy_kernel(const i32x4* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(s + v + u * step);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (kNtStore) __builtin_nontemporal_store(x[u], d + v + u * step);
-      else d[v + u * step] = x[u];
-    }
+    for (int u = 0; u < U; ++u) store(x[u], v + u * step);
   }
-  for (; v < n4l; v += step) {
-    const i32x4 x = __builtin_nontemporal_load(s + v);
-    if constexpr (kNtStore) __builtin_nontemporal_store(x, d + v);
-    else d[v] = x;
-  }
+  for (; v < n4l; v += step) store(__builtin_nontemporal_load(s + v), v);
 }
 
 // Reads every vector and folds it into one word per thread; a thread writes
@@ -73,9 +76,11 @@ hipError_t launch(int mode, const void* src, void* dst, int64_t n4l, int32_t chu
   if (mode == 0)
     ref_read_kernel<NT, U><<<blocks, NT, 0, s>>>((const i32x4*)src, n4l, chunks, (int32_t*)dst);
   else if (mode == 1)
-    ref_copy_kernel<NT, U, true><<<blocks, NT, 0, s>>>((const i32x4*)src, (i32x4*)dst, n4l, chunks);
+    ref_copy_kernel<NT, U, 1><<<blocks, NT, 0, s>>>((const i32x4*)src, (i32x4*)dst, n4l, chunks);
+  else if (mode == 2)
+    ref_copy_kernel<NT, U, 0><<<blocks, NT, 0, s>>>((const i32x4*)src, (i32x4*)dst, n4l, chunks);
   else
-    ref_copy_kernel<NT, U, false><<<blocks, NT, 0, s>>>((const i32x4*)src, (i32x4*)dst, n4l, chunks);
+    ref_copy_kernel<NT, U, 2><<<blocks, NT, 0, s>>>((const i32x4*)src, (i32x4*)dst, n4l, chunks);
   return hipGetLastError();
 }
 
@@ -84,7 +89,8 @@ hipError_t launch(int mode, const void* src, void* dst, int64_t n4l, int32_t chu
 extern "C" {
 
 // mode 0: read src (dst, 4 bytes, is left as it is); 1: copy src to dst with
-// non-temporal stores; 2: copy with plain stores.  The bytes are `layers`
+// non-temporal stores; 2: copy with plain stores; 3: copy with sc1 nt buffer
+// stores (rows below 2 GiB).  The bytes are `layers`
 // rows of bytes / layers each (a multiple of 16), 16-byte aligned; `chunks`
 // workgroups per row of `threads` threads, `unroll` vectors in flight each.
 // threads in {256, 512, 1024}, unroll in {1, 2, 4, 8}, layers * chunks
@@ -92,8 +98,9 @@ extern "C" {
 // argument, 2 for a launch error.
 int32_t eplb_ref_stream(int32_t mode, const void* src, void* dst, int64_t bytes, int64_t layers, int32_t threads,
                         int32_t unroll, int32_t chunks, void* stream) {
-  if (src == nullptr || dst == nullptr || bytes < 0 || layers < 1 || chunks < 1 || mode < 0 || mode > 2) return 1;
+  if (src == nullptr || dst == nullptr || bytes < 0 || layers < 1 || chunks < 1 || mode < 0 || mode > 3) return 1;
   if (bytes % (16 * layers) != 0 || layers * chunks > (1 << 20)) return 1;
+  if (mode == 3 && bytes / layers >= ((int64_t)1 << 31)) return 1;
   if (((uintptr_t)src | (uintptr_t)dst) & 15) return 1;
   const int64_t n4l = bytes / 16 / layers;
   const unsigned blocks = (unsigned)(layers * chunks);
