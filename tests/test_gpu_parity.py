@@ -229,6 +229,47 @@ def test_stream_1m_full_size():
                     ora.redirect(idx_h[l:l + 1], ref["log2phy"][l:l + 1], ref["logcnt"][l:l + 1]))
 
 
+def test_layer_beyond_2gib():
+    """One layer of 2^29 + 24 ids (just over 2 GiB): the redirect and the
+    fused pass store through global stores instead of the buffer stores of
+    smaller layers.  Every id is checked by the redirect's definition and the
+    counts against a bincount; a slice of tokens element by element against
+    the oracle."""
+    pl = wl.DSV3_PREFILL.placement
+    E, T, K = pl.E, (1 << 26) + 3, 8
+    load = wl.zipf_loads(1, E, 1.1, 1 << 20)
+    (phy2log, log2phy, logcnt, status), ref = rebalance_both(load, pl.P, pl.G, pl.N, pl.RK)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2026)
+    note("layer beyond 2 GiB: generate")
+    idx = torch.randint(0, E, (1, T, K), dtype=torch.int32, device=DEV, generator=g)
+    l2p, cnt = gpu(log2phy), gpu(logcnt)
+    note("layer beyond 2 GiB: redirect")
+    out = eplb.redirect(idx, l2p, cnt)
+    W = 2
+    ring = torch.zeros((W, 1, E), dtype=torch.int32, device=DEV)
+    note("layer beyond 2 GiB: hist_redirect")
+    wload, bad, fused = eplb.hist_redirect(idx, E, ring, 0, l2p, cnt)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(out, fused)), "fused pass and redirect differ"
+    e = idx[0].long()
+    t = torch.arange(T, device=DEV).unsqueeze(1)
+    want = l2p[0].long()[e, t % cnt[0].long()[e]]
+    assert bool((out[0].long() == want).all()), "a redirected id is not log2phy[e][t mod logcnt[e]]"
+    del e, want
+    counts = torch.bincount(idx.view(-1).long(), minlength=E)
+    assert bool(torch.equal(ring[0, 0].long(), counts)) and bool(torch.equal(wload[0], counts))
+    assert int(bad.sum()) == 0
+    # the last 5000 tokens against the oracle: their rows start at T0, so
+    # T0 mod lcm(counts) rows of padding in front give every count the same
+    # row residues
+    T0 = T - 5000
+    pad = T0 % int(np.lcm.reduce(ref["logcnt"][0].astype(np.int64)))
+    idx_h = np.concatenate([np.zeros((1, pad, K), np.int32), host(idx[:, T0:])], axis=1)
+    want_h = ora.redirect(idx_h, ref["log2phy"], ref["logcnt"])[:, pad:]
+    assert_same("last 5000 tokens", host(out[:, T0:]), want_h)
+
+
 # ---------------------------------------------------------------- edge cases
 
 def test_decode_144_global():
