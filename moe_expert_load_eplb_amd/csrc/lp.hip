@@ -576,10 +576,12 @@ __global__ __launch_bounds__(kLpDkThreads) void lp_solve_dk_kernel(
 // wave each: (A) count every segment's ids per compact number into the
 // workspace, (B) turn the counts into exclusive prefixes over the segments,
 // (C) each wave starts its counters at those prefixes and walks its segment
-// 64 ids at a time; a group of 64 with no replicated id is copied through,
-// otherwise equal numbers are ranked among the lanes with one ballot per bit
-// of the number (peers share every bit), so the numbering matches a
-// sequential pass exactly.
+// 64 ids at a time.  An expert whose occurrences in the segment lie wholly
+// below its flow (the next segment's prefix is at most the flow) or wholly
+// at or above it is mapped by one table read; only the one segment where
+// the flow runs out ranks that expert's ids: equal numbers among the lanes
+// with one ballot per bit of the number (peers share every bit), so the
+// numbering matches a sequential pass exactly.
 
 __host__ __device__ inline int lp_waves_per_block(int words_per_wave) {
   const int w = (kMaxLdsBytes / 4) / words_per_wave;
@@ -701,7 +703,28 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
   }
   const int32_t* base = seg + q * C;
   for (int c = lane; c < C; c += 64) run[c] = base[c];
-  const bool bad = lp_build_map(rep + l * RKR, flow + l * RKR, RKR, E, C, cmap, pid, fx);
+  const int32_t* rl = rep + l * RKR;
+  const bool bad = lp_build_map(rl, flow + l * RKR, RKR, E, C, cmap, pid, fx);
+  // A replicated expert's ids in this segment all go to its replica when
+  // the segment ends at or before its flow, all stay when it starts at or
+  // beyond it; only in the segment where the flow runs out are they decided
+  // one by one.  cmap[e] becomes -1 (stay), -2 - pid (all to the replica),
+  // or the compact number (one by one).  The next segment's prefix ends this
+  // one's occurrences; the layer's last segment counts as undecided.
+  const bool has_next = s + 1 < S;
+  for (int i0 = 0; i0 < RKR && !bad; i0 += 64) {
+    const int i = i0 + lane;
+    const int32_t x = i < RKR ? rl[i] : -1;
+    if ((uint32_t)x < (uint32_t)E) {
+      const int c = cmap[x];
+      if (c >= 0 && pid[c] == E + i) {                 // the slot that holds x's compact number
+        const int32_t f = fx[c];
+        if (run[c] >= f) cmap[x] = -1;
+        else if (has_next && base[C + c] <= f) cmap[x] = -2 - (E + i);
+      }
+    }
+  }
+  lp_wave_sync();
   const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
   for (int k = 0; k < kLpSeg / 64; ++k) {
@@ -709,8 +732,9 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
     if (k * 64 >= len) break;                          // uniform
     const int32_t e = v[k];
     const bool inr = i < len && (uint32_t)e < (uint32_t)E && !bad;
-    const int c = inr ? cmap[e] : -1;
-    int32_t res = inr ? e : -1;
+    const int32_t mp = inr ? cmap[e] : -1;
+    const int c = mp >= 0 ? mp : -1;
+    int32_t res = inr ? (mp <= -2 ? -2 - mp : e) : -1;
     const uint64_t has = __builtin_amdgcn_ballot_w64(c >= 0);
     if (has != 0) {                                    // uniform
       uint64_t peers = has;
