@@ -1385,21 +1385,36 @@ __device__ void node_place(const RbPlan& p, const Smem& s, int n, int ws,
       const int pos = r * 64 + lane;
       if (pos < En) ordr[coff[stv[r]] + (pos - stv[r])] = li[r];
     }
-    for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]] & 0xffff;
-    wave_lds_sync();
-    for (int rr = lane; rr < Rn; rr += 64) {   // replicas
-      const int cls = rcls[rr];
-      int before = 0;                           // earlier replicas of the same class
-      int r2 = 0;
-      for (; r2 + 8 <= rr; r2 += 8) {
+    // Replicas: the rank of a replica among the earlier replicas of its class
+    // is the count of equal class numbers before it.  Inside a chunk of 64
+    // that count comes from ballots over the class number's bits (the lanes
+    // that agree on every bit); earlier chunks, when a node has more than 64
+    // replicas, are counted from their class numbers in LDS.
+    const int cbits = En > 1 ? 32 - __builtin_clz((unsigned)(En - 1)) : 0;
+    if (Rn > 64) {
+      for (int rr = lane; rr < Rn; rr += 64) rcls[rr] = cstart[posof[rep[rr] & 0xffff]] & 0xffff;
+      wave_lds_sync();
+    }
+    for (int base = 0; base < Rn; base += 64) {
+      const int rr = base + lane;
+      const bool act = rr < Rn;
+      const int v = act ? rep[rr] : 0;
+      const int cls = act ? cstart[posof[v & 0xffff]] & 0xffff : 0;
+      u64 same = ballot(act);
+      for (int b = 0; b < cbits; ++b) {
+        const bool bit = (cls >> b) & 1;
+        const u64 mb = ballot(bit);
+        same &= bit ? mb : ~mb;
+      }
+      int before = __popcll(same & ((1ull << lane) - 1));
+      for (int r2 = 0; r2 < base; r2 += 8) {
         int a[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) a[k] = rcls[r2 + k];
 #pragma unroll
         for (int k = 0; k < 8; ++k) before += a[k] == cls ? 1 : 0;
       }
-      for (; r2 < rr; ++r2) before += rcls[r2] == cls ? 1 : 0;
-      ordr[coff[cls] + (cstart[cls] >> 16) + before] = rep[rr];   // local index | rank << 16
+      if (act) ordr[coff[cls] + (cstart[cls] >> 16) + before] = v;   // local index | rank << 16
     }
     wave_lds_sync();
     const u128* kexp = s.kexp + n * En;
