@@ -600,41 +600,83 @@ __device__ __forceinline__ u64 sort_lanes(u64 x) {
   return x;
 }
 
+// One run of pack_words_few: lane s (s < M) offers item j + s (key k) to the
+// s-th lightest pack; the run is the longest prefix of lanes, all below nz,
+// for which that pack is lighter than every pack the run already updated.
+// Places the run's items and returns their number; us: the updated words.
+template <int M>
+__device__ __forceinline__ int pack_run(u64 w, u64 k, int j, int nz, int cap, int32_t* res, u64& us) {
+  constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
+  const int lane = lane_id();
+  const bool real = w < kSent;
+  us = w + k;
+  if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
+  u64 pmin = us;                                 // prefix minimum of us within the first M lanes
+  if constexpr (M <= 16) {
+    pmin = min(pmin, dpp64<0x111>(~0ull, pmin));
+    pmin = min(pmin, dpp64<0x112>(~0ull, pmin));
+    pmin = min(pmin, dpp64<0x114>(~0ull, pmin));
+    if constexpr (M == 16) pmin = min(pmin, dpp64<0x118>(~0ull, pmin));
+  } else {
+    pmin = wave_scan_incl<u64>(pmin, ~0ull, [](u64 a, u64 b) { return a < b ? a : b; });
+  }
+  const u64 before = shr1_or64(~0ull, pmin);    // over the lanes before this one
+  const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < nz && real && w < before);
+  const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);   // lane 0 is always valid; all 64 only when m = 64
+  if (lane < mb) res[j + lane] = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
+  return mb;
+}
+
 template <int M, class KeyOf>
 __device__ void pack_words_few(KeyOf key_of, int n, int m, int cap, int32_t* res) {
   constexpr u64 kSent = 0xFFFFFFFFFFFF0000ull;
   const int lane = lane_id();
   u64 w = lane < m ? ((u64)lane << 8) : (kSent | ((u64)lane << 8) | 0xffull);
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    const int tn = n - t0 < 64 ? n - t0 : 64;
-    const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
-    const int nz = __popcll(__builtin_amdgcn_ballot_w64(lane < tn && kk != 1ull));   // items of load > 0 first
-    u64 k = kk;                                    // lane s: key of item j + s
+  if constexpr (M >= 32) {
+    // Runs may start at any item: after each run the lanes read the keys of
+    // the next 64 items (the read hides behind the network of 32 or 64
+    // lanes).  The items of load 0 (key 1) come last; nz is the first of them
+    // among the keys seen so far (successive views cover every item).
+    u64 k = lane < n ? key_of(lane) : 1ull;
+    int nz = n;
+    {
+      const u64 zm = __builtin_amdgcn_ballot_w64(lane < n && k == 1ull);
+      if (zm != 0) nz = __builtin_ctzll(zm);
+    }
     for (int j = 0; j < nz; ) {
-      const bool real = w < kSent;
-      u64 us = w + k;
-      if ((int)(us & 0xff) == cap) us = kSent | (us & 0xff00ull) | 0xffull;
-      u64 pmin = us;                               // prefix minimum of us within the first M lanes
-      if constexpr (M <= 16) {
-        pmin = min(pmin, dpp64<0x111>(~0ull, pmin));
-        pmin = min(pmin, dpp64<0x112>(~0ull, pmin));
-        pmin = min(pmin, dpp64<0x114>(~0ull, pmin));
-        if constexpr (M == 16) pmin = min(pmin, dpp64<0x118>(~0ull, pmin));
-      } else {
-        pmin = wave_scan_incl<u64>(pmin, ~0ull, [](u64 a, u64 b) { return a < b ? a : b; });
-      }
-      const u64 before = shr1_or64(~0ull, pmin);  // over the lanes before this one
-      const u64 vm = __builtin_amdgcn_ballot_w64(lane < M && j + lane < nz && real && w < before);
-      const int mb = ~vm == 0 ? 64 : __builtin_ctzll(~vm);   // lane 0 is always valid; all 64 only when m = 64
-      if (lane < mb) res[t0 + j + lane] = (int)((w >> 8) & 0xff) * cap + (int)(w & 0xff);
+      u64 us;
+      const int mb = pack_run<M>(w, k, j, nz, cap, res, us);
       j += mb;
-      k = shfl64(kk, (j + lane) & 63);
+      k = j + lane < n ? key_of(j + lane) : 1ull;
+      const u64 zm = __builtin_amdgcn_ballot_w64(j + lane < n && k == 1ull);
+      if (zm != 0) nz = min(nz, j + (int)__builtin_ctzll(zm));
       w = sort_lanes<M>(lane < mb ? us : w);
     }
-    if (nz < tn) {                                 // the rest has load 0
+    if (nz < n) {                                // the rest has load 0
       const int items = (int)(w & 0xff);
-      fill_zero_keys(lane < M && w < kSent ? cap - items : 0, (int)((w >> 8) & 0xff), items, t0 + nz, n, cap, res);
-      return;
+      fill_zero_keys(lane < M && w < kSent ? cap - items : 0, (int)((w >> 8) & 0xff), items, nz, n, cap, res);
+    }
+  } else {
+    // Short networks: the keys of 64 items at a time sit in registers and a
+    // run's keys come from them by a lane shuffle (runs end at the chunk).
+    for (int t0 = 0; t0 < n; t0 += 64) {
+      const int tn = n - t0 < 64 ? n - t0 : 64;
+      const u64 kk = lane < tn ? key_of(t0 + lane) : 0ull;
+      const int nz = __popcll(__builtin_amdgcn_ballot_w64(lane < tn && kk != 1ull));   // items of load > 0 first
+      u64 k = kk;                                // lane s: key of item j + s
+      for (int j = 0; j < nz; ) {
+        u64 us;
+        const int mb = pack_run<M>(w, k, j, nz, cap, res + t0, us);
+        j += mb;
+        k = shfl64(kk, (j + lane) & 63);
+        w = sort_lanes<M>(lane < mb ? us : w);
+      }
+      if (nz < tn) {                             // the rest has load 0
+        const int items = (int)(w & 0xff);
+        fill_zero_keys(lane < M && w < kSent ? cap - items : 0, (int)((w >> 8) & 0xff), items, t0 + nz, n, cap,
+                       res);
+        return;
+      }
     }
   }
 }
