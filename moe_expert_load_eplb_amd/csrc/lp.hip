@@ -29,8 +29,11 @@
 //      which fixes one definite flow among the optimal ones;
 //   4. the net flow of each rank pair is split over the pair's replica slots
 //      in ascending slot order.
-// Integer work throughout; RK <= 16 (the 8-GPU cube and 16-GPU hypercube
-// topologies of the pages), so every structure fits in LDS.
+// Integer work throughout.  Steps 1-4 as written serve up to 16 ranks (the
+// pages' 8-GPU cube and 16-GPU hypercube), where every structure fits in
+// LDS; 17 to 64 ranks (a torus over several nodes) take the cut iteration
+// of lp_solve_dk_kernel below, which reaches the same optimum and flow
+// without enumerating rank sets.
 #include <climits>
 
 #include "eplb_internal.h"
