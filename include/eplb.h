@@ -29,9 +29,9 @@
  *     output buffers do not overlap.
  *   - A non-zero return code means nothing was enqueued (EPLB_E_HIP: a launch
  *     failed and earlier kernels of the same call may have run).
- *   - Outputs must not share a byte with the inputs or with each other where
- *     a call says so; the check compares address ranges and returns
- *     EPLB_E_ARG.
+ *   - No output (in/out buffers such as `ring` and `ema` included) may share
+ *     a byte with an input or with another output of the same call; the
+ *     check compares address ranges and returns EPLB_E_ARG.
  *   - One call takes at most 2^22 layers (streaming calls) or 2^22 problems
  *     (rebalance-like calls), else EPLB_E_LIMIT, so that each launch stays
  *     below 2^32 work-items.
@@ -89,6 +89,11 @@ extern "C" {
  *   load       [L][E] int64      out: sum over all W slots of `ring`
  *   n_invalid  [L] int64         out: ids of layer l outside [0, E); they are
  *                                not counted
+ *
+ * Errors: EPLB_E_ARG (L or T < 0, K, E or W < 1, step < 0, a NULL array, or
+ * ring, load or n_invalid sharing a byte with idx or with each other),
+ * EPLB_E_LIMIT (E > 4096, L > 2^22), EPLB_E_RANGE (T * K >= 2^31),
+ * EPLB_E_HIP.
  */
 int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                        int32_t* ring, int32_t W, int64_t step,
@@ -149,7 +154,7 @@ int32_t eplb_rebalance(const int64_t* load, int64_t B, int32_t E, int32_t P,
  *   log2phy    [L][E][X] int32   from eplb_rebalance
  *   logcnt     [L][E] int32      from eplb_rebalance
  *   out        [L][T][K] int32   out: physical ids; must not share a byte
- *                                with idx
+ *                                with idx, log2phy or logcnt
  */
 int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                       const int32_t* log2phy, const int32_t* logcnt, int32_t X,
@@ -164,7 +169,8 @@ int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
  * typically the one computed from the window before this step.  Every output
  * is identical to calling eplb_load_hist then eplb_redirect with the same
  * arguments; each id is read once instead of twice.  Arguments, layouts,
- * errors: as for those two calls (out must not overlap idx).
+ * errors: as for those two calls (no output, ring included, may share a byte
+ * with idx, log2phy, logcnt or another output).
  */
 int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E,
                            int32_t* ring, int32_t W, int64_t step, int64_t* load, int64_t* n_invalid,
@@ -204,7 +210,8 @@ int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
  * (log2phy, logcnt) given.  Every output is identical to calling
  * eplb_load_ema then eplb_redirect with the same arguments; each id is read
  * once instead of twice.  Arguments, layouts, errors: as for those two calls
- * (out must not overlap idx).
+ * (no output, ema included, may share a byte with idx, log2phy, logcnt or
+ * another output).
  */
 int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, int32_t* count,
                           int32_t shift, int64_t* ema, int64_t* n_invalid, const int32_t* log2phy,
@@ -358,11 +365,12 @@ int32_t eplb_lp_solve(const int64_t* cnt, const int32_t* home, const int32_t* re
  *                                bytes (per-segment counts; contents on entry
  *                                do not matter and are overwritten)
  *   workspace_bytes              its size
- *   out        [L][T][K] int32   out: physical ids; must not overlap idx
+ *   out        [L][T][K] int32   out: physical ids; must not share a byte
+ *                                with idx, rep or flow
  *
  * Errors: as for eplb_redirect; EPLB_E_ARG also for RK or R < 1, a NULL
  * array or workspace, a workspace below the size needed, or a workspace
- * sharing a byte with idx or out; EPLB_E_LIMIT for RK > 64, R > 64, or more
+ * sharing a byte with idx, rep, flow or out; EPLB_E_LIMIT for RK > 64, R > 64, or more
  * than 2^25 segments of 2048 ids over all layers.
  */
 int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32_t E, const int32_t* rep,

@@ -17,11 +17,21 @@ int32_t check_stream_args(const void* idx, int64_t L, int64_t T, int32_t K, int3
   return EPLB_OK;
 }
 
-// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte (ends
+// taken in 128 bits, so a range reaching past the address space still
+// compares correctly).
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+  const unsigned __int128 x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (unsigned __int128)nb && y < x + (unsigned __int128)na;
+}
+
+// a * b * c bytes, saturated at 2^63 - 1 (a caller's window of W steps is
+// not bounded above, so its byte count may not fit).
+int64_t bytes_of(int64_t a, int64_t b, int64_t c) {
+  int64_t ab = 0, abc = 0;
+  if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc)) return INT64_MAX;
+  return abc;
 }
 
 // A call with B problems and these input and output ranges: every pointer
@@ -30,18 +40,26 @@ struct Range {
   const void* p;
   int64_t bytes;
 };
+// No output shares a byte with an input or another output (empty ranges and
+// NULL pointers share nothing; the calls check NULLs themselves).
 template <int NI, int NO>
-int32_t check_buffers(const Range (&in)[NI], const Range (&out)[NO]) {
-  for (const Range& a : in)
-    if (a.p == nullptr) return EPLB_E_ARG;
+int32_t check_disjoint(const Range (&in)[NI], const Range (&out)[NO]) {
   for (int i = 0; i < NO; ++i) {
-    if (out[i].p == nullptr) return EPLB_E_ARG;
     for (const Range& c : in)
       if (overlap(out[i].p, out[i].bytes, c.p, c.bytes)) return EPLB_E_ARG;
     for (int j = 0; j < i; ++j)
       if (overlap(out[i].p, out[i].bytes, out[j].p, out[j].bytes)) return EPLB_E_ARG;
   }
   return EPLB_OK;
+}
+
+template <int NI, int NO>
+int32_t check_buffers(const Range (&in)[NI], const Range (&out)[NO]) {
+  for (const Range& a : in)
+    if (a.p == nullptr) return EPLB_E_ARG;
+  for (const Range& a : out)
+    if (a.p == nullptr) return EPLB_E_ARG;
+  return check_disjoint(in, out);
 }
 
 }  // namespace
@@ -58,7 +76,10 @@ int32_t check_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, i
   if (L * lp_segments(n) > kLpMaxSegments) return EPLB_E_LIMIT;
   if (L > 0 && n > 0) {
     if (rep == nullptr || flow == nullptr || out == nullptr) return EPLB_E_ARG;
-    if (overlap(out, L * n * 4, idx, L * n * 4)) return EPLB_E_ARG;
+    const int64_t slots = L * RK * (int64_t)R;
+    const Range in[3] = {{idx, L * n * 4}, {rep, slots * 4}, {flow, slots * 8}};
+    const Range outs[1] = {{out, L * n * 4}};
+    return check_disjoint(in, outs);
   }
   return EPLB_OK;
 }
@@ -74,6 +95,12 @@ int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
   if (rc != EPLB_OK) return rc;
   if (W < 1 || step < 0) return EPLB_E_ARG;
   if (L > 0 && (ring == nullptr || load == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
+  {
+    const Range in[1] = {{idx, L * T * K * 4}};
+    const Range out[3] = {{ring, bytes_of(W, L * E, 4)}, {load, L * E * 8}, {n_invalid, L * 8}};
+    rc = check_disjoint(in, out);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_hist(idx, L, T, K, E, ring, W, step, load, n_invalid, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
@@ -106,7 +133,12 @@ int32_t eplb_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
   if (X < 1) return EPLB_E_ARG;
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
+  if (T > 0) {
+    const Range in[3] = {{idx, L * T * K * 4}, {log2phy, L * E * (int64_t)X * 4}, {logcnt, L * E * 4}};
+    const Range outs[1] = {{out, L * T * K * 4}};
+    rc = check_disjoint(in, outs);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_redirect(idx, L, T, K, E, log2phy, logcnt, X, out, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
@@ -121,7 +153,14 @@ int32_t eplb_hist_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, 
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && (ring == nullptr || load == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
+  {
+    const int64_t tab = T > 0 ? L * E : 0;             // the tables are read only when there are ids
+    const Range in[3] = {{idx, L * T * K * 4}, {log2phy, tab * X * 4}, {logcnt, tab * 4}};
+    const Range outs[4] = {{ring, bytes_of(W, L * E, 4)}, {load, L * E * 8}, {n_invalid, L * 8},
+                           {out, L * T * K * 4}};
+    rc = check_disjoint(in, outs);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_hist_redirect(idx, L, T, K, E, ring, W, step, load, n_invalid, log2phy, logcnt, X,
                                         out, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -133,6 +172,12 @@ int32_t eplb_load_ema(const int32_t* idx, int64_t L, int64_t T, int32_t K, int32
   if (rc != EPLB_OK) return rc;
   if (shift < 0 || shift > 62) return EPLB_E_ARG;
   if (L > 0 && (count == nullptr || ema == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
+  {
+    const Range in[1] = {{idx, L * T * K * 4}};
+    const Range out[3] = {{count, L * E * 4}, {ema, L * E * 8}, {n_invalid, L * 8}};
+    rc = check_disjoint(in, out);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_load_ema(idx, L, T, K, E, count, shift, ema, n_invalid, (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
 }
@@ -146,7 +191,13 @@ int32_t eplb_ema_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, i
   if (X > kMaxX) return EPLB_E_LIMIT;
   if (L > 0 && (count == nullptr || ema == nullptr || n_invalid == nullptr)) return EPLB_E_ARG;
   if (L > 0 && T > 0 && (log2phy == nullptr || logcnt == nullptr || out == nullptr)) return EPLB_E_ARG;
-  if (overlap(out, L * T * K * 4, idx, L * T * K * 4)) return EPLB_E_ARG;
+  {
+    const int64_t tab = T > 0 ? L * E : 0;
+    const Range in[3] = {{idx, L * T * K * 4}, {log2phy, tab * X * 4}, {logcnt, tab * 4}};
+    const Range outs[4] = {{count, L * E * 4}, {ema, L * E * 8}, {n_invalid, L * 8}, {out, L * T * K * 4}};
+    rc = check_disjoint(in, outs);
+    if (rc != EPLB_OK) return rc;
+  }
   hipError_t err = launch_ema_redirect(idx, L, T, K, E, count, shift, ema, n_invalid, log2phy, logcnt, X, out,
                                        (hipStream_t)stream);
   return err == hipSuccess ? EPLB_OK : EPLB_E_HIP;
@@ -220,7 +271,11 @@ int32_t eplb_lp_redirect(const int32_t* idx, int64_t L, int64_t T, int32_t K, in
     if (workspace == nullptr) return EPLB_E_ARG;
     const int64_t need = eplb_lp_redirect_workspace_bytes(L, T, K, E);
     if (workspace_bytes < need) return EPLB_E_ARG;
-    if (overlap(workspace, need, idx, L * n * 4) || overlap(workspace, need, out, L * n * 4)) return EPLB_E_ARG;
+    const int64_t slots = L * RK * (int64_t)R;
+    const Range in[3] = {{idx, L * n * 4}, {rep, slots * 4}, {flow, slots * 8}};
+    const Range outs[2] = {{out, L * n * 4}, {workspace, need}};
+    rc = check_disjoint(in, outs);
+    if (rc != EPLB_OK) return rc;
   }
   hipError_t err = launch_lp_redirect(idx, L, n, E, rep, flow, RK, R, static_cast<int32_t*>(workspace), out,
                                       (hipStream_t)stream);

@@ -331,9 +331,29 @@ def test_overlapping_buffers_rejected(lib):
     assert lib.eplb_rebalance(F[0], 2, 16, 24, 4, 2, 8, 5, F[1], F[2], F[3], F[2] + 8, None) == 1
     # lp_solve: flow overlapping rep
     assert lib.eplb_lp_solve(F[0], F[1], F[2], 2, 16, 8, 2, F[3], F[2] + 4, F[5], F[6], None) == 1
-    # lp_redirect: workspace inside out
+    # lp_redirect: workspace inside out; out over flow
     need = lib.eplb_lp_redirect_workspace_bytes(2, 5000, 2, 64)
     assert lib.eplb_lp_redirect(F[0], 2, 5000, 2, 64, F[1], F[2], 8, 2, F[4] + 16, need, F[4], None) == 1
+    assert lib.eplb_lp_redirect(F[0], 2, 5000, 2, 64, F[1], F[2], 8, 2, F[3], need, F[2] + 8, None) == 1
+    # streaming calls: in/out buffers (ring, ema), loads, counters and tables
+    L, T, K, E, W, X = 2, 10, 8, 256, 4, 9
+    ring_b, load_b = W * L * E * 4, L * E * 8
+    assert lib.eplb_load_hist(F[0], L, T, K, E, F[1], W, 0, F[1] + ring_b - 8, F[3], None) == 1   # load in ring
+    assert lib.eplb_load_hist(F[0], L, T, K, E, F[1], W, 0, F[2], F[2] + load_b - 8, None) == 1  # n_invalid in load
+    assert lib.eplb_load_hist(F[0], L, T, K, E, F[0] + 4, W, 0, F[2], F[3], None) == 1          # ring over idx
+    # a ring whose byte count (2^31 - 1 steps x 2^22 layers x 4096 experts x 4 B)
+    # does not fit in 63 bits still holds the load placed 2^60 bytes into it
+    assert lib.eplb_load_hist(FAKE << 4, 1 << 22, 1, 1, 4096, 1 << 44, (1 << 31) - 1, 0, (1 << 44) + (1 << 60),
+                              1 << 36, None) == 1
+    assert lib.eplb_redirect(F[0], L, T, K, E, F[1], F[2], X, F[1] + L * E * X * 4 - 4, None) == 1  # out over log2phy
+    assert lib.eplb_redirect(F[0], L, T, K, E, F[1], F[2], X, F[2] - 4, None) == 1                # out over logcnt
+    good = [F[0], L, T, K, E, F[1], W, 0, F[2], F[3], F[4], F[5], X, F[6], None]
+    for pos, bad in [(8, F[1] + 8), (9, F[2]), (13, F[4]), (13, F[5] + 4), (5, F[6]), (9, F[0])]:
+        args = list(good)
+        args[pos] = bad
+        assert lib.eplb_hist_redirect(*args) == 1, (pos, bad)
+    assert lib.eplb_load_ema(F[0], L, T, K, E, F[1], 4, F[1] + 16, F[3], None) == 1                # ema over count
+    assert lib.eplb_ema_redirect(F[0], L, T, K, E, F[1], 4, F[2], F[3], F[4], F[5], X, F[2] + 8, None) == 1
 
 
 def test_lp_redirect_noalloc_validation(lib):
