@@ -82,6 +82,60 @@ def test_lp_solve_random(RK, R, E, top):
     check_solution(cnt, home, rep, q)
 
 
+def structured_topology(kind, RK, B, seed):
+    """Replica graphs with long paths for the cut iteration (17 to 64 ranks):
+    a chain (rank g holds replicas of experts homed on g - 1 and g + 1), a
+    ring (the chain closed), a star (every rank holds a replica of one of
+    rank 0's experts) and two chains joined by one edge; loads all on rank
+    0, a ramp, alternating heavy and light ranks, or near 2^40 on three
+    ranks."""
+    rng = np.random.default_rng(seed)
+    E = 4 * RK
+    home = np.tile(np.arange(E) % RK, (B, 1)).astype(np.int64)
+    if kind == "star":
+        home[:, :RK] = 0
+    rep = np.full((B, RK, 2), -1, dtype=np.int64)
+    h = RK // 2
+    for g in range(RK):
+        if kind in ("chain", "ring"):
+            if g > 0 or kind == "ring":
+                rep[:, g, 0] = (g - 1) % RK + RK
+            if g < RK - 1 or kind == "ring":
+                rep[:, g, 1] = (g + 1) % RK + 2 * RK
+        elif kind == "star" and g > 0:
+            rep[:, g, 0] = g
+        elif kind == "bridge":
+            if g % h > 0:
+                rep[:, g, 0] = (g - 1) + RK
+            if g == h:
+                rep[:, g, 1] = (h - 1) + 2 * RK
+    cnt = np.zeros((B, E), dtype=np.int64)
+    for b in range(B):
+        pat = b % 4
+        if pat == 0:
+            cnt[b] = np.where(home[b] == 0, rng.integers(1000, 100000, size=E), rng.integers(0, 10, size=E))
+        elif pat == 1:
+            cnt[b] = home[b] * 1000 + rng.integers(0, 1000, size=E)
+        elif pat == 2:
+            cnt[b] = np.where(home[b] % 2 == 0, rng.integers(10000, 20000, size=E), rng.integers(0, 100, size=E))
+        else:
+            cnt[b] = np.where(home[b] < 3, rng.integers((1 << 40) - 1000, (1 << 40) + 1, size=E),
+                              rng.integers(0, 1 << 20, size=E))
+    return cnt, home, rep
+
+
+@pytest.mark.parametrize("kind", ["chain", "ring", "star", "bridge"])
+@pytest.mark.parametrize("RK", [12, 16, 17, 24, 40, 64])
+def test_lp_solve_structured(kind, RK):
+    """Long augmenting paths: the enumeration (12, 16 ranks) and many rounds
+    of the cut iteration (17 to 64 ranks), every output against the
+    oracle."""
+    cnt, home, rep = structured_topology(kind, RK, B=8, seed=RK)
+    q = solve_both(cnt, home, rep)
+    assert (q["status"] == 0).all()
+    check_solution(cnt, home, rep, q)
+
+
 @pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE, wl.LPLB_TORUS], ids=lambda w: w.name)
 def test_lp_solve_topologies(work):
     """Batches of 16384 tokens x top-8 on the 8-GPU cube (the pages' r2o),

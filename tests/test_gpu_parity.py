@@ -229,6 +229,35 @@ def test_stream_1m_full_size():
                     ora.redirect(idx_h[l:l + 1], ref["log2phy"][l:l + 1], ref["logcnt"][l:l + 1]))
 
 
+def test_stream_1m_global_placement():
+    """One step of the streaming workload (58 x 2^20 x 8 ids) through the
+    global-policy decode placement (E = 256, P = 320 on 5 nodes x 8 GPUs,
+    X = 65), the launch bench.py times for the wide-table redirect: the
+    placement from the step's own histogram against the oracle, then the
+    redirect and the fused pass element by element on every layer."""
+    work, pl = wl.STREAM_1M, wl.GLOBAL_DECODE.placement
+    L, T, K, E = work.layers, work.tokens, work.topk, pl.E
+    idx = torch.empty((L, T, K), dtype=torch.int32, device=DEV)
+    note("global placement stream: generate + hist")
+    wl.routing_step_device(work, 3, DEV, out=idx)
+    ring = torch.zeros((2, L, E), dtype=torch.int32, device=DEV)
+    load, bad = eplb.load_hist(idx, E, ring, step=0)
+    torch.cuda.synchronize()
+    (phy2log, log2phy, logcnt, status), ref = rebalance_both(host(load), pl.P, pl.G, pl.N, pl.RK)
+    assert log2phy.shape[2] == 65 and int(logcnt.max()) > 1
+    l2p, cnt = gpu(log2phy), gpu(logcnt)
+    note("global placement stream: redirect + fused pass")
+    out = eplb.redirect(idx, l2p, cnt)
+    _, _, fused = eplb.hist_redirect(idx, E, ring, 1, l2p, cnt)
+    torch.cuda.synchronize()
+    assert bool(torch.equal(out, fused)), "fused pass and redirect differ"
+    assert bool(torch.equal(ring[1], ring[0])), "the fused pass counted other totals"
+    idx_h, out_h = host(idx), host(out)
+    for l in range(L):
+        assert_same(f"redirect layer {l}", out_h[l:l + 1],
+                    ora.redirect(idx_h[l:l + 1], ref["log2phy"][l:l + 1], ref["logcnt"][l:l + 1]))
+
+
 def test_layer_beyond_2gib():
     """One layer of 2^29 + 24 ids (just over 2 GiB): the redirect and the
     fused pass store through global stores instead of the buffer stores of
