@@ -133,8 +133,8 @@ int32_t eplb_load_hist(const int32_t* idx, int64_t L, int64_t T, int32_t K, int3
  * (P < E), EPLB_E_CAPACITY (X too small), EPLB_E_LIMIT (B > 2^22, E > 4096,
  * P > 8192, X > 65535, more than 512 experts or 512 GPUs on one node (the
  * global policy counts all of them as one node), more than 512 nodes, a
- * possible replica count above 16128, or a working set above 64 KiB of
- * LDS), EPLB_E_HIP.
+ * possible replica count above 16128, or a working set above 160 KiB of
+ * LDS, the LDS of one gfx950 compute unit), EPLB_E_HIP.
  */
 int32_t eplb_rebalance(const int64_t* load, int64_t B, int32_t E, int32_t P,
                        int32_t G, int32_t N, int32_t RK, int32_t X,

@@ -1777,7 +1777,9 @@ int32_t rb_make_plan(int32_t E, int32_t P, int32_t G, int32_t N, int32_t RK, int
   p.o_nflag = take(4ll * Np, 4);
   p.o_flags = take(16, 8);
   off = (off + 15) / 16 * 16;
-  if (off > kMaxLdsBytes) return EPLB_E_LIMIT;
+  // up to 64 KiB for every shape of the pages' workloads; wider shapes take
+  // more of the CU's 160 KiB (one workgroup per CU then)
+  if (off > kMaxRebalanceLdsBytes) return EPLB_E_LIMIT;
   p.lds_bytes = (int32_t)off;
   *out = p;
   return 0;

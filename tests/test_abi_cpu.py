@@ -112,6 +112,9 @@ def test_rebalance_limits_and_nulls(lib):
     assert lib.eplb_rebalance_lds_bytes(1024, 1024, 1, 1, 8, 1) == -5          # 1024 experts on one node
     assert lib.eplb_rebalance_lds_bytes(512, 512, 1, 1, 8, 1) > 0               # 512 fit
     assert lib.eplb_rebalance_lds_bytes(1024, 1024, 2, 2, 8, 1) > 0             # 512 per node
+    # up to 160 KiB (the LDS of one gfx950 compute unit), not beyond
+    assert 64 * 1024 < lib.eplb_rebalance_lds_bytes(2560, 3072, 8, 8, 64, 65) <= 160 * 1024
+    assert lib.eplb_rebalance_lds_bytes(3072, 4096, 8, 8, 64, 129) == -5
     # the documented workloads fit
     for args in [(16, 24, 4, 2, 8, 5), (256, 288, 8, 4, 32, 9), (256, 320, 8, 5, 40, 65),
                  (512, 640, 16, 8, 64, 17), (256, 288, 8, 18, 144, 33), (60, 1830, 1, 1, 10, 1771)]:

@@ -516,6 +516,31 @@ def test_step1_packing_forms(shape):
     rebalance_both(load, P, G, N, RK)
 
 
+@pytest.mark.parametrize("shape", [
+    (1164, 12, 6, 186, 1302),    # 66 KiB
+    (600, 8, 4, 512, 3072),      # 80 KiB: 128 GPUs per node, counts up to 619
+    (1860, 20, 5, 500, 2000),    # 114 KiB, global policy
+    (2048, 8, 4, 32, 2304),      # 116 KiB
+    (2048, 16, 8, 256, 4096),    # 144 KiB
+    (2560, 8, 8, 64, 3072),      # 148 KiB
+])
+def test_shapes_beyond_64k_lds(shape):
+    """Shapes whose working set is between 64 and 160 KiB of LDS (one
+    workgroup per compute unit), zero, tied, skewed and 2^40-scale loads,
+    against the oracle."""
+    E, G, N, RK, P = shape
+    X = ora.max_count(E, P, G, N)
+    assert eplb.lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, X) > 64 * 1024
+    rng = np.random.default_rng(E + P)
+    load = np.stack([
+        rng.integers(0, 3, size=E),
+        (rng.zipf(1.2, size=E) * 1000).clip(0, 1 << 40),
+        rng.integers((1 << 40) - 1000, (1 << 40) + 1, size=E),
+        np.where(np.arange(E) % 7 == 0, rng.integers(0, 1 << 30, size=E), 0),
+    ]).astype(np.int64)
+    rebalance_both(load, P, G, N, RK, X)
+
+
 def test_large_loads_and_exactness():
     rng = np.random.default_rng(5)
     load = rng.integers((1 << 40) - 5000, (1 << 40) + 1, size=(16, 64))
