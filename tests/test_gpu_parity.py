@@ -490,6 +490,93 @@ def test_random_shapes_fuzz():
         rebalance_both(load.astype(np.int64), P, G, N, RK)
 
 
+def _wide_fuzz_shapes(rng, count):
+    """Valid shapes over a wider range than _fuzz_shapes: up to 16 nodes and
+    1024 experts, 1 to 256 GPUs per node, 1 to 8 experts per GPU, group
+    sizes up to 16."""
+    out = []
+    while len(out) < count:
+        N = int(rng.choice([1, 1, 2, 3, 4, 5, 6, 8, 16]))
+        hier = N == 1 or rng.random() < 0.6
+        G = N * int(rng.integers(1, 5)) if hier else int(rng.choice([g for g in range(2, 20) if g % N]))
+        Np = N if hier else 1
+        E = G * int(rng.integers(1, 17)) if hier else int(rng.integers(2, 300))
+        RK = Np * int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 15, 16, 17, 20, 24, 31, 32, 33, 40, 48, 63,
+                                  64, 65, 80, 100, 128, 130, 200, 256]))
+        P = RK * int(rng.integers(1, 9))
+        if P < E or E > 1024 or P > 2048 or E // Np > 512 or RK > 512 or (hier and E % G):
+            continue
+        out.append((E, G, N, RK, P))
+    return out
+
+
+def _fuzz_loads(rng, E, B):
+    """B load rows of one of ten kinds: ties of small values, uniform, Zipf,
+    near 2^40, one hot expert, all equal, powers of two, values whose ratios
+    to replica counts tie, mostly zero, all zero."""
+    rows = []
+    for _ in range(B):
+        k = int(rng.integers(0, 10))
+        if k == 0:
+            r = rng.integers(0, 3, size=E)
+        elif k == 1:
+            r = rng.integers(0, 1 << 20, size=E)
+        elif k == 2:
+            r = (rng.zipf(1.2, size=E) * 997).clip(0, 1 << 40)
+        elif k == 3:
+            r = rng.integers((1 << 40) - 50, (1 << 40) + 1, size=E)
+        elif k == 4:
+            r = rng.integers(0, 100, size=E)
+            r[rng.integers(0, E)] = int(rng.integers(1 << 20, 1 << 40))
+        elif k == 5:
+            r = np.full(E, int(rng.integers(0, 1 << 40)))
+        elif k == 6:
+            r = 1 << rng.integers(0, 41, size=E)
+        elif k == 7:
+            r = rng.choice([0, 6, 12, 18, 24, 36, 60, 120, 360, 720], size=E)
+        elif k == 8:
+            r = np.where(rng.random(E) < 0.8, 0, rng.integers(1, 1000, size=E))
+        else:
+            r = np.zeros(E)
+        rows.append(np.asarray(r, dtype=np.int64))
+    return np.stack(rows)
+
+
+def _oracle_check(job):
+    """In a worker process (numpy and the oracle only): the first output of
+    one shape that differs from the oracle's, or None."""
+    shape, X, load, got = job
+    E, G, N, RK, P = shape
+    ref = ora.rebalance(load, P, G, N, RK, X)
+    for name, g in zip(("phy2log", "log2phy", "logcnt", "status"), got):
+        if not np.array_equal(g, ref[name]):
+            return shape, name, tuple(np.argwhere(g != ref[name])[0])
+    return None
+
+
+def test_wide_random_fuzz():
+    """3000 random shapes of _wide_fuzz_shapes, four load rows each of the
+    ten kinds of _fuzz_loads, every output against the oracle (the oracle on
+    a pool of forked worker processes, which touch no GPU)."""
+    import multiprocessing
+    import os
+    rng = np.random.default_rng(20261204)
+    jobs = []
+    for i, (E, G, N, RK, P) in enumerate(_wide_fuzz_shapes(rng, 3000)):
+        X = ora.max_count(E, P, G, N)
+        load = _fuzz_loads(rng, E, 4)
+        outs = eplb.rebalance(gpu(load), P, G, N, RK, X)
+        torch.cuda.synchronize()
+        jobs.append(((E, G, N, RK, P), X, load, [host(t) for t in outs]))
+        if i % 500 == 0:
+            note(f"wide fuzz: {i} shapes on the GPU")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    note(f"wide fuzz: oracle on {workers} processes")
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        bad = [r for r in pool.imap_unordered(_oracle_check, jobs, chunksize=8) if r is not None]
+    assert not bad, f"{len(bad)} shapes differ from the oracle, first: {bad[0]}"
+
+
 @pytest.mark.parametrize("shape", [
     (512, 16, 8, 64, 640),       # 16 groups onto 8 nodes; totals of 2^48 and above take the 64-bit sums
     (128, 64, 32, 32, 160),      # 64 groups onto 32 nodes: runs found in LDS (17 to 64 nodes)
