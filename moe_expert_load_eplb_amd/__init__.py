@@ -182,6 +182,34 @@ def rebalance(load: torch.Tensor, P: int, G: int, N: int, RK: int, X: int | None
     return phy2log, log2phy, logcnt, status
 
 
+def rebalance_experts(weight: torch.Tensor, num_replicas: int, num_groups: int, num_nodes: int, num_gpus: int):
+    """The pages' interface to the rebalance (EPLB README translation,
+    «DualPipe и EPLB», Part 2, section "Интерфейс и пример"): the same
+    arguments and the same three maps, for a caller switching from it.
+
+    weight [layers, E]: token counts per logical expert, any integer dtype or
+    a floating dtype holding whole numbers, on the GPU or the host (a host
+    tensor is copied to the current GPU).  Returns int64 (phy2log [layers,
+    num_replicas], log2phy [layers, E, max logcnt], logcnt [layers, E]) on
+    weight's device; log2phy is as wide as the largest replica count, as the
+    pages' function returns it, which costs one device-to-host read.  A load
+    outside [0, 2^40] raises EplbError.
+    """
+    if weight.dim() != 2:
+        raise ValueError("weight must be [layers, experts]")
+    if weight.is_floating_point() and not bool(torch.equal(weight, torch.trunc(weight))):
+        raise ValueError("weight must hold whole token counts")
+    dev = weight.device if weight.device.type == "cuda" else torch.device("cuda", torch.cuda.current_device())
+    load = weight.to(device=dev, dtype=torch.int64).contiguous()
+    phy2log, log2phy, logcnt, status = rebalance(load, num_replicas, num_groups, num_nodes, num_gpus)
+    bad = status.ne(0).nonzero()
+    if bad.numel():
+        raise EplbError(int(status[bad[0, 0]]), f"eplb_rebalance (layer {int(bad[0, 0])})")
+    width = int(logcnt.max()) if logcnt.numel() else 1
+    out = (phy2log.long(), log2phy[:, :, :width].long(), logcnt.long())
+    return tuple(t.to(weight.device) for t in out)
+
+
 def redirect(idx: torch.Tensor, log2phy: torch.Tensor, logcnt: torch.Tensor,
              out: torch.Tensor | None = None) -> torch.Tensor:
     """Physical replica of every routed (token, k): [L, T, K] int32."""

@@ -82,6 +82,30 @@ def test_worked_example_gpu():
     rebalance_both(w, 16, 3, 2, 8, 5)
 
 
+def test_rebalance_experts_interface():
+    """The pages' call on their example (float weights on the host, as the
+    pages pass them, and int64 on the GPU): int64 maps on the weight's
+    device, log2phy as wide as the largest count, the printed values."""
+    g = oracle_pins.GOLDEN
+    inp = g["inputs"]
+    args = (inp["num_replicas"], inp["num_groups"], inp["num_nodes"], inp["num_gpus"])
+    w = torch.tensor(inp["weight"], dtype=torch.float32)
+    for weight in (w, w.to(torch.int64).to(DEV)):
+        phy2log, log2phy, logcnt = eplb.rebalance_experts(weight, *args)
+        assert all(t.dtype == torch.int64 and t.device == weight.device for t in (phy2log, log2phy, logcnt))
+        assert phy2log.tolist() == g["phy2log"]["value"]
+        assert logcnt[0].tolist() == g["layer0_logcnt"]["value"]
+        assert log2phy.shape == (2, 12, 2)
+        assert log2phy[0, 0].tolist() == g["layer0_log2phy"]["expert0"]
+        assert log2phy[0, 1].tolist() == g["layer0_log2phy"]["expert1"]
+    with pytest.raises(ValueError):
+        eplb.rebalance_experts(w + 0.5, *args)
+    with pytest.raises(eplb.EplbError):
+        eplb.rebalance_experts(-w, *args)                       # negative loads: the problem's status
+    with pytest.raises(eplb.EplbError):
+        eplb.rebalance_experts(w, 16, 4, 2, 7)                  # 16 slots do not divide over 7 GPUs
+
+
 # ---------------------------------------------------------------- the five workloads
 
 def _routing_steps(work, steps, tokens=None):
