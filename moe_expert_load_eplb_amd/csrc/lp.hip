@@ -607,6 +607,9 @@ __global__ __launch_bounds__(kLpDkThreads) void lp_solve_dk_kernel(
 // with one ballot per bit of the number (peers share every bit), so the
 // numbering matches a sequential pass exactly.
 
+// Waves per workgroup within the 64 KiB budget; a single wave whose tables
+// alone exceed it (E = 4096 with 4096 filled slots: 80 KiB) still fits the
+// 160 KiB of a gfx950 compute unit.
 __host__ __device__ inline int lp_waves_per_block(int words_per_wave) {
   const int w = (kMaxLdsBytes / 4) / words_per_wave;
   return w < 1 ? 1 : (w > 4 ? 4 : w);
@@ -615,8 +618,11 @@ __host__ __device__ inline int lp_waves_per_block(int words_per_wave) {
 // cmap[e] = compact number (< C) of expert e (-1: not replicated); with
 // pid/fx, the slot's physical id and its flow clamped to int32.  Returns whether the
 // layer's table is bad (an id out of range, or an expert named twice).
+// x0 and f0 are slot `lane`'s entry of rl and fl, read by the caller
+// together with its other loads (f0 only when pid is set); slots from 64 on
+// are read here.
 __device__ bool lp_build_map(const int32_t* rl, const int64_t* fl, int32_t RKR, int32_t E, int32_t C,
-                             int32_t* cmap, int32_t* pid, int32_t* fx) {
+                             int32_t* cmap, int32_t* pid, int32_t* fx, int32_t x0, int64_t f0) {
   const int lane = threadIdx.x & 63;
   for (int e = lane; e < E; e += 64) cmap[e] = -1;
   lp_wave_sync();
@@ -624,7 +630,7 @@ __device__ bool lp_build_map(const int32_t* rl, const int64_t* fl, int32_t RKR, 
   int base = 0;
   for (int i0 = 0; i0 < RKR; i0 += 64) {
     const int i = i0 + lane;
-    const int32_t x = i < RKR ? rl[i] : -1;
+    const int32_t x = i0 == 0 ? x0 : (i < RKR ? rl[i] : -1);
     const bool inr = (uint32_t)x < (uint32_t)E;
     if (x != -1 && !inr) bad = 1;
     const uint64_t m = __builtin_amdgcn_ballot_w64(inr);
@@ -634,7 +640,7 @@ __device__ bool lp_build_map(const int32_t* rl, const int64_t* fl, int32_t RKR, 
       if (atomicExch(&cmap[x], c) != -1) bad = 1;   // named twice
       if (pid != nullptr) {
         pid[c] = E + i;
-        const int64_t f = fl[i];
+        const int64_t f = i0 == 0 ? f0 : fl[i];
         fx[c] = f <= 0 ? 0 : (f >= 0x7fffffff ? 0x7fffffff : (int32_t)f);
       }
     }
@@ -664,7 +670,9 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
     const int i = k * 64 + lane;
     v[k] = i < len ? src[i] : -1;
   }
-  lp_build_map(rep + l * RKR, nullptr, RKR, E, C, cmap, nullptr, nullptr);
+  const int32_t* rl = rep + l * RKR;
+  const int32_t x0 = lane < RKR ? rl[lane] : -1;       // with the ids: one round trip for both
+  lp_build_map(rl, nullptr, RKR, E, C, cmap, nullptr, nullptr, x0, 0);
 #pragma unroll
   for (int k = 0; k < kLpSeg / 64; ++k) {
     const int c = (uint32_t)v[k] < (uint32_t)E ? cmap[v[k]] : -1;
@@ -712,10 +720,11 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
   const int64_t q = (int64_t)blockIdx.x * wpb + wave;
   if (q >= LS) return;                                 // whole wave; no workgroup barrier below
   const int64_t l = q / S, s = q - l * S;
-  int32_t* cmap = lp_tab + wave * (E + 3 * C);
+  int32_t* cmap = lp_tab + wave * (E + 4 * C);
   int32_t* run = cmap + E;                             // running occurrence count per compact number
   int32_t* pid = run + C;                              // its replica's physical id
   int32_t* fx = pid + C;                               // its replica's flow (clamped to int32)
+  int32_t* nxt = fx + C;                               // the next segment's prefix
   const int32_t* src = idx + l * n + s * kLpSeg;
   int32_t* dst = out + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
@@ -725,26 +734,35 @@ __global__ __launch_bounds__(256) void lp_redirect_kernel(const int32_t* __restr
     const int i = k * 64 + lane;
     v[k] = i < len ? src[i] : -1;
   }
+  // the tables' first 64 entries are read with the ids (one round trip)
   const int32_t* base = seg + q * C;
-  for (int c = lane; c < C; c += 64) run[c] = base[c];
+  const bool has_next = s + 1 < S;
   const int32_t* rl = rep + l * RKR;
-  const bool bad = lp_build_map(rl, flow + l * RKR, RKR, E, C, cmap, pid, fx);
+  const int64_t* fl = flow + l * RKR;
+  const int32_t x0 = lane < RKR ? rl[lane] : -1;
+  const int64_t f0 = lane < RKR ? fl[lane] : 0;
+  const int32_t b0 = lane < C ? base[lane] : 0;
+  const int32_t n0 = has_next && lane < C ? base[C + lane] : 0;
+  for (int c = lane; c < C; c += 64) {
+    run[c] = c == lane ? b0 : base[c];
+    nxt[c] = c == lane ? n0 : (has_next ? base[C + c] : 0);
+  }
+  const bool bad = lp_build_map(rl, fl, RKR, E, C, cmap, pid, fx, x0, f0);
   // A replicated expert's ids in this segment all go to its replica when
   // the segment ends at or before its flow, all stay when it starts at or
   // beyond it; only in the segment where the flow runs out are they decided
   // one by one.  cmap[e] becomes -1 (stay), -2 - pid (all to the replica),
   // or the compact number (one by one).  The next segment's prefix ends this
   // one's occurrences; the layer's last segment counts as undecided.
-  const bool has_next = s + 1 < S;
   for (int i0 = 0; i0 < RKR && !bad; i0 += 64) {
     const int i = i0 + lane;
-    const int32_t x = i < RKR ? rl[i] : -1;
+    const int32_t x = i0 == 0 ? x0 : (i < RKR ? rl[i] : -1);
     if ((uint32_t)x < (uint32_t)E) {
       const int c = cmap[x];
       if (c >= 0 && pid[c] == E + i) {                 // the slot that holds x's compact number
         const int32_t f = fx[c];
         if (run[c] >= f) cmap[x] = -1;
-        else if (has_next && base[C + c] <= f) cmap[x] = -2 - (E + i);
+        else if (has_next && nxt[c] <= f) cmap[x] = -2 - (E + i);
       }
     }
   }
@@ -802,8 +820,8 @@ hipError_t launch_lp_redirect(const int32_t* idx, int64_t L, int64_t n, int32_t 
   lp_seg_scan_kernel<<<(unsigned)(scan_blocks < 65536 ? scan_blocks : 65536), 256, 0, stream>>>(seg, L, S, C);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int wpb_c = lp_waves_per_block(E + 3 * C);
-  lp_redirect_kernel<<<(unsigned)((LS + wpb_c - 1) / wpb_c), 64 * wpb_c, (size_t)wpb_c * (E + 3 * C) * 4, stream>>>(
+  const int wpb_c = lp_waves_per_block(E + 4 * C);
+  lp_redirect_kernel<<<(unsigned)((LS + wpb_c - 1) / wpb_c), 64 * wpb_c, (size_t)wpb_c * (E + 4 * C) * 4, stream>>>(
       idx, n, E, nbits, rep, flow, RKR, C, S, LS, wpb_c, seg, out);
   return hipGetLastError();
 }
