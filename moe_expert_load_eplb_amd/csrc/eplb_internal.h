@@ -13,8 +13,7 @@ typedef unsigned __int128 u128;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));   // one 16-byte vector of ids
 
 constexpr int64_t kLoadMax = int64_t(1) << 40;   // largest accepted load
-constexpr int kMaxLdsBytes = 64 * 1024;          // per-workgroup LDS budget of the streaming kernels
-constexpr int kMaxRebalanceLdsBytes = 160 * 1024;  // a rebalance workgroup may take a whole gfx950 CU's LDS
+constexpr int kMaxLdsBytes = 64 * 1024;          // per-workgroup LDS budget
 constexpr int kMaxE = 4096;                      // per-expert LDS tables
 constexpr int kMaxX = 65535;                     // log2phy width
 constexpr int kMaxCount = 16128;                 // replica count bound (< 131^2)

@@ -1699,6 +1699,10 @@ RbKernel pick_kr(int KR, int KP) {   // kFull = false only
   }
 }
 
+// A rebalance workgroup may take the whole LDS of a gfx950 compute unit (the
+// other kernels keep to kMaxLdsBytes).
+constexpr int kMaxRebalanceLdsBytes = 160 * 1024;
+
 // Up to one workgroup per CU (256 CUs): the uncapped instantiations.
 constexpr int64_t kRbFewProblems = 256;
 
