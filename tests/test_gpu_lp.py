@@ -136,6 +136,78 @@ def test_lp_solve_structured(kind, RK):
     check_solution(cnt, home, rep, q)
 
 
+def _fuzz_problem(rng):
+    """Four problems of one random topology: 1 to 64 ranks, 1 to 64 slots per
+    rank filled to 20-100%, homes round-robin or random, counts small, large,
+    Zipf, near 2^40 or mostly zero."""
+    RK = int(rng.choice([1, 2, 3, 5, 8, 11, 12, 13, 16, 17, 20, 24, 31, 32, 33, 40, 48, 63, 64]))
+    R = int(rng.choice([1, 1, 2, 2, 3, 4, 8, 16, 64]))
+    E = int(rng.integers(max(2, RK), 600))
+    B = 4
+    kind = int(rng.integers(0, 5))
+    if kind == 0:
+        cnt = rng.integers(0, 50, size=(B, E))
+    elif kind == 1:
+        cnt = rng.integers(0, 10**6, size=(B, E))
+    elif kind == 2:
+        cnt = (rng.zipf(1.3, size=(B, E)) * 100).clip(0, 1 << 40)
+    elif kind == 3:
+        cnt = rng.integers((1 << 40) - 10**6, (1 << 40) + 1, size=(B, E))
+    else:
+        cnt = np.where(rng.random((B, E)) < 0.7, 0, rng.integers(1, 1000, size=(B, E)))
+    home = (np.tile(np.arange(E) % RK, (B, 1)) if rng.random() < 0.5 else rng.integers(0, RK, size=(B, E)))
+    fill = float(rng.choice([0.2, 0.5, 0.9, 1.0]))
+    rep = np.full((B, RK, R), -1, dtype=np.int64)
+    for b in range(B):
+        pool = list(rng.permutation(E))
+        for g in range(RK):
+            for j in range(R):
+                if pool and rng.random() < fill:
+                    rep[b, g, j] = pool.pop()
+    return cnt.astype(np.int64), home.astype(np.int64), rep
+
+
+def _oracle_check(job):
+    """In a worker process (numpy and the oracle only): what differs from the
+    oracle for one batch, or None."""
+    i, cnt, home, rep, got, idx, red = job
+    ref = ora.lp_solve(cnt, home, rep, rep.shape[1])
+    for k, g in zip(SOLVE_KEYS, got):
+        if not np.array_equal(g, ref[k]):
+            return i, k
+    if idx is not None and not np.array_equal(red, ora.lp_redirect(idx, rep, ref["flow"], cnt.shape[1])):
+        return i, "redirect"
+    return None
+
+
+def test_lp_wide_random_fuzz():
+    """2000 random topologies (four problems each) through the solve, every
+    fourth also a routed batch through the redirect by its flows, all against
+    the oracle (on a pool of forked worker processes, which touch no GPU)."""
+    import multiprocessing
+    import os
+    rng = np.random.default_rng(20261205)
+    jobs = []
+    for i in range(2000):
+        cnt, home, rep = _fuzz_problem(rng)
+        B, E = cnt.shape
+        got = [t.cpu().numpy() for t in eplb.lp_solve(gpu(cnt, torch.int64), gpu(home, torch.int32),
+                                                      gpu(rep, torch.int32))]
+        idx = red = None
+        if i % 4 == 0:
+            T, K = int(rng.integers(1, 3000)), int(rng.integers(1, 9))
+            idx = rng.integers(-1, E + 1, size=(B, T, K)).astype(np.int32)
+            red = eplb.lp_redirect(gpu(idx, torch.int32), E, gpu(rep, torch.int32), gpu(got[1], torch.int64)).cpu().numpy()
+        jobs.append((i, cnt, home, rep, got, idx, red))
+        if i % 500 == 0:
+            note(f"wide fuzz: {i} batches on the GPU")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    note(f"wide fuzz: oracle on {workers} processes")
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        bad = [r for r in pool.imap_unordered(_oracle_check, jobs, chunksize=4) if r is not None]
+    assert not bad, f"{len(bad)} batches differ from the oracle, first: {bad[0]}"
+
+
 @pytest.mark.parametrize("work", [wl.LPLB_CUBE, wl.LPLB_HYPERCUBE, wl.LPLB_TORUS], ids=lambda w: w.name)
 def test_lp_solve_topologies(work):
     """Batches of 16384 tokens x top-8 on the 8-GPU cube (the pages' r2o),

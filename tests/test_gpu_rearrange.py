@@ -132,6 +132,66 @@ def test_rearrange_random(B, E, RK, ppr, N):
     check_properties(old, new, RK, q)
 
 
+def _oracle_check(job):
+    """In a worker process (numpy and the oracle only): the first output of
+    one case that differs from the oracle's, or None."""
+    i, old, new, l2p, RK, N, got = job
+    ref = ora.rearrange_plan(old, new, l2p, RK, N)
+    for k, g in zip(KEYS, got):
+        if not np.array_equal(g, ref[k]):
+            return i, k
+    return None
+
+
+def test_rearrange_wide_fuzz():
+    """1500 random cases of three problems: 1 to 256 ranks, any node count
+    dividing them, 1 to 9 slots per rank, fresh or slightly changed
+    placements, log2phy wider than needed, and one problem in eight with a
+    bad entry; every output against the oracle (on a pool of forked worker
+    processes, which touch no GPU)."""
+    import multiprocessing
+    import os
+    rng = np.random.default_rng(20261206)
+    jobs = []
+    for i in range(1500):
+        RK = int(rng.choice([1, 2, 3, 4, 5, 8, 13, 16, 32, 64, 100, 256]))
+        N = int(rng.choice([d for d in range(1, RK + 1) if RK % d == 0]))
+        ppr = int(rng.integers(1, 10))
+        P = RK * ppr
+        E = int(rng.integers(1, P + 1))
+        B = 3
+
+        def placement():
+            return np.stack([rng.permutation(np.concatenate([np.arange(E), rng.integers(0, E, P - E)]))
+                             for _ in range(B)])
+        old = placement()
+        new = placement() if rng.random() < 0.5 else old.copy()
+        if rng.random() < 0.5:
+            for b in range(B):
+                j = rng.integers(0, P, size=max(1, P // 8))
+                new[b, j] = new[b, rng.permutation(j)]
+        X = max(int(np.bincount(new[b], minlength=E).max()) for b in range(B)) + int(rng.integers(0, 3))
+        l2p = oracle_pins._valid_l2p(new, E, X)
+        if rng.random() < 0.125:
+            b = int(rng.integers(0, B))
+            which = int(rng.integers(0, 3))
+            if which == 0:
+                old[b, int(rng.integers(0, P))] = E
+            elif which == 1:
+                new[b, int(rng.integers(0, P))] = -1
+            else:
+                l2p[b, int(rng.integers(0, E)), 0] = P
+        got = [t.cpu().numpy() for t in eplb.rearrange(gpu(old), gpu(new), gpu(l2p), RK, N)]
+        jobs.append((i, old, new, l2p, RK, N, got))
+        if i % 500 == 0:
+            note(f"wide fuzz: {i} cases on the GPU")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    note(f"wide fuzz: oracle on {workers} processes")
+    with multiprocessing.get_context("fork").Pool(workers) as pool:
+        bad = [r for r in pool.imap_unordered(_oracle_check, jobs, chunksize=4) if r is not None]
+    assert not bad, f"{len(bad)} cases differ from the oracle, first: {bad[0]}"
+
+
 def test_rearrange_max_size():
     """P = 8192 on one rank (the longest scans) and on 512 ranks; E = 4096;
     checked by properties."""
