@@ -829,6 +829,53 @@ def test_stream_entries_fuzz():
         assert_same("fused ema redirect", host(out), want)
 
 
+def test_stream_entries_wide_fuzz():
+    """300 more random cases through the redirect, the fused pass and the
+    fused moving average over a wider range: up to 4096 experts and log2phy
+    widths up to 70 (placements whose replica lists exceed the workgroup's
+    staged table read the global rows), outputs on every 4-byte phase
+    against the input, against the oracle."""
+    rng = np.random.default_rng(2026)
+    for case in range(300):
+        L = int(rng.integers(1, 5))
+        T = int(rng.choice([1, 5, int(rng.integers(1, 3000))]))
+        K = int(rng.integers(1, 9))
+        E = int(rng.choice([3, 64, 256, 1000, 4096, int(rng.integers(1, 4097))]))
+        X = int(rng.choice([1, 2, 9, 33, 65, 70]))
+        W = int(rng.integers(1, 4))
+        step = int(rng.integers(0, 9))
+        shift = int(rng.integers(0, 8))
+        phase = int(rng.integers(0, 4))
+        idx_h = rng.integers(-2, E + 2, size=(L, T, K)).astype(np.int32)
+        if rng.random() < 0.5:                        # mostly valid counts, many replicas
+            logcnt = rng.integers(1, X + 1, size=(L, E)).astype(np.int32)
+        else:
+            logcnt = rng.integers(-1, X + 2, size=(L, E)).astype(np.int32)
+        log2phy = rng.integers(0, 1 << 20, size=(L, E, X)).astype(np.int32)
+        ring_h = rng.integers(0, 1000, size=(W, L, E)).astype(np.int32)
+        cnt, invl = ora.load_hist(idx_h, E)
+        want = ora.redirect(idx_h, log2phy, logcnt)
+        idx_d, l2p_d, cnt_d = gpu(idx_h), gpu(log2phy), gpu(logcnt)
+        n = L * T * K
+        big = torch.empty(n + 4, dtype=torch.int32, device=DEV)
+        out = big[phase:phase + n].view(L, T, K)
+        eplb.redirect(idx_d, l2p_d, cnt_d, out=out)
+        torch.cuda.synchronize()
+        assert_same(f"case {case} redirect", host(out), want)
+        ring = gpu(ring_h)
+        others = ring_h.astype(np.int64).sum(axis=0) - ring_h[step % W]
+        load, bad, _ = eplb.hist_redirect(idx_d, E, ring, step, l2p_d, cnt_d, out=out)
+        torch.cuda.synchronize()
+        assert_same(f"case {case} fused redirect", host(out), want)
+        assert_same(f"case {case} fused window", host(load), others + cnt)
+        assert_same(f"case {case} fused invalid", host(bad), invl)
+        ema_h = rng.integers(0, 1 << 40, size=(L, E)).astype(np.int64)
+        ema, count, bad, _ = eplb.ema_redirect(idx_d, E, gpu(ema_h), shift, l2p_d, cnt_d, out=out)
+        torch.cuda.synchronize()
+        assert_same(f"case {case} fused ema redirect", host(out), want)
+        assert_same(f"case {case} fused ema", host(ema), ora.ema_update(ema_h, cnt, shift).reshape(L, E))
+
+
 @pytest.mark.parametrize("work", [wl.TINY_HIER, wl.DSV3_PREFILL], ids=lambda w: w.name)
 def test_fused_serving_loop(work):
     """A serving loop: step s is redirected with the placement from the window
