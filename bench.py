@@ -53,7 +53,7 @@ def main() -> int:
                     help="run one phase alone (for a kernel trace of it) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs the path on a single MI355X "
+        print(f"bench.py measures one GPU: the library runs the path on a single MI355X "
               f"(--gpus {args.gpus} is not supported; EP ranks and nodes are placement "
               f"parameters, not devices)", file=sys.stderr)
         return 2
