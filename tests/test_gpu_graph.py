@@ -94,3 +94,41 @@ def test_graph_replay_matches_eager(work, tokens, W):
                             ora.max_count(work.placement.E, work.placement.P, work.placement.G, work.placement.N))
         assert np.array_equal(g[3], ref["phy2log"]) and np.array_equal(g[5], ref["logcnt"])
         prev = g[3:]
+
+
+def test_concurrent_streams():
+    """Calls on three streams at once (disjoint buffers; the library keeps no
+    state) give the outputs of the same calls made one after another."""
+    work = wl.DSV3_PREFILL
+    pl = work.placement
+    idx = torch.from_numpy(wl.routing_step(work, 0, tokens=2048)).to(DEV)
+    loads = torch.from_numpy(wl.zipf_loads(58, pl.E, 1.1, 1 << 20)).to(DEV)
+    sk = wl.SKEWED_1024.placement
+    sk_loads = torch.from_numpy(wl.skewed_loads(wl.SKEWED_1024, range(256))).to(DEV)
+    base = eplb.rebalance(loads, pl.P, pl.G, pl.N, pl.RK)
+
+    def calls(ring):
+        return eplb.hist_redirect(idx, pl.E, ring, 0, base[1], base[2])
+
+    # one after another on the current stream
+    ring0 = torch.zeros((2, 58, pl.E), dtype=torch.int32, device=DEV)
+    want_a = [t.clone() for t in calls(ring0)]
+    want_b = [t.clone() for t in eplb.rebalance(loads, pl.P, pl.G, pl.N, pl.RK)]
+    want_c = [t.clone() for t in eplb.rebalance(sk_loads, sk.P, sk.G, sk.N, sk.RK)]
+    torch.cuda.synchronize()
+    for rep in range(5):
+        note(f"three streams, round {rep}")
+        streams = [torch.cuda.Stream(DEV) for _ in range(3)]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream(DEV))
+        ring = torch.zeros((2, 58, pl.E), dtype=torch.int32, device=DEV)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(streams[0]):
+            got_a = calls(ring)
+        with torch.cuda.stream(streams[1]):
+            got_b = eplb.rebalance(loads, pl.P, pl.G, pl.N, pl.RK)
+        with torch.cuda.stream(streams[2]):
+            got_c = eplb.rebalance(sk_loads, sk.P, sk.G, sk.N, sk.RK)
+        torch.cuda.synchronize()
+        for w, g in zip(want_a + want_b + want_c, list(got_a) + list(got_b) + list(got_c)):
+            assert torch.equal(w, g)
