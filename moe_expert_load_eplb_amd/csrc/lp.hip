@@ -665,10 +665,22 @@ __global__ __launch_bounds__(256) void lp_seg_count_kernel(const int32_t* __rest
   const int32_t* src = idx + l * n + s * kLpSeg;
   const int len = (int)min((int64_t)kLpSeg, n - s * kLpSeg);
   int32_t v[kLpSeg / 64];                              // the whole segment in flight at once
+  if (len == kLpSeg && ((uintptr_t)src & 15) == 0) {   // uniform: counting needs no order, so 16-byte loads
+    const i32x4* s4 = reinterpret_cast<const i32x4*>(src);
 #pragma unroll
-  for (int k = 0; k < kLpSeg / 64; ++k) {
-    const int i = k * 64 + lane;
-    v[k] = i < len ? src[i] : -1;
+    for (int k = 0; k < kLpSeg / 256; ++k) {
+      const i32x4 x = s4[k * 64 + lane];
+      v[4 * k] = x.x;
+      v[4 * k + 1] = x.y;
+      v[4 * k + 2] = x.z;
+      v[4 * k + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kLpSeg / 64; ++k) {
+      const int i = k * 64 + lane;
+      v[k] = i < len ? src[i] : -1;
+    }
   }
   const int32_t* rl = rep + l * RKR;
   const int32_t x0 = lane < RKR ? rl[lane] : -1;       // with the ids: one round trip for both
