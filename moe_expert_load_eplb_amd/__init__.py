@@ -199,6 +199,8 @@ def rebalance_experts(weight: torch.Tensor, num_replicas: int, num_groups: int, 
         raise ValueError("weight must be [layers, experts]")
     if weight.is_floating_point() and not bool(torch.equal(weight, torch.trunc(weight))):
         raise ValueError("weight must hold whole token counts")
+    if weight.is_floating_point() and weight.numel() and float(weight.abs().max()) >= 2.0 ** 62:
+        raise ValueError("weight holds values that do not convert to int64")
     dev = weight.device if weight.device.type == "cuda" else torch.device("cuda", torch.cuda.current_device())
     load = weight.to(device=dev, dtype=torch.int64).contiguous()
     phy2log, log2phy, logcnt, status = rebalance(load, num_replicas, num_groups, num_nodes, num_gpus)
