@@ -100,6 +100,8 @@ def test_rebalance_experts_interface():
         assert log2phy[0, 1].tolist() == g["layer0_log2phy"]["expert1"]
     with pytest.raises(ValueError):
         eplb.rebalance_experts(w + 0.5, *args)
+    with pytest.raises(ValueError):
+        eplb.rebalance_experts(w * 2.0 ** 70, *args)            # beyond int64
     with pytest.raises(eplb.EplbError):
         eplb.rebalance_experts(-w, *args)                       # negative loads: the problem's status
     with pytest.raises(eplb.EplbError):
