@@ -132,3 +132,34 @@ def test_concurrent_streams():
         torch.cuda.synchronize()
         for w, g in zip(want_a + want_b + want_c, list(got_a) + list(got_b) + list(got_c)):
             assert torch.equal(w, g)
+
+
+def test_resume_from_saved_state():
+    """The window ring, the step number and the placement in force are all
+    the state a serving loop keeps (the library keeps none): saving them
+    after step 3 and resuming in fresh buffers gives the outputs of the
+    uninterrupted loop, step for step."""
+    work, tokens, W = wl.DSV3_PREFILL, 3000, 4
+    steps = [wl.routing_step(work, s, tokens=tokens) for s in range(8)]
+    run = Loop(work, tokens, W)
+    outs = []
+    saved = None
+    for s, idx_h in enumerate(steps):
+        run.idx.copy_(torch.from_numpy(idx_h))
+        run.step(s)
+        torch.cuda.synchronize()
+        outs.append(run.state())
+        if s == 3:                              # checkpoint: host copies of the loop's state
+            saved = (run.ring.cpu().clone(), [t.cpu().clone() for t in run.placement])
+    resumed = Loop(work, tokens, W)
+    resumed.ring.copy_(saved[0].to(DEV))
+    for t, h in zip(resumed.placement, saved[1]):
+        t.copy_(h.to(DEV))
+    for s in range(4, len(steps)):
+        note(f"resumed step {s}")
+        resumed.idx.copy_(torch.from_numpy(steps[s]))
+        resumed.step(s)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "load", "n_invalid", "phy2log", "log2phy", "logcnt", "status"),
+                              resumed.state(), outs[s]):
+            assert np.array_equal(a, b), f"step {s}: {name} differs after resuming"
