@@ -695,6 +695,39 @@ def test_counts_with_large_prime_factors():
         assert logcnt[0].tolist() == counts and status.tolist() == [0]
 
 
+def test_many_problems_and_layers():
+    """Grids far past 65,535 workgroups: 200,000 small rebalance problems
+    (every 997th against the oracle, all by the invariants) and 70,000
+    streaming layers through the fused pass (all against the oracle)."""
+    rng = np.random.default_rng(31)
+    B, E, P, G, N, RK = 200_000, 16, 24, 4, 2, 8
+    load = rng.integers(0, 1 << 20, size=(B, E)).astype(np.int64)
+    note(f"rebalance B={B}")
+    phy2log, log2phy, logcnt, status = (host(t) for t in eplb.rebalance(gpu(load), P, G, N, RK))
+    rows = list(range(0, B, 997)) + [B - 1]
+    ref = ora.rebalance(load[rows], P, G, N, RK, ora.max_count(E, P, G, N))
+    for name, got in zip(("phy2log", "log2phy", "logcnt", "status"), (phy2log, log2phy, logcnt, status)):
+        assert_same(name, got[rows], ref[name])
+    assert (status == 0).all() and (logcnt.sum(axis=1) == P).all() and (logcnt >= 1).all()
+    placed = np.zeros((B, E), dtype=np.int64)                          # each expert's slots = its count
+    np.add.at(placed, (np.repeat(np.arange(B), P), phy2log.ravel()), 1)
+    assert (placed == logcnt).all()
+    L, T, K = 70_000, 3, 2
+    idx_h = rng.integers(-1, E + 1, size=(L, T, K)).astype(np.int32)
+    X = 4
+    cnt_h = rng.integers(1, X + 1, size=(L, E)).astype(np.int32)
+    l2p_h = rng.integers(0, 1000, size=(L, E, X)).astype(np.int32)
+    ring = torch.zeros((2, L, E), dtype=torch.int32, device=DEV)
+    note(f"hist_redirect L={L}")
+    load_w, bad, out = eplb.hist_redirect(gpu(idx_h), E, ring, 1, gpu(l2p_h), gpu(cnt_h))
+    torch.cuda.synchronize()
+    cnt, invl = ora.load_hist(idx_h, E)
+    assert_same("counts", host(ring[1]).astype(np.int64), cnt)
+    assert_same("window", host(load_w), cnt)
+    assert_same("invalid", host(bad), invl)
+    assert_same("redirect", host(out), ora.redirect(idx_h, l2p_h, cnt_h))
+
+
 def test_empty_inputs():
     E, P = 16, 24
     outs = eplb.rebalance(torch.zeros((0, E), dtype=torch.int64, device=DEV), P, 4, 2, 8, 5)
