@@ -221,6 +221,26 @@ def test_lp_solve_topologies(work):
     assert (q["lam"] <= base.max(axis=1)).all() and (q["lam"] < base.max(axis=1)).any()
 
 
+@pytest.mark.parametrize("RK", [8, 12, 24])
+def test_lp_solve_many_problems(RK):
+    """70,000 problems in one call (the enumeration, its four-way split from
+    12 ranks on, and the cut iteration): grids past 65,535 workgroups; every
+    499th problem against the oracle, all by the flow checks."""
+    rng = np.random.default_rng(RK)
+    B, R, E = 70_000, 1, 2 * RK
+    cnt = rng.integers(0, 1000, size=(B, E)).astype(np.int64)
+    home = np.tile(np.arange(E) % RK, (B, 1)).astype(np.int64)
+    rep = np.full((B, RK, R), -1, dtype=np.int64)
+    rep[:, :, 0] = (np.arange(RK) + 1) % RK                  # rank g holds a replica of expert g + 1 (homed on g + 1)
+    rows = list(range(0, B, 499)) + [B - 1]
+    q = solve_both(cnt, home, rep, rows=rows)
+    assert (q["status"] == 0).all()
+    home_loads = np.zeros((B, RK), dtype=np.int64)
+    np.add.at(home_loads, (np.repeat(np.arange(B), E), home.ravel()), cnt.ravel())
+    assert (q["lam"] <= home_loads.max(axis=1)).all() and (q["rank_load"].max(axis=1) == q["lam"]).all()
+    assert (q["rank_load"].sum(axis=1) == home_loads.sum(axis=1)).all()          # tokens are moved, not lost
+
+
 def test_lp_solve_degenerate_and_bad():
     # no replicas, zero counts, already even loads, and each invalid input
     cnt = np.array([[5, 9, 1, 7]] * 3 + [[5, 1, 2, 0]] * 6, dtype=np.int64)
