@@ -192,6 +192,30 @@ def test_rearrange_wide_fuzz():
     assert not bad, f"{len(bad)} cases differ from the oracle, first: {bad[0]}"
 
 
+def test_rearrange_many_problems():
+    """100,000 problems in one call (a grid past 65,535 workgroups); every
+    997th against the oracle."""
+    rng = np.random.default_rng(8)
+    B, E, RK, ppr, N = 100_000, 6, 4, 2, 2
+    P = RK * ppr
+
+    def placement():
+        base = np.concatenate([np.arange(E), rng.integers(0, E, size=(P - E,))])
+        return np.stack([rng.permutation(base) for _ in range(B)])
+    old, new = placement(), placement()
+    X = max(int(np.bincount(r, minlength=E).max()) for r in new[::1000]) + 3
+    # log2phy of every problem, vectorised: slot of the r-th copy of each expert
+    l2p = np.full((B, E, X), -1, dtype=np.int64)
+    order = np.argsort(new, axis=1, kind="stable")
+    sorted_e = np.take_along_axis(new, order, axis=1)
+    first = np.zeros((B, P), dtype=np.int64)
+    for j in range(1, P):
+        first[:, j] = np.where(sorted_e[:, j] == sorted_e[:, j - 1], first[:, j - 1] + 1, 0)
+    l2p[np.repeat(np.arange(B), P), sorted_e.ravel(), first.ravel()] = order.ravel()
+    rows = list(range(0, B, 997)) + [B - 1]
+    plan_both(old, new, l2p, RK, N, rows=rows)
+
+
 def test_rearrange_max_size():
     """P = 8192 on one rank (the longest scans) and on 512 ranks; E = 4096;
     checked by properties."""
