@@ -654,6 +654,23 @@ def test_shapes_beyond_64k_lds(shape):
     rebalance_both(load, P, G, N, RK, X)
 
 
+def test_wide_shape_many_problems():
+    """300 problems of a shape above 64 KiB of LDS with one register of
+    experts and of GPUs per node (the form held to 64 registers for batches
+    beyond one workgroup per compute unit); every 7th against the oracle."""
+    E, G, N, RK, P = 2048, 64, 32, 64, 2304                  # 32 nodes of 64 experts, 2 GPUs each
+    X = ora.max_count(E, P, G, N)
+    assert eplb.lib.eplb_rebalance_lds_bytes(E, P, G, N, RK, X) > 64 * 1024
+    rng = np.random.default_rng(17)
+    load = (rng.zipf(1.2, size=(300, E)) * 100).clip(0, 1 << 40).astype(np.int64)
+    load[::5] = rng.integers(0, 3, size=(60, E))
+    got = [host(t) for t in eplb.rebalance(gpu(load), P, G, N, RK, X)]
+    rows = list(range(0, 300, 7)) + [299]
+    ref = ora.rebalance(load[rows], P, G, N, RK, X)
+    for name, g in zip(("phy2log", "log2phy", "logcnt", "status"), got):
+        assert_same(name, g[rows], ref[name])
+
+
 def test_large_loads_and_exactness():
     rng = np.random.default_rng(5)
     load = rng.integers((1 << 40) - 5000, (1 << 40) + 1, size=(16, 64))
